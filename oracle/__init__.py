@@ -1,0 +1,168 @@
+"""Double-precision CPU oracle for causal GQA attention and RoPE.
+
+TEST INFRASTRUCTURE ONLY.  The oracle is loaded by the test suite, by the
+smoke check and by the CPU-baseline leg of the benchmark, and by nothing
+else: the attention library never imports, links or calls it, and the two
+share no code.  The arithmetic lives in ``attn_oracle.c`` (plain C, double
+precision, one score row at a time); this module only compiles it with gcc,
+widens the caller's arrays exactly to float64 and passes pointers.
+
+Functions (each cites its passage in ``attn_oracle.c``):
+    attn(q, k, v, scale, causal=True, q_offset=0, return_lse=False)
+    attn_rows(q, k, v, rows, scale, causal=True, q_offset=0)
+    rope(x, pos0=0, base=10000.0, pairing="split")
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+import tempfile
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attn_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+          "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def compile_library(source: str = SOURCE, out: str = LIBRARY) -> str:
+    """Compile the oracle C source into a shared library with gcc."""
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    fd, tmp = tempfile.mkstemp(suffix=".so", dir=os.path.dirname(os.path.abspath(out)))
+    os.close(fd)
+    cmd = ["gcc", *CFLAGS, source, "-o", tmp, "-lm"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        os.unlink(tmp)
+        raise RuntimeError("oracle build failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+def _as_f64(a) -> np.ndarray:
+    """Exact widening of a float32/bfloat16/float64 array (numpy or torch CPU)."""
+    if hasattr(a, "detach"):  # torch tensor: bf16 has no numpy dtype, widen in torch
+        import torch
+        a = a.detach().to("cpu")
+        a = a.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+_D = ctypes.POINTER(ctypes.c_double)
+_L = ctypes.c_long
+
+
+class Oracle:
+    """Bindings to one compiled copy of ``attn_oracle.c``."""
+
+    def __init__(self, lib_path: str = LIBRARY):
+        self.path = lib_path
+        lib = ctypes.CDLL(lib_path)
+        lib.oracle_attn.restype = ctypes.c_int
+        lib.oracle_attn.argtypes = [_D, _D, _D, _D, _D, _L, _L, _L, _L, _L, _L,
+                                    ctypes.c_double, ctypes.c_int, _L]
+        lib.oracle_attn_rows.restype = ctypes.c_int
+        lib.oracle_attn_rows.argtypes = [_D, _D, _D, ctypes.POINTER(ctypes.c_long), _L,
+                                         _D, _D, _L, _L, _L, _L, _L, _L,
+                                         ctypes.c_double, ctypes.c_int, _L]
+        lib.oracle_rope.restype = ctypes.c_int
+        lib.oracle_rope.argtypes = [_D, _L, _L, _L, _L, _L, ctypes.c_double, ctypes.c_int]
+        self._lib = lib
+
+    @staticmethod
+    def _ptr(a: np.ndarray):
+        return a.ctypes.data_as(_D)
+
+    def attn(self, q, k, v, scale: float, causal: bool = True, q_offset: int = 0,
+             return_lse: bool = False):
+        """o[B,Hq,Tq,d] (and lse[B,Hq,Tq]) for q[B,Hq,Tq,d], k/v[B,Hkv,Tk,d]."""
+        q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+        B, Hq, Tq, d = q.shape
+        _, Hkv, Tk, _ = k.shape
+        if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+            raise ValueError("shape mismatch")
+        o = np.empty_like(q)
+        lse = np.empty((B, Hq, Tq), dtype=np.float64) if return_lse else None
+        st = self._lib.oracle_attn(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(o),
+                                   self._ptr(lse) if lse is not None else None,
+                                   B, Hq, Hkv, Tq, Tk, d, float(scale), int(bool(causal)),
+                                   int(q_offset))
+        if st != 0:
+            raise ValueError(f"oracle_attn rejected its arguments (status {st})")
+        return (o, lse) if return_lse else o
+
+    def attn_rows(self, q, k, v, rows, scale: float, causal: bool = True,
+                  q_offset: int = 0, return_lse: bool = False):
+        """Selected rows: rows is an (n, 3) integer array of (b, hq, i)."""
+        q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+        B, Hq, Tq, d = q.shape
+        _, Hkv, Tk, _ = k.shape
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+        n = rows.shape[0]
+        o = np.empty((n, d), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64) if return_lse else None
+        st = self._lib.oracle_attn_rows(
+            self._ptr(q), self._ptr(k), self._ptr(v),
+            rows.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), n, self._ptr(o),
+            self._ptr(lse) if lse is not None else None,
+            B, Hq, Hkv, Tq, Tk, d, float(scale), int(bool(causal)), int(q_offset))
+        if st != 0:
+            raise ValueError(f"oracle_attn_rows rejected its arguments (status {st})")
+        return (o, lse) if return_lse else o
+
+    def rope(self, x, pos0: int = 0, base: float = 10000.0, pairing: str = "split"):
+        """Rotated copy of x[B,H,T,d] (token t at position pos0 + t)."""
+        y = _as_f64(x).copy()
+        B, H, T, d = y.shape
+        pm = {"split": 0, "adjacent": 1}[pairing]
+        st = self._lib.oracle_rope(self._ptr(y), B, H, T, d, int(pos0), float(base), pm)
+        if st != 0:
+            raise ValueError(f"oracle_rope rejected its arguments (status {st})")
+        return y
+
+
+_default: Oracle | None = None
+
+
+def _stale() -> bool:
+    return (not os.path.exists(LIBRARY)
+            or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE))
+
+
+def default() -> Oracle:
+    """The oracle built from ``attn_oracle.c`` (compiled on first use)."""
+    global _default
+    if _default is None:
+        if _stale():
+            compile_library()
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def attn(*args, **kwargs):
+    return default().attn(*args, **kwargs)
+
+
+def attn_rows(*args, **kwargs):
+    return default().attn_rows(*args, **kwargs)
+
+
+def rope(*args, **kwargs):
+    return default().rope(*args, **kwargs)
+
+
+def threads_used() -> int:
+    """OpenMP threads the oracle runs with (OMP_NUM_THREADS, else all cores)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.strip().isdigit():
+        return int(env)
+    return os.cpu_count() or 1
+
+
+if __name__ == "__main__":  # pragma: no cover
+    print(compile_library(), file=sys.stderr)

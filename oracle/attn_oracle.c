@@ -1,0 +1,217 @@
+/*
+ * attn_oracle.c -- plain, slow, double-precision CPU oracle for causal
+ * multi-head scaled dot-product attention with grouped KV heads, and for the
+ * rotary position embedding applied to queries and keys.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call this file:
+ * only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark load it.  It shares no source, header, table or helper with the
+ * HIP library, and it is written for a reader who checks it against the
+ * pages by eye: every loop follows the formula it cites, in the formula's
+ * order, with no blocking, fusion or reordering.
+ *
+ * Sources (page title -- section):
+ *   [P1] "Transformer Math and Implementation Deep Dive" -- Attention Shapes,
+ *        Attention Equation, Causal Masking.
+ *   [P2] "The Transformer architecture" -- Scaled dot-product attention;
+ *        Softmax is a differentiable allocation; Now: RoPE (apply_rope);
+ *        What else the modern decoder-only model changed (GQA); Hands-on
+ *        (queries of a cached step sit at cache.pos + i).
+ *   [P4] "Transformer" (ai-notes) -- Scaled dot-product attention
+ *        (Attn(Q,K,V;M)); What is the causal mask?; RoPE (Rotary Positional
+ *        Embedding) (theta_i(pos)).
+ *
+ * Layouts (all row-major, last index fastest, element type double):
+ *   q, o : [B][Hq ][Tq][d]        k, v : [B][Hkv][Tk][d]
+ *   lse  : [B][Hq][Tq]  (optional, may be NULL)
+ *
+ * Every function returns 0 on success and a negative value when its
+ * arguments cannot describe a defined result (see each function).
+ */
+#include <math.h>
+#include <stdlib.h>
+
+/* Query head hq reads key/value head hq / (Hq / Hkv): contiguous groups of
+ * n_rep = Hq / Hkv query heads share one K/V head [P1 Attention Shapes: "the
+ * implementation repeats or maps KV heads across query head groups"; P2 GQA:
+ * "each group of n_rep query heads share one set of K/V heads"]. */
+static long kv_head_of(long hq, long Hq, long Hkv) { return hq / (Hq / Hkv); }
+
+/* Last key a query row may read.  Causal: key j is visible to query row i
+ * iff j <= q_offset + i, where q_offset is the absolute position of the
+ * first query row (0 for a plain prefill; cache.pos for a cached step)
+ * [P1 Causal Masking: scores[i,j] = -inf if j > i; P4 What is the causal
+ * mask?: M[t,s] = 0 for s <= t, -inf otherwise; P2 Hands-on: query
+ * positions start at cache.pos + i, keys run from 0 to cache.pos + T - 1].
+ * Keys past Tk - 1 do not exist.  Returns -1 when no key is visible. */
+static long last_visible_key(long i, long Tk, int causal, long q_offset) {
+    if (!causal) return Tk - 1;
+    long lim = q_offset + i;
+    return lim < Tk - 1 ? lim : Tk - 1;
+}
+
+/* One output row o[b,hq,i,:] of
+ *     o_i = sum_j alpha_ij v_j,
+ *     alpha_ij = exp(s_ij) / sum_j' exp(s_ij'),   s_ij = scale * q_i . k_j
+ * over the visible keys j [P2 Scaled dot-product attention; P4 Attn(Q,K,V;M)
+ * = softmax(QK^T/sqrt(d_k) + M) V].  A key with M = -inf has exp(-inf) = 0
+ * and contributes nothing [P3 "Grasping Codes and Math 02" -- Why Fill with
+ * Negative Infinity?], so the masked keys are simply left out of both sums.
+ * Subtracting the row maximum m from every score before exp leaves alpha
+ * unchanged in exact arithmetic (the factor exp(-m) cancels) and keeps
+ * exp() finite.  `srow` is caller scratch of at least Tk doubles. */
+static void attn_row(const double* qi, const double* kh, const double* vh,
+                     double* oi, double* lse_i, double* srow,
+                     long Tk, long d, double scale, long lim) {
+    /* scores s_j = scale * sum_c q[c] k[j][c] */
+    for (long j = 0; j <= lim; ++j) {
+        const double* kj = kh + j * d;
+        double dot = 0.0;
+        for (long c = 0; c < d; ++c) dot += qi[c] * kj[c];
+        srow[j] = scale * dot;
+    }
+    (void)Tk;
+    /* m = max_j s_j */
+    double m = srow[0];
+    for (long j = 1; j <= lim; ++j)
+        if (srow[j] > m) m = srow[j];
+    /* w_j = exp(s_j - m),  l = sum_j w_j */
+    double l = 0.0;
+    for (long j = 0; j <= lim; ++j) {
+        srow[j] = exp(srow[j] - m);
+        l += srow[j];
+    }
+    /* o[c] = sum_j w_j v[j][c] / l */
+    for (long c = 0; c < d; ++c) oi[c] = 0.0;
+    for (long j = 0; j <= lim; ++j) {
+        const double* vj = vh + j * d;
+        for (long c = 0; c < d; ++c) oi[c] += srow[j] * vj[c];
+    }
+    for (long c = 0; c < d; ++c) oi[c] /= l;
+    /* log of the softmax denominator of the unshifted scores */
+    if (lse_i) *lse_i = m + log(l);
+}
+
+static int check_shape(long B, long Hq, long Hkv, long Tq, long Tk, long d,
+                       double scale, int causal, long q_offset) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || d <= 0) return -2;
+    if (Hq % Hkv != 0) return -2;
+    if (!isfinite(scale)) return -6;
+    /* a causal row with no visible key has the softmax of all -inf, which is
+     * undefined; the first row sees key q_offset, so q_offset >= 0 */
+    if (causal && q_offset < 0) return -5;
+    return 0;
+}
+
+/* Full attention forward.  lse may be NULL. */
+int oracle_attn(const double* q, const double* k, const double* v, double* o,
+                double* lse, long B, long Hq, long Hkv, long Tq, long Tk,
+                long d, double scale, int causal, long q_offset) {
+    int st = check_shape(B, Hq, Hkv, Tq, Tk, d, scale, causal, q_offset);
+    if (st) return st;
+    const long nrows = B * Hq * Tq;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* srow = (double*)malloc(sizeof(double) * (size_t)Tk);
+        if (!srow) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (long r = 0; r < nrows; ++r) {
+                long i = r % Tq, bh = r / Tq, hq = bh % Hq, b = bh / Hq;
+                long hk = kv_head_of(hq, Hq, Hkv);
+                const double* qi = q + r * d;
+                const double* kh = k + (b * Hkv + hk) * Tk * d;
+                const double* vh = v + (b * Hkv + hk) * Tk * d;
+                long lim = last_visible_key(i, Tk, causal, q_offset);
+                attn_row(qi, kh, vh, o + r * d, lse ? lse + r : NULL, srow,
+                         Tk, d, scale, lim);
+            }
+            free(srow);
+        }
+    }
+    return failed ? -10 : 0;
+}
+
+/* The same rows as oracle_attn, but only the n rows listed in `rows`
+ * (triples b, hq, i), written densely to o_rows[n][d] (and lse_rows[n] if
+ * not NULL).  Used to check selected rows of workloads too large for the
+ * full loop. */
+int oracle_attn_rows(const double* q, const double* k, const double* v,
+                     const long* rows, long n, double* o_rows, double* lse_rows,
+                     long B, long Hq, long Hkv, long Tq, long Tk, long d,
+                     double scale, int causal, long q_offset) {
+    int st = check_shape(B, Hq, Hkv, Tq, Tk, d, scale, causal, q_offset);
+    if (st) return st;
+    for (long r = 0; r < n; ++r) {
+        long b = rows[3 * r], hq = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || hq < 0 || hq >= Hq || i < 0 || i >= Tq) return -2;
+    }
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* srow = (double*)malloc(sizeof(double) * (size_t)Tk);
+        if (!srow) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (long r = 0; r < n; ++r) {
+                long b = rows[3 * r], hq = rows[3 * r + 1], i = rows[3 * r + 2];
+                long hk = kv_head_of(hq, Hq, Hkv);
+                const double* qi = q + ((b * Hq + hq) * Tq + i) * d;
+                const double* kh = k + (b * Hkv + hk) * Tk * d;
+                const double* vh = v + (b * Hkv + hk) * Tk * d;
+                long lim = last_visible_key(i, Tk, causal, q_offset);
+                attn_row(qi, kh, vh, o_rows + r * d,
+                         lse_rows ? lse_rows + r : NULL, srow, Tk, d, scale, lim);
+            }
+            free(srow);
+        }
+    }
+    return failed ? -10 : 0;
+}
+
+/* Rotary position embedding, in place on x[B][H][T][d].
+ *
+ * Token t sits at absolute position pos = pos0 + t (pos0 = cache.pos for a
+ * cached step [P2 Hands-on: "RoPE is sliced from cache.pos too"]).  Channel
+ * pair p (p = 0 .. d/2 - 1) turns by the angle
+ *     theta_p(pos) = pos * base^(-2p/d)
+ * [P4 RoPE: theta_i(pos) = pos * 10000^(-2i/d_head)], through the 2x2
+ * rotation [[cos, -sin], [sin, cos]] [P2 Now: RoPE, R_m; P4 RoPE].
+ *
+ * pairing 0 (split-half): pair p is channels (p, p + d/2) [P2 Now: RoPE,
+ *     apply_rope: x1, x2 = the two halves; (x1 cos - x2 sin, x1 sin + x2 cos)].
+ * pairing 1 (adjacent):   pair p is channels (2p, 2p + 1) [P4 RoPE].
+ * The two differ by a channel permutation [P2 Now: RoPE, warning note].
+ *
+ * Angle, cosine and sine are taken in double precision.  Returns -4 for an
+ * odd d, -2 for other bad sizes. */
+int oracle_rope(double* x, long B, long H, long T, long d, long pos0,
+                double base, int pairing) {
+    if (B <= 0 || H <= 0 || T <= 0 || d <= 0) return -2;
+    if (d % 2 != 0) return -4;
+    if (pairing != 0 && pairing != 1) return -3;
+    if (!(base > 0.0) || !isfinite(base)) return -6;
+    const long half = d / 2;
+    const long nvec = B * H * T;
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < nvec; ++r) {
+        long t = r % T;
+        double pos = (double)(pos0 + t);
+        double* xr = x + r * d;
+        for (long p = 0; p < half; ++p) {
+            double theta = pos * pow(base, -2.0 * (double)p / (double)d);
+            double cs = cos(theta), sn = sin(theta);
+            long a = pairing == 0 ? p : 2 * p;
+            long b2 = pairing == 0 ? p + half : 2 * p + 1;
+            double x1 = xr[a], x2 = xr[b2];
+            xr[a] = x1 * cs - x2 * sn;
+            xr[b2] = x1 * sn + x2 * cs;
+        }
+    }
+    return 0;
+}
