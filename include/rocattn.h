@@ -1,0 +1,166 @@
+/*
+ * rocattn.h -- C ABI of the gfx950 (MI355X) causal attention library
+ * (librocattn.so).
+ *
+ * The library computes, per batch b and query head hq,
+ *
+ *     O = softmax(scale * Q K^T + M) V                                   (1)
+ *
+ * with M the additive causal mask (0 where key j may be read by query row
+ * i, -inf where it may not), on queries and keys that `rope_apply` has
+ * rotated by position, and with several query heads sharing one K/V head.
+ *
+ * Sources (page title -- section):
+ *   "Transformer" (ai-notes) -- Scaled dot-product attention:
+ *       Attn(Q,K,V;M) = softmax(QK^T/sqrt(d_k) + M) V; What is the causal
+ *       mask? (M[t,s] = 0 for s <= t, -inf otherwise); How to "kill" the
+ *       sqrt(d_k) (an explicit temperature alpha may replace 1/sqrt(d_k));
+ *       RoPE (theta_i(pos) = pos * 10000^(-2i/d_head)).
+ *   "The Transformer architecture" -- Scaled dot-product attention
+ *       (shapes, scale uses the per-head d_k); Now: RoPE (apply_rope with
+ *       split-half pairing, cos/sin of shape (T, d/2)); What else the modern
+ *       decoder-only model changed (GQA groups of n_rep query heads);
+ *       Hands-on (with a cache, query row i sits at cache.pos + i and RoPE
+ *       is sliced from cache.pos).
+ *   "Transformer Math and Implementation Deep Dive" -- Attention Shapes
+ *       (q: [B, n_q_heads, T, d_head], k/v: [B, n_kv_heads, T, d_head]).
+ *   "Grasping Codes and Math 02" -- Flash Attention (one fused kernel that
+ *       never materialises the T x T attention matrix).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * Layout.  q and o are [B][Hq][Tq][d_head]; k and v are [B][Hkv][Tk][d_head];
+ *   dense, row-major, d_head fastest.  o has q's element type.
+ * Heads.  Query head hq reads K/V head hq / (Hq / Hkv) (contiguous groups,
+ *   the grouping torch's repeat_interleave makes); Hq % Hkv must be 0.
+ *   K/V are never replicated.
+ * Causal rule.  With causal != 0, key j is visible to query row i iff
+ *   j <= q_offset + i.  q_offset is the absolute position of the first
+ *   query row: 0 for a plain prefill (Tq == Tk), Tk - Tq for a chunk of new
+ *   rows appended to a cache, Tk - 1 for a one-token decode step.
+ *   causal == 0 makes every key visible (q_offset is then ignored).
+ * Pointers.  Device pointers (memory from hipMalloc or a torch CUDA tensor),
+ *   each 16-byte aligned.  The caller owns every buffer; the library never
+ *   frees or retains caller memory.  o must not overlap q, k or v.
+ * Stream.  `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *   only enqueued: nothing synchronises, results are ready when the stream
+ *   is, and a fault inside a kernel surfaces at the caller's next
+ *   synchronisation, not in the returned status.
+ * Errors.  Arguments are validated on the host before any launch; a
+ *   rejected call launches nothing and writes nothing.  The status covers
+ *   validation and launch errors only.
+ * Threads.  Entry points are reentrant; the library keeps no state across
+ *   calls apart from a per-device cache of the kernel properties it queries.
+ */
+#ifndef ROCATTN_H
+#define ROCATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. */
+typedef enum {
+    ROCATTN_F32 = 0,   /* float32 in, float32 math, float32 out */
+    ROCATTN_BF16 = 1   /* bfloat16 in, float32 accumulation, bfloat16 out (RNE) */
+} rocattn_dtype;
+
+/* Status codes (0 = success, negative = rejected or failed). */
+typedef enum {
+    ROCATTN_OK = 0,
+    ROCATTN_ERR_NULL = -1,      /* a required pointer is NULL */
+    ROCATTN_ERR_SHAPE = -2,     /* a size <= 0, Hq % Hkv != 0, overlap of o with an input,
+                                   or a tensor too large for 64-bit element offsets */
+    ROCATTN_ERR_DTYPE = -3,     /* dtype not a rocattn_dtype */
+    ROCATTN_ERR_HEADDIM = -4,   /* d_head not supported for this dtype / entry point */
+    ROCATTN_ERR_OFFSET = -5,    /* causal with q_offset < 0: row 0 would see no key */
+    ROCATTN_ERR_SCALE = -6,     /* scale (or RoPE base) not finite, or base <= 0 */
+    ROCATTN_ERR_ALIGN = -7,     /* a pointer is not 16-byte aligned */
+    ROCATTN_ERR_WORKSPACE = -8, /* workspace NULL or smaller than attn_workspace_bytes() */
+    ROCATTN_ERR_HIP = -9        /* the HIP runtime reported an error while launching */
+} rocattn_status;
+
+/*
+ * attn_fwd -- equation (1) for every (b, hq, query row).
+ *
+ *   q, k, v   inputs, layouts above; read only.
+ *   o         output [B][Hq][Tq][d_head], fully overwritten.
+ *   B, Hq, Hkv, Tq, Tk, d_head   sizes (all > 0, Hq % Hkv == 0).
+ *   scale     multiplies q.k before the softmax; 1/sqrt(d_head) for standard
+ *             attention, any finite value (a temperature; 0 gives the mean of
+ *             the visible values).
+ *   causal    non-zero: causal rule above; zero: no mask.
+ *   q_offset  position of query row 0 (causal only; must be >= 0).
+ *   dtype     rocattn_dtype of q, k, v and o.
+ *   stream    hipStream_t.
+ *
+ * Supported head sizes: bf16 d_head in {64, 128}; f32 d_head <= 256 with
+ * d_head % 4 == 0.  bf16 with Tq == 1 runs the split-K decode kernels, which
+ * need a workspace: attn_fwd takes it from the stream-ordered allocator
+ * (hipMallocAsync / hipFreeAsync on `stream`); use attn_fwd_ws to pass one.
+ * Returns a rocattn_status.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o,
+             int B, int Hq, int Hkv, int Tq, int Tk, int d_head,
+             float scale, int causal, int q_offset, int dtype, void* stream);
+
+/*
+ * attn_workspace_bytes -- bytes of device workspace attn_fwd_ws needs for
+ * these sizes (0 when the chosen kernels need none).  Returns 0 for
+ * arguments attn_fwd would reject.
+ */
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d_head, int dtype);
+
+/*
+ * attn_fwd_ws -- attn_fwd with a caller-owned workspace and an optional
+ * log-sum-exp output.
+ *
+ *   workspace, ws_bytes  device buffer of at least attn_workspace_bytes()
+ *             bytes (may be NULL when that is 0); contents on entry are
+ *             ignored and on return are unspecified.  Calls that share a
+ *             workspace must be ordered on one stream.
+ *   lse       NULL, or float32 [B][Hq][Tq]: lse = log(sum_j exp(scale q_i.k_j))
+ *             over the visible keys j (natural log), for a later backward
+ *             pass or for merging partial attentions.
+ * Other arguments and the result as attn_fwd.
+ */
+int attn_fwd_ws(const void* q, const void* k, const void* v, void* o,
+                int B, int Hq, int Hkv, int Tq, int Tk, int d_head,
+                float scale, int causal, int q_offset, int dtype, void* stream,
+                void* workspace, size_t ws_bytes, float* lse);
+
+/*
+ * rope_apply -- rotary position embedding, in place, on q and (optionally) k.
+ *
+ * Token t (0 <= t < T) sits at position pos0 + t (pos0 = cache.pos for a
+ * cached step).  Channel pair p (0 <= p < d_head/2) is channels
+ * (p, p + d_head/2) (split-half pairing) and turns by
+ *     theta_p = (pos0 + t) * base^(-2p / d_head)
+ * through [[cos, -sin], [sin, cos]]:
+ *     x'[p]        = x[p] cos - x[p + d/2] sin
+ *     x'[p + d/2]  = x[p] sin + x[p + d/2] cos.
+ * The angle and its cosine and sine are formed in double precision and
+ * rounded once to float32; the rotation runs in float32 and bf16 results are
+ * rounded to nearest even.  Values are never rotated.
+ *
+ *   q         [B][Hq][T][d_head], rotated in place.
+ *   k         [B][Hkv][T][d_head] rotated in place, or NULL (q only; Hkv is
+ *             then ignored).
+ *   pos0      position of token 0 (>= 0).
+ *   base      frequency base (10000 in the original schedule), finite, > 0.
+ *   dtype     rocattn_dtype of q and k.
+ * Supported: d_head even, 2 <= d_head <= 256.  Returns a rocattn_status.
+ */
+int rope_apply(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head,
+               int pos0, double base, int dtype, void* stream);
+
+/* attn_status_string -- static English text for a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROCATTN_H */

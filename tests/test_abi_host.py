@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/rocattn.h declares, and rejects bad arguments with the documented
+status before anything is launched (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_causal_self_amd as rocattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rocattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rocattn.LIBRARY),
+                                reason="librocattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(rocattn.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(rocattn.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(-9, 1):
+        s = rocattn.status_string(code)
+        assert s and s != "unknown status"
+    assert rocattn.status_string(-100) == "unknown status"
+
+
+# fake, 16-byte aligned, never dereferenced: every call below fails validation
+A, Bp, C, D = 0x10000, 0x20000000, 0x40000000, 0x60000000
+F32, BF16 = rocattn.F32, rocattn.BF16
+
+
+def fwd(q=A, k=Bp, v=C, o=D, B=1, Hq=4, Hkv=2, Tq=16, Tk=16, d=64, scale=0.125, causal=1,
+        q_offset=0, dtype=BF16):
+    return rocattn.library().attn_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d, scale, causal,
+                                      q_offset, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(B=0), -2), (dict(Hq=0), -2), (dict(Hkv=-1), -2), (dict(Tq=0), -2), (dict(Tk=0), -2),
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(dtype=2), -3), (dict(dtype=-1), -3),
+    (dict(d=96), -4), (dict(d=32), -4), (dict(d=258, dtype=F32), -4), (dict(d=6, dtype=F32), -4),
+    (dict(q_offset=-1), -5),
+    (dict(scale=float("inf")), -6), (dict(scale=float("nan")), -6),
+    (dict(q=A + 8), -7), (dict(o=D + 2), -7),
+    (dict(o=A), -2),                      # output aliases q
+    (dict(o=Bp + 64), -2),                # output overlaps k
+])
+def test_attn_fwd_rejects(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_attn_fwd_ws_rejects_small_workspace_and_bad_lse():
+    lib = rocattn.library()
+    # a decode step (bf16, Tq == 1) needs a workspace
+    need = lib.attn_workspace_bytes(2, 8, 2, 1, 4096, 128, BF16)
+    assert need > 0
+    args = (A, Bp, C, D, 2, 8, 2, 1, 4096, 128, 0.088, 1, 4095, BF16, None)
+    assert lib.attn_fwd_ws(*args, None, 0, None) == -8
+    assert lib.attn_fwd_ws(*args, 0x70000000, need - 1, None) == -8
+    assert lib.attn_fwd_ws(*args, 0x70000008, need, None) == -7      # misaligned workspace
+    assert lib.attn_fwd_ws(*args, 0x70000000, need, 0x7F000002) == -7  # misaligned lse
+
+
+def test_workspace_bytes():
+    lib = rocattn.library()
+    assert lib.attn_workspace_bytes(8, 12, 12, 1024, 1024, 64, BF16) == 0     # prefill
+    assert lib.attn_workspace_bytes(1, 4, 4, 1, 128, 64, F32) == 0            # f32 path
+    assert lib.attn_workspace_bytes(32, 32, 8, 1, 8192, 128, BF16) > 0        # decode
+    assert lib.attn_workspace_bytes(32, 32, 8, 1, 8192, 96, BF16) == 0        # rejected shape
+    assert lib.attn_workspace_bytes(32, 30, 8, 1, 8192, 128, BF16) == 0       # Hq % Hkv
+    # the bound covers every shorter cache
+    big = lib.attn_workspace_bytes(4, 8, 2, 1, 100000, 128, BF16)
+    for tk in (1, 63, 64, 1000, 1025, 4096, 99999):
+        assert lib.attn_workspace_bytes(4, 8, 2, 1, tk, 128, BF16) <= big
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(dtype=5), -3), (dict(B=0), -2), (dict(T=0), -2),
+    (dict(Hkv=0), -2), (dict(d=7), -4), (dict(d=258), -4), (dict(pos0=-1), -5),
+    (dict(base=0.0), -6), (dict(base=-2.0), -6), (dict(base=float("nan")), -6),
+    (dict(q=A + 4), -7), (dict(k=Bp + 2), -7), (dict(k=A + 64), -2),
+])
+def test_rope_apply_rejects(kw, status):
+    args = dict(q=A, k=Bp, B=1, Hq=4, Hkv=2, T=8, d=64, pos0=0, base=10000.0, dtype=BF16)
+    args.update(kw)
+    lib = rocattn.library()
+    assert lib.rope_apply(args["q"], args["k"], args["B"], args["Hq"], args["Hkv"], args["T"],
+                          args["d"], args["pos0"], args["base"], args["dtype"], None) == status
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rocattn.attn_fwd(q, q, q)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rocattn.rope_apply(q)

@@ -1,0 +1,383 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the fp64
+CPU oracle on the same seeded inputs, plus invariants the pages fix.
+
+Tolerances (max |gpu - oracle| over the compared outputs): 1e-5 for float32,
+1.5e-2 for bfloat16 with float32 accumulation.  The oracle reads the very
+arrays the GPU reads (bf16 widened exactly to float64); end-to-end RoPE cases
+rotate on each side with that side's own RoPE.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_causal_self_amd as ra
+from transformer_causal_self_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 1.5e-2}
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def gpu(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def run_attn(q, k, v, scale, causal=True, q_offset=0, lse=False):
+    qd, kd, vd = gpu(q, k, v)
+    od = torch.empty_like(qd)
+    if lse:
+        B, Hq, Tq, d = q.shape
+        ws_b = ra.attn_workspace_bytes(B, Hq, k.shape[1], Tq, k.shape[2], d, q.dtype)
+        ws = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=DEV)
+        lsed = torch.empty(B, Hq, Tq, dtype=torch.float32, device=DEV)
+        ra.attn_fwd_ws(qd, kd, vd, od, ws if ws_b else None, lsed, scale=scale, causal=causal,
+                       q_offset=q_offset)
+        torch.cuda.synchronize()
+        return od.cpu(), lsed.cpu()
+    ra.attn_fwd(qd, kd, vd, od, scale=scale, causal=causal, q_offset=q_offset)
+    torch.cuda.synchronize()
+    return od.cpu()
+
+
+def check(q, k, v, scale, causal=True, q_offset=0, tol=None):
+    got = run_attn(q, k, v, scale, causal, q_offset)
+    want = oracle.attn(q, k, v, scale, causal=causal, q_offset=q_offset)
+    err = float(np.max(np.abs(f64(got) - want)))
+    tol = TOL[q.dtype] if tol is None else tol
+    assert np.all(np.isfinite(f64(got)))
+    assert err <= tol, f"max abs err {err:.3e} > {tol:.1e}"
+    return err
+
+
+# --------------------------------------------------------------------------
+# RoPE
+# --------------------------------------------------------------------------
+
+def rope_tol(want, dtype):
+    if dtype == torch.float32:
+        return 1e-5
+    # one bf16 ulp of the exact result (round-to-nearest of a float32 value
+    # that is itself within a few float32 ulps of the exact rotation)
+    return np.abs(want) * 2.0 ** -7 + 1e-6
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [2, 6, 64, 128])
+@pytest.mark.parametrize("pos0", [0, 4093, 16300])
+def test_rope_matches_oracle(dtype, d, pos0):
+    say("rope", dtype, d, pos0)
+    q, k, _ = wl.random_qkv(2, 4, 2, 37, 37, d, dtype=dtype, seed=10 + d + pos0)
+    qd, kd = gpu(q, k)
+    ra.rope_apply(qd, kd, pos0=pos0, base=10000.0)
+    torch.cuda.synchronize()
+    for got, x in ((qd, q), (kd, k)):
+        want = oracle.rope(x, pos0=pos0, base=10000.0)
+        diff = np.abs(f64(got) - want)
+        assert np.all(diff <= rope_tol(want, dtype)), float(diff.max())
+
+
+def test_rope_q_only_and_other_base():
+    say("rope q only, base 5e5")
+    q, k, _ = wl.random_qkv(1, 3, 1, 5, 5, 128, dtype=torch.bfloat16, seed=77)
+    qd, kd = gpu(q, k)
+    ra.rope_apply(qd, None, pos0=9, base=500000.0)
+    torch.cuda.synchronize()
+    want = oracle.rope(q, pos0=9, base=500000.0)
+    assert np.all(np.abs(f64(qd) - want) <= rope_tol(want, torch.bfloat16))
+    assert torch.equal(kd.cpu(), k)  # untouched
+
+
+def test_rope_position_zero_is_identity():
+    say("rope pos 0 identity")
+    q, k, _ = wl.random_qkv(1, 2, 2, 1, 1, 64, dtype=torch.bfloat16, seed=5)
+    qd, kd = gpu(q, k)
+    ra.rope_apply(qd, kd, pos0=0)
+    torch.cuda.synchronize()
+    assert torch.equal(qd.cpu(), q) and torch.equal(kd.cpu(), k)
+
+
+def test_rope_full_workload3_shape():
+    """Every element of the GQA prefill workload's q and k (positions 0..4095)."""
+    w = wl.WORKLOADS[3]
+    say("rope full", w.name)
+    q, k, _ = wl.inputs(w)
+    qd, kd = gpu(q, k)
+    ra.rope_apply(qd, kd, pos0=0, base=w.rope_base)
+    torch.cuda.synchronize()
+    for got, x in ((qd, q), (kd, k)):
+        want = oracle.rope(x, pos0=0, base=w.rope_base)
+        assert np.all(np.abs(f64(got) - want) <= rope_tol(want, torch.bfloat16))
+
+
+# --------------------------------------------------------------------------
+# float32 path
+# --------------------------------------------------------------------------
+
+def test_attn_f32_workload1():
+    w = wl.WORKLOADS[1]
+    say("f32", w.name)
+    q, k, v = wl.inputs(w)
+    err = check(q, k, v, w.scale)
+    say("max abs err", err)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tk,d,causal,qo,scale", [
+    (2, 4, 2, 100, 100, 64, True, 0, 0.125),
+    (1, 6, 3, 37, 200, 128, True, 163, 0.0884),
+    (1, 2, 1, 130, 130, 256, True, 0, 0.0625),
+    (1, 2, 2, 33, 70, 8, False, 0, 0.35),
+    (1, 4, 1, 1, 513, 64, True, 512, 0.125),
+    (1, 2, 2, 65, 65, 36, True, 0, -0.2),
+    (1, 2, 2, 40, 40, 64, True, 0, 0.0),
+])
+def test_attn_f32_shapes(B, Hq, Hkv, Tq, Tk, d, causal, qo, scale):
+    say("f32", B, Hq, Hkv, Tq, Tk, d, causal, qo, scale)
+    q, k, v = wl.random_qkv(B, Hq, Hkv, Tq, Tk, d, dtype=torch.float32, seed=Tq + Tk + d)
+    check(q, k, v, scale, causal, qo)
+
+
+# --------------------------------------------------------------------------
+# bf16 prefill (MFMA kernel)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tk,d,causal,qo,scale", [
+    (2, 4, 2, 300, 300, 64, True, 0, 0.125),        # several tiles + ragged tail
+    (1, 8, 2, 257, 257, 128, True, 0, 0.0884),
+    (1, 2, 2, 1, 1, 128, True, 0, 0.0884),          # single row / key
+    (1, 4, 4, 64, 64, 64, True, 0, 0.125),
+    (1, 4, 1, 100, 357, 128, True, 257, 0.0884),    # chunk appended to a cache
+    (1, 3, 3, 129, 200, 64, False, 0, 0.125),       # no mask, Tq != Tk
+    (2, 16, 16, 128, 128, 64, True, 0, 0.125),      # K/V heads a multiple of 8 (XCD grouping)
+    (1, 16, 8, 200, 200, 128, True, 0, 0.0884),
+    (1, 2, 1, 150, 150, 64, True, 0, -0.125),       # negative temperature
+    (1, 2, 1, 150, 150, 128, True, 0, 0.0),         # scale 0: prefix means
+    (1, 2, 2, 190, 190, 128, True, 0, 0.5),         # peaky softmax
+])
+def test_attn_bf16_shapes(B, Hq, Hkv, Tq, Tk, d, causal, qo, scale):
+    say("bf16", B, Hq, Hkv, Tq, Tk, d, causal, qo, scale)
+    q, k, v = wl.random_qkv(B, Hq, Hkv, Tq, Tk, d, dtype=torch.bfloat16, seed=B * Tq + Tk + d)
+    check(q, k, v, scale, causal, qo)
+
+
+def test_attn_bf16_workload2_full():
+    """GPT-2-small attention shape, every output element."""
+    w = wl.WORKLOADS[2]
+    say("bf16 full", w.name)
+    q, k, v = wl.inputs(w)
+    err = check(q, k, v, w.scale)
+    say("max abs err", err)
+
+
+def test_end_to_end_workload3_full():
+    """RoPE then GQA causal attention on the B2 Hq32 Hkv8 T4096 d128
+    workload, every output element."""
+    w = wl.WORKLOADS[3]
+    say("rope+attn full", w.name)
+    q, k, v = wl.inputs(w)
+    qd, kd, vd = gpu(q, k, v)
+    ra.rope_apply(qd, kd, pos0=0, base=w.rope_base)
+    od = ra.attn_fwd(qd, kd, vd, scale=w.scale)
+    torch.cuda.synchronize()
+    want = oracle.attn(oracle.rope(q, 0, w.rope_base), oracle.rope(k, 0, w.rope_base), v, w.scale)
+    err = float(np.max(np.abs(f64(od) - want)))
+    say("max abs err", err)
+    assert err <= TOL[torch.bfloat16]
+
+
+def test_end_to_end_workload4_sampled():
+    """Long-context workload (T16384, sigma 0.5): every row of one query
+    head plus 96 seeded random rows of every head."""
+    w = wl.WORKLOADS[4]
+    say("rope+attn sampled", w.name)
+    q, k, v = wl.inputs(w)
+    qd, kd, vd = gpu(q, k, v)
+    ra.rope_apply(qd, kd, pos0=0, base=w.rope_base)
+    od = ra.attn_fwd(qd, kd, vd, scale=w.scale)
+    torch.cuda.synchronize()
+    got = f64(od)
+    rng = np.random.default_rng(4)
+    rows = [(0, 31, i) for i in range(w.Tq)]
+    for hq in range(w.Hq):
+        rows += [(0, hq, int(i)) for i in rng.integers(0, w.Tq, 96)]
+        rows += [(0, hq, 0), (0, hq, w.Tq - 1)]
+    rows = np.array(rows)
+    qr = oracle.rope(q, 0, w.rope_base)
+    kr = oracle.rope(k, 0, w.rope_base)
+    want = oracle.attn_rows(qr, kr, v, rows, w.scale)
+    err = float(np.max(np.abs(got[rows[:, 0], rows[:, 1], rows[:, 2]] - want)))
+    say("max abs err over", len(rows), "rows", err)
+    assert err <= TOL[torch.bfloat16]
+
+
+# --------------------------------------------------------------------------
+# bf16 decode (split-K kernels)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tk,d,causal,qo", [
+    (2, 8, 2, 1000, 128, True, 999),
+    (3, 4, 4, 37, 64, True, 36),
+    (1, 16, 1, 5000, 128, True, 4999),      # 16 query heads per K/V head
+    (2, 8, 1, 700, 64, True, 400),          # query earlier than the cache end
+    (1, 6, 2, 1, 128, True, 0),             # one cached key
+    (4, 8, 8, 300, 128, False, 0),          # no mask
+    (1, 2, 1, 20000, 64, True, 19999),      # long cache, few heads: many chunks
+    (1, 24, 2, 513, 128, True, 512),        # 12 query heads per K/V head
+])
+def test_decode_shapes(B, Hq, Hkv, Tk, d, causal, qo):
+    say("decode", B, Hq, Hkv, Tk, d, causal, qo)
+    q, k, v = wl.random_qkv(B, Hq, Hkv, 1, Tk, d, dtype=torch.bfloat16, seed=Tk + Hq)
+    check(q, k, v, 1.0 / math.sqrt(d), causal, qo)
+
+
+def test_decode_workload5_sampled():
+    """The decode workload (B32 Hq32 Hkv8 Tk8192 d128, RoPE-rotated cache):
+    GPU rotates the cache and the new query, then attends; the oracle does
+    the same for three of the 32 sequences."""
+    w = wl.WORKLOADS[5]
+    say("decode", w.name)
+    q, k, v = wl.inputs(w)
+    qd, kd, vd = gpu(q, k, v)
+    ra.rope_apply(kd, None, pos0=0, base=w.rope_base)
+    ra.rope_apply(qd, None, pos0=w.Tk - 1, base=w.rope_base)
+    od = ra.attn_fwd(qd, kd, vd, scale=w.scale, causal=True, q_offset=w.q_offset)
+    torch.cuda.synchronize()
+    got = f64(od)
+    for b in (0, 17, 31):
+        qb = oracle.rope(q[b:b + 1], w.Tk - 1, w.rope_base)
+        kb = oracle.rope(k[b:b + 1], 0, w.rope_base)
+        want = oracle.attn(qb, kb, v[b:b + 1], w.scale, causal=True, q_offset=w.q_offset)
+        err = float(np.max(np.abs(got[b:b + 1] - want)))
+        say("batch", b, "max abs err", err)
+        assert err <= TOL[torch.bfloat16]
+
+
+# --------------------------------------------------------------------------
+# invariants fixed by the pages
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 64), (torch.bfloat16, 64), (torch.bfloat16, 128)])
+def test_row0_is_v0_bit_exact(dtype, d):
+    """Row 0 sees only key 0: its weight is exactly 1 and o_0 = v_0."""
+    say("row0", dtype, d)
+    q, k, v = wl.random_qkv(2, 8, 2, 150, 150, d, dtype=dtype, seed=3)
+    o = run_attn(q, k, v, 1.0 / math.sqrt(d))
+    for hq in range(8):
+        assert torch.equal(o[:, hq, 0], v[:, hq // 4, 0]), hq
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 64), (torch.bfloat16, 64), (torch.bfloat16, 128)])
+def test_causal_prefix_invariance_bit_exact(dtype, d):
+    """Changing token t and later leaves the outputs of rows < t bit-identical
+    (the page's causality check: logits before the changed token differ by
+    exactly 0)."""
+    say("prefix invariance", dtype, d)
+    T, t = 300, 137
+    q, k, v = wl.random_qkv(1, 4, 2, T, T, d, dtype=dtype, seed=8)
+    o1 = run_attn(q, k, v, 0.1)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    g = torch.Generator().manual_seed(9)
+    for x in (q2, k2, v2):
+        x[:, :, t:] = torch.randn(x[:, :, t:].shape, generator=g).to(dtype) * 3
+    o2 = run_attn(q2, k2, v2, 0.1)
+    assert torch.equal(o1[:, :, :t], o2[:, :, :t])
+    assert not torch.equal(o1[:, :, t:], o2[:, :, t:])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_rows_equal_prefill_rows(dtype):
+    """Incremental decode (one query at position t over keys 0..t) equals row
+    t of the one-shot forward; chunked prefill equals the same rows too."""
+    say("decode == prefill", dtype)
+    T, d = 260, 128
+    q, k, v = wl.random_qkv(1, 8, 2, T, T, d, dtype=dtype, seed=21)
+    full = run_attn(q, k, v, 0.0884)
+    tol = 1e-5 if dtype == torch.float32 else 2 * TOL[torch.bfloat16]
+    for t in (0, 1, 63, 64, 127, 200, 259):
+        step = run_attn(q[:, :, t:t + 1], k[:, :, :t + 1], v[:, :, :t + 1], 0.0884, q_offset=t)
+        assert float((step[:, :, 0].double() - full[:, :, t].double()).abs().max()) <= tol
+    for c0, c1 in ((0, 70), (70, 200), (200, 260)):
+        part = run_attn(q[:, :, c0:c1], k[:, :, :c1], v[:, :, :c1], 0.0884, q_offset=c0)
+        assert float((part.double() - full[:, :, c0:c1].double()).abs().max()) <= tol
+
+
+def test_gqa_equals_mha_on_repeat_interleave_bit_exact():
+    """Grouped heads read their K/V head by index: the result is bit-identical
+    to MHA on K/V expanded with repeat_interleave, and differs from the
+    tiled (wrong) expansion."""
+    say("gqa == mha")
+    q, k, v = wl.random_qkv(2, 8, 2, 200, 200, 128, dtype=torch.bfloat16, seed=31)
+    o_gqa = run_attn(q, k, v, 0.0884)
+    o_mha = run_attn(q, k.repeat_interleave(4, dim=1), v.repeat_interleave(4, dim=1), 0.0884)
+    o_bad = run_attn(q, k.repeat(1, 4, 1, 1), v.repeat(1, 4, 1, 1), 0.0884)
+    assert torch.equal(o_gqa, o_mha)
+    assert float((o_gqa.double() - o_bad.double()).abs().max()) > 0.1
+
+
+@pytest.mark.parametrize("dtype,Tq", [(torch.float32, 90), (torch.bfloat16, 300), (torch.bfloat16, 1)])
+def test_constant_values_give_constant_output(dtype, Tq):
+    """Weights of a row sum to 1, so V = 1 gives O = 1."""
+    say("V=1", dtype, Tq)
+    q, k, _ = wl.random_qkv(2, 4, 2, Tq, 300, 128, dtype=dtype, seed=41)
+    v = torch.ones(2, 2, 300, 128, dtype=dtype)
+    o = run_attn(q, k, v, 0.0884, q_offset=300 - Tq)
+    tol = 1e-6 if dtype == torch.float32 else 2.0 ** -8
+    assert float((o.double() - 1.0).abs().max()) <= tol
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 64), (torch.bfloat16, 64), (torch.bfloat16, 128)])
+def test_softmax_worked_example(dtype, d):
+    """softmax([2, 1, 0]) ~ [0.665, 0.245, 0.090]: with v_j = e_j the output
+    row is the weight row."""
+    say("worked example", dtype, d)
+    q = torch.zeros(1, 1, 3, d); k = torch.zeros(1, 1, 3, d); v = torch.zeros(1, 1, 3, d)
+    q[0, 0, 2, 0] = 1.0
+    for j, s in enumerate((2.0, 1.0, 0.0)):
+        k[0, 0, j, 0] = s
+        v[0, 0, j, j] = 1.0
+    o = run_attn(q.to(dtype), k.to(dtype), v.to(dtype), 1.0)
+    w = o[0, 0, 2, :3].double().numpy()
+    tol = 5e-4 + (1e-5 if dtype == torch.float32 else 2.0 ** -8)
+    assert np.all(np.abs(w - np.array([0.665, 0.245, 0.090])) <= tol), w
+
+
+@pytest.mark.parametrize("dtype,Tq,Tk,qo", [(torch.float32, 100, 100, 0), (torch.bfloat16, 300, 300, 0),
+                                            (torch.bfloat16, 1, 3000, 2999),
+                                            (torch.bfloat16, 50, 250, 200)])
+def test_lse_matches_oracle(dtype, Tq, Tk, qo):
+    say("lse", dtype, Tq, Tk, qo)
+    q, k, v = wl.random_qkv(1, 8, 2, Tq, Tk, 128, dtype=dtype, seed=51)
+    o, lse = run_attn(q, k, v, 0.0884, q_offset=qo, lse=True)
+    want_o, want_lse = oracle.attn(q, k, v, 0.0884, q_offset=qo, return_lse=True)
+    assert float(np.max(np.abs(f64(o) - want_o))) <= TOL[dtype]
+    assert float(np.max(np.abs(lse.double().numpy() - want_lse))) <= 1e-4
+
+
+def test_bf16_deterministic():
+    say("determinism")
+    q, k, v = wl.random_qkv(2, 8, 2, 333, 333, 128, dtype=torch.bfloat16, seed=61)
+    a = run_attn(q, k, v, 0.0884)
+    b = run_attn(q, k, v, 0.0884)
+    assert torch.equal(a, b)
+    qd, kd, vd = wl.random_qkv(4, 8, 2, 1, 4000, 128, dtype=torch.bfloat16, seed=62)
+    assert torch.equal(run_attn(qd, kd, vd, 0.0884, q_offset=3999),
+                       run_attn(qd, kd, vd, 0.0884, q_offset=3999))
+
+
+def test_decode_with_caller_workspace_matches_internal():
+    say("decode ws vs internal")
+    q, k, v = wl.random_qkv(4, 16, 4, 1, 3000, 128, dtype=torch.bfloat16, seed=71)
+    a = run_attn(q, k, v, 0.0884, q_offset=2999)
+    b, _ = run_attn(q, k, v, 0.0884, q_offset=2999, lse=True)
+    assert torch.equal(a, b)

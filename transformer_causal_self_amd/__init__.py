@@ -1,0 +1,181 @@
+"""Python binding of librocattn, the gfx950 causal attention library.
+
+Argument marshalling only: every function here checks that the torch
+tensors it is given are device tensors of the right dtype, shape and
+layout, takes their pointers and the current HIP stream, and calls the C
+ABI declared in ``include/rocattn.h``.  All arithmetic runs in the HIP
+kernels; there is no fallback.  When ``librocattn.so`` has not been built,
+or a call is made with CPU tensors, the call raises.
+
+    attn_fwd(q, k, v, o=None, scale=None, causal=True, q_offset=0)
+    attn_fwd_ws(q, k, v, o, workspace, lse=None, scale=None, causal=True, q_offset=0)
+    attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype)
+    rope_apply(q, k=None, pos0=0, base=10000.0)
+    status_string(code)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "librocattn.so")
+
+# the C ABI, as declared in include/rocattn.h
+SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_workspace_bytes", "rope_apply",
+           "attn_status_string")
+
+F32, BF16 = 0, 1
+OK = 0
+STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_DTYPE", -4: "ERR_HEADDIM",
+          -5: "ERR_OFFSET", -6: "ERR_SCALE", -7: "ERR_ALIGN", -8: "ERR_WORKSPACE",
+          -9: "ERR_HIP"}
+
+
+class RocattnError(RuntimeError):
+    """A librocattn entry point returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded librocattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(
+                f"{LIBRARY} is missing: build it with `python -m transformer_causal_self_amd.build` "
+                "(or __graft_entry__.build()); there is no fallback implementation")
+        lib = ctypes.CDLL(LIBRARY)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.attn_fwd.restype = i
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+        lib.attn_fwd_ws.restype = i
+        lib.attn_fwd_ws.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, vp, sz, vp]
+        lib.attn_workspace_bytes.restype = sz
+        lib.attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        lib.rope_apply.restype = i
+        lib.rope_apply.argtypes = [vp, vp, i, i, i, i, i, i, ctypes.c_double, i, vp]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_status_string.argtypes = [i]
+        _lib = lib
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return library().attn_status_string(int(code)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16 only")
+
+
+def _check_dev(name, t, dtype=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device}); "
+                         "there is no CPU implementation")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream(t, stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _fwd_args(q, k, v, o, scale, causal, q_offset):
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_dev(n, t, q.dtype)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.shape != q.shape:
+        raise ValueError("q, o: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]")
+    B, Hq, Tq, d = q.shape
+    Bk, Hkv, Tk, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return (B, Hq, Hkv, Tq, Tk, d, float(scale), int(bool(causal)), int(q_offset),
+            _dtype_code(q))
+
+
+def attn_fwd(q, k, v, o=None, scale=None, causal=True, q_offset=0, stream=None):
+    """softmax(scale q k^T + M) v on the GPU; returns o ([B, Hq, Tq, d])."""
+    import torch
+    if o is None:
+        o = torch.empty_like(q)
+    B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt = _fwd_args(q, k, v, o, scale, causal, q_offset)
+    st = library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, d, sc, ca,
+                            qo, dt, _stream(q, stream))
+    if st != OK:
+        raise RocattnError("attn_fwd", st)
+    return o
+
+
+def attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype) -> int:
+    if not isinstance(dtype, int):
+        import torch
+        dtype = F32 if dtype == torch.float32 else BF16
+    return int(library().attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype))
+
+
+def attn_fwd_ws(q, k, v, o, workspace=None, lse=None, scale=None, causal=True, q_offset=0,
+                stream=None):
+    """attn_fwd with a caller-owned workspace (a uint8 GPU tensor, or None when
+    attn_workspace_bytes() is 0) and an optional float32 lse [B, Hq, Tq]."""
+    import torch
+    B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt = _fwd_args(q, k, v, o, scale, causal, q_offset)
+    ws_bytes = 0
+    if workspace is not None:
+        _check_dev("workspace", workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, Hq, Tq):
+            raise ValueError("lse must be [B, Hq, Tq]")
+    st = library().attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, d, sc, ca,
+                               qo, dt, _stream(q, stream), _ptr(workspace), ws_bytes, _ptr(lse))
+    if st != OK:
+        raise RocattnError("attn_fwd_ws", st)
+    return o
+
+
+def rope_apply(q, k=None, pos0=0, base=10000.0, stream=None):
+    """Rotate q (and k) in place by position pos0 + t (split-half pairing)."""
+    _check_dev("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, Hq, T, d]")
+    B, Hq, T, d = q.shape
+    Hkv = 0
+    if k is not None:
+        _check_dev("k", k, q.dtype)
+        if k.dim() != 4 or k.shape[0] != B or k.shape[2] != T or k.shape[3] != d:
+            raise ValueError("k must be [B, Hkv, T, d] with q's B, T and d")
+        Hkv = k.shape[1]
+    st = library().rope_apply(_ptr(q), _ptr(k), B, Hq, Hkv, T, d, int(pos0), float(base),
+                              _dtype_code(q), _stream(q, stream))
+    if st != OK:
+        raise RocattnError("rope_apply", st)
+    return q, k

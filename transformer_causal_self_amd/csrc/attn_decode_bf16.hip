@@ -1,0 +1,309 @@
+// attn_decode_bf16.hip -- one-token decode step over a key/value cache,
+// bf16 in/out, float32 accumulation.  Head size 64 or 128, up to 16 query
+// heads per K/V head.
+//
+// A decode step computes one new query row per query head at position
+// q_offset (cache.pos) against the cached keys 0 .. q_offset ("The
+// Transformer architecture" -- Hands-on; "Transformer" (ai-notes) -- Notes on
+// compute: the KV cache makes each new token step incremental).  The work is
+// dominated by reading the cache once, so the kernels are built for HBM
+// bandwidth, not arithmetic:
+//
+//  * Split-K: the visible keys of each (batch, K/V head) are cut into chunks
+//    and each chunk is one workgroup, so thousands of workgroups stream the
+//    cache at once.  A workgroup serves all n_rep query heads of its K/V
+//    head ("The Transformer architecture" -- GQA), so every K/V byte is read
+//    exactly once.
+//  * Scores: one v_mfma_f32_16x16x32_bf16 per 32 channels takes 16 keys
+//    straight from the 16-byte global loads (the B operand is a key row) and
+//    the query heads as the A operand, so no key is staged or converted.
+//  * The chunk's scores (base-2 exponent units) sit in LDS; the chunk max
+//    and the weights 2^(t - m) are formed there exactly once, then each lane
+//    streams 8 channels of one value row and accumulates weight x value for
+//    every query head in float32.
+//  * Each chunk writes its unnormalised output, its max m and its weight sum
+//    l; a second small kernel merges the chunks of a row with
+//        o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s,
+//    which equals the softmax over the whole row.
+#include <math.h>
+
+#include "internal.hpp"
+
+namespace rocattn {
+namespace {
+
+constexpr int kSplitTarget = 4096;  // workgroups the split aims for in total
+constexpr int kLdsFloats = 16384;   // 64 KiB of LDS per workgroup at most
+
+struct DecArgs {
+    const bf16* q;
+    const bf16* k;
+    const bf16* v;
+    float* o_part;   // [B*Hq][S][D]
+    float* ml;       // [B*Hq][S][2]  (max in base-2 units, weight sum)
+    int Hq, Hkv, Tk;
+    int R;           // query heads per K/V head
+    int kv_len;      // visible keys (keys 0 .. kv_len-1)
+    int C;           // keys per chunk (multiple of 64)
+    int S;           // chunks per (batch, K/V head)
+    float c;         // |scale| * log2(e)
+    unsigned neg;    // sign flip for q when scale < 0
+};
+
+struct CombArgs {
+    const float* o_part;
+    const float* ml;
+    bf16* o;
+    float* lse;
+    int S;
+};
+
+template <int D, int RP>  // RP: query heads per K/V head, padded to 4, 8 or 16
+__global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
+    extern __shared__ float dsm[];
+    float* St = dsm;                  // [RP][C] scores (base-2 units)
+    float* Pl = dsm + RP * a.C;       // [C][RP] weights
+    float* Red = Pl + RP * a.C;       // [4][RP][D] per-wave partial outputs
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int s = blockIdx.x % a.S;
+    const int g = blockIdx.x / a.S;                  // b * Hkv + hk
+    const int b = g / a.Hkv, hk = g - (g / a.Hkv) * a.Hkv;
+    const int j_begin = s * a.C;
+    const int nkeys = min(a.kv_len, j_begin + a.C) - j_begin;   // >= 1
+    const size_t kv_head = (size_t)g * a.Tk * D;
+    const int hq0 = hk * a.R;
+
+    // ---- query heads as the A operand: lane (rho, quarter) holds
+    //      q[hq0 + rho][DL*quarter + 8m .. +7]; the same channel order is
+    //      used for the key rows, so the products are unchanged.
+    constexpr int NM = D / 32;
+    constexpr int DL = D / 4;
+    const int rho = lane & 15, quarter = lane >> 4;
+    bf16x8 qa[NM];
+    {
+        const bool ok = rho < a.R;
+        const uint4* src = reinterpret_cast<const uint4*>(
+            a.q + (size_t)(b * a.Hq + hq0 + (ok ? rho : 0)) * D + DL * quarter);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            uint4 u = src[m];
+            if (!ok) u = make_uint4(0, 0, 0, 0);
+            u.x ^= a.neg; u.y ^= a.neg; u.z ^= a.neg; u.w ^= a.neg;
+            qa[m] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+
+    // ---- phase 1: scores of 16 keys per MFMA group
+    const int ngroups = (nkeys + 15) >> 4;
+    const bf16* kbase = a.k + kv_head + DL * quarter;
+#pragma unroll 2
+    for (int gi = wave; gi < ngroups; gi += 4) {
+        const int kl = gi * 16 + rho;            // key (local) whose row this lane loads
+        const bool kvalid = kl < nkeys;
+        const uint4* kp = reinterpret_cast<const uint4*>(
+            kbase + (size_t)(j_begin + (kvalid ? kl : 0)) * D);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, kp[m]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], kf, acc, 0, 0, 0);
+        }
+        // acc[r] = score of query head 4*quarter + r against key gi*16 + rho
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * quarter + r;
+            if (row < RP && row < a.R) St[row * a.C + kl] = kvalid ? acc[r] * a.c : -INFINITY;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: chunk max and weights, one wave per query head
+    for (int row = wave; row < a.R; row += 4) {
+        const float* sr = St + row * a.C;
+        float mx = -INFINITY;
+        for (int j = lane; j < nkeys; j += 64) mx = fmaxf(mx, sr[j]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        float sum = 0.f;
+        for (int j = lane; j < nkeys; j += 64) {
+            const float p = exp2f(sr[j] - mx);
+            Pl[j * RP + row] = p;
+            sum += p;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+        if (lane == 0) {
+            float* mlp = a.ml + ((size_t)(b * a.Hq + hq0 + row) * a.S + s) * 2;
+            mlp[0] = mx;
+            mlp[1] = sum;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: weighted sum of value rows, 8 channels per lane
+    constexpr int LPK = D / 8;       // lanes per value row
+    constexpr int KPW = 64 / LPK;    // value rows per wave per step
+    const int kk = lane / LPK, col = (lane % LPK) * 8;
+    float acc[RP][8];
+#pragma unroll
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+    const bf16* vbase = a.v + kv_head + (size_t)j_begin * D + col;
+#pragma unroll 4
+    for (int j = wave * KPW + kk; j < nkeys; j += 4 * KPW) {
+        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vbase + (size_t)j * D);
+        float vf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = (float)vv[e];
+        const float* pr = Pl + j * RP;
+#pragma unroll
+        for (int r4 = 0; r4 < RP; r4 += 4) {
+            const float4 p4 = *reinterpret_cast<const float4*>(pr + r4);
+            const float pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[r4 + u][e] = fmaf(pp[u], vf[e], acc[r4 + u][e]);
+        }
+    }
+    // lanes that share `col` hold different keys: fold them together
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1)
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[r][e] += __shfl_xor(acc[r][e], off);
+    if (kk == 0) {
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; e += 4)
+                *reinterpret_cast<float4*>(Red + (wave * RP + r) * D + col + e) =
+                    make_float4(acc[r][e], acc[r][e + 1], acc[r][e + 2], acc[r][e + 3]);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < a.R * D; idx += 256) {
+        const int r = idx / D, dd = idx - r * D;
+        const float sum = Red[(0 * RP + r) * D + dd] + Red[(1 * RP + r) * D + dd] +
+                          Red[(2 * RP + r) * D + dd] + Red[(3 * RP + r) * D + dd];
+        a.o_part[((size_t)(b * a.Hq + hq0 + r) * a.S + s) * D + dd] = sum;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(CombArgs a) {
+    const size_t row = blockIdx.x;             // b * Hq + hq
+    const int col = threadIdx.x;
+    const float* mlr = a.ml + row * a.S * 2;
+    float M = -INFINITY;
+    for (int s = 0; s < a.S; ++s) M = fmaxf(M, mlr[2 * s]);
+    float den = 0.f, acc = 0.f;
+    const float* op = a.o_part + row * a.S * D + col;
+    for (int s = 0; s < a.S; ++s) {
+        const float w = exp2f(mlr[2 * s] - M);
+        den = fmaf(w, mlr[2 * s + 1], den);
+        acc = fmaf(w, op[(size_t)s * D], acc);
+    }
+    a.o[row * D + col] = (bf16)(acc / den);
+    if (a.lse && col == 0) a.lse[row] = (M + log2f(den)) * kLn2;
+}
+
+int pad_r(int R) { return R <= 4 ? 4 : (R <= 8 ? 8 : 16); }
+
+// longest chunk whose scores, weights and partial outputs fit the LDS cap
+int chunk_max(int R, int D) {
+    const int rp = pad_r(R);
+    return ((kLdsFloats - 4 * rp * D) / (2 * rp)) & ~63;
+}
+
+int split_target(int G) {
+    const int s = (kSplitTarget + G - 1) / G;
+    return s < 1 ? 1 : s;
+}
+
+// chunk length and split count for kv_len visible keys
+void plan(int G, int R, int D, int kv_len, int* C_out, int* S_out) {
+    const int c_max = chunk_max(R, D);
+    const int s_target = split_target(G);
+    int C = (kv_len + s_target - 1) / s_target;
+    C = (C + 63) & ~63;
+    if (C < 64) C = 64;
+    if (C > c_max) C = c_max;
+    *C_out = C;
+    *S_out = (kv_len + C - 1) / C;
+}
+
+template <int D, int RP>
+hipError_t launch_split(const DecArgs& a, int grid, hipStream_t stream) {
+    const size_t lds = sizeof(float) * ((size_t)2 * RP * a.C + (size_t)4 * RP * D);
+    hipLaunchKernelGGL((decode_split_kernel<D, RP>), dim3(grid), dim3(256), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dec_d(const FwdParams& p, float* o_part, float* ml, int C, int S,
+                        int kv_len, hipStream_t stream) {
+    DecArgs a;
+    a.q = static_cast<const bf16*>(p.q);
+    a.k = static_cast<const bf16*>(p.k);
+    a.v = static_cast<const bf16*>(p.v);
+    a.o_part = o_part;
+    a.ml = ml;
+    a.Hq = p.Hq; a.Hkv = p.Hkv; a.Tk = p.Tk;
+    a.R = p.Hq / p.Hkv;
+    a.kv_len = kv_len;
+    a.C = C; a.S = S;
+    a.c = fabsf(p.scale) * kLog2e;
+    a.neg = p.scale < 0.f ? 0x80008000u : 0u;
+    const int grid = p.B * p.Hkv * S;
+    const int rp = pad_r(a.R);
+    hipError_t e = rp == 4 ? launch_split<D, 4>(a, grid, stream)
+                 : rp == 8 ? launch_split<D, 8>(a, grid, stream)
+                           : launch_split<D, 16>(a, grid, stream);
+    if (e != hipSuccess) return e;
+    CombArgs c;
+    c.o_part = o_part;
+    c.ml = ml;
+    c.o = static_cast<bf16*>(p.o);
+    c.lse = p.lse;
+    c.S = S;
+    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(p.B * p.Hq), dim3(D), 0, stream, c);
+    return hipGetLastError();
+}
+
+int visible_keys(int Tk, int causal, int q_offset) {
+    return causal ? (q_offset + 1 < Tk ? q_offset + 1 : Tk) : Tk;
+}
+
+}  // namespace
+
+bool decode_bf16_supported(int Hq, int Hkv, int d) {
+    return (d == 64 || d == 128) && Hq / Hkv <= 16;
+}
+
+// Bytes for any call with at most Tk visible keys: the split count never
+// exceeds max(split_target, ceil(Tk / chunk_max)).
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Tk, int d) {
+    const int s_target = split_target(B * Hkv);
+    const int c_max = chunk_max(Hq / Hkv, d);
+    int S = (Tk + c_max - 1) / c_max;
+    if (S < s_target) S = s_target;
+    return sizeof(float) * (size_t)B * Hq * S * (d + 2);
+}
+
+hipError_t launch_decode_bf16(const FwdParams& p, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+    const int kv_len = visible_keys(p.Tk, p.causal, p.q_offset);
+    int C, S;
+    plan(p.B * p.Hkv, p.Hq / p.Hkv, p.d, kv_len, &C, &S);
+    const size_t need = sizeof(float) * (size_t)p.B * p.Hq * S * (p.d + 2);
+    if (ws_bytes < need) return hipErrorInvalidValue;
+    float* o_part = static_cast<float*>(workspace);
+    float* ml = o_part + (size_t)p.B * p.Hq * S * p.d;
+    if (p.d == 64) return launch_dec_d<64>(p, o_part, ml, C, S, kv_len, stream);
+    return launch_dec_d<128>(p, o_part, ml, C, S, kv_len, stream);
+}
+
+}  // namespace rocattn

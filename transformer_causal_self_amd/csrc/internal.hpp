@@ -1,0 +1,51 @@
+// internal.hpp -- types and launcher declarations shared by the kernels and
+// the host-side API of librocattn.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rocattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Everything a forward launch needs, validated by the host API.
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;      // may be null
+    int B, Hq, Hkv, Tq, Tk, d;
+    float scale;
+    int causal;
+    int q_offset;
+};
+
+// Prefill (any Tq) bf16 MFMA kernel; d in {64, 128}.
+hipError_t launch_prefill_bf16(const FwdParams& p, hipStream_t stream);
+
+// Split-K decode (Tq == 1) bf16 kernels; d in {64, 128}, Hq / Hkv <= 16.
+bool decode_bf16_supported(int Hq, int Hkv, int d);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Tk, int d);
+hipError_t launch_decode_bf16(const FwdParams& p, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+// Generic float32 kernel; d <= 256, d % 4 == 0.
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+
+// RoPE in place; dtype 0 = f32, 1 = bf16.  x has nvec = rows of d elements,
+// grouped as [nrow_groups][T][d] with token t at position pos0 + t.
+hipError_t launch_rope(void* x, long long n_seq, int T, int d, int pos0, double base,
+                       int dtype, hipStream_t stream);
+
+}  // namespace rocattn

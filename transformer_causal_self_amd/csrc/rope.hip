@@ -1,0 +1,126 @@
+// rope.hip -- rotary position embedding applied in place to q and k.
+//
+// Token t of a sequence sits at position pos = pos0 + t ("The Transformer
+// architecture" -- Hands-on: RoPE is sliced from cache.pos).  Channel pair p
+// of a head vector is (p, p + d/2) (split-half pairing, "The Transformer
+// architecture" -- Now: RoPE, apply_rope) and turns by
+// theta_p = pos * base^(-2p/d) ("Transformer" (ai-notes) -- RoPE) through
+// [[cos, -sin], [sin, cos]].
+//
+// The angle table is not stored in HBM: each lane forms, in double
+// precision, the cosine and sine of the few pairs it owns at one position,
+// rounds them once to float32, and then rotates that (position, pairs) slot
+// in every head and batch entry of its share.  The work is HBM-bound
+// (one read and one write of q and k); each lane moves 2 x 8 bytes (bf16) or
+// 2 x 16 bytes (f32) per head row, with neighbouring lanes on neighbouring
+// pairs so every head row is read and written by full, coalesced segments.
+#include <math.h>
+
+#include "internal.hpp"
+
+namespace rocattn {
+namespace {
+
+constexpr int kThreads = 256;
+
+// NP consecutive elements of type T, moved as one load / store.
+template <typename T, int NP>
+struct __attribute__((aligned(sizeof(T) * NP))) Pack {
+    T e[NP];
+};
+
+template <typename T, int NP>
+__device__ inline void load_f32(const T* src, float* f) {
+    Pack<T, NP> v = *reinterpret_cast<const Pack<T, NP>*>(src);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) f[u] = (float)v.e[u];
+}
+
+template <typename T, int NP>
+__device__ inline void store_f32(T* dst, const float* f) {
+    Pack<T, NP> v;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) v.e[u] = (T)f[u];
+    *reinterpret_cast<Pack<T, NP>*>(dst) = v;
+}
+
+// grid.x: (token, pair-group) slots; grid.y: chunks of the n_seq head rows.
+template <typename T, int kPairs>  // kPairs channel pairs per lane
+__global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long long n_seq,
+                                                        int rows_per_chunk, int T_len, int d,
+                                                        int pos0, double neg_log2_base_over_half) {
+    const int half = d >> 1;
+    const int groups = half / kPairs;  // lanes per token
+    const long long slot = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (slot >= (long long)T_len * groups) return;
+    const int t = (int)(slot / groups);
+    const int p0 = (int)(slot - (long long)t * groups) * kPairs;
+
+    float cs[kPairs], sn[kPairs];
+    const double pos = (double)pos0 + (double)t;
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) {
+        // base^(-2p/d) = 2^(-(p / (d/2)) * log2(base))
+        const double inv_freq = exp2((double)(p0 + u) * neg_log2_base_over_half);
+        double s, c;
+        sincos(pos * inv_freq, &s, &c);
+        cs[u] = (float)c;
+        sn[u] = (float)s;
+    }
+
+    const long long r0 = (long long)blockIdx.y * rows_per_chunk;
+    const long long r1 = min(n_seq, r0 + rows_per_chunk);
+    const size_t row_stride = (size_t)T_len * d;
+    T* base = x + (size_t)t * d + p0;
+#pragma unroll 4
+    for (long long r = r0; r < r1; ++r) {
+        T* lo = base + (size_t)r * row_stride;
+        T* hi = lo + half;
+        float x1[kPairs], x2[kPairs], y1[kPairs], y2[kPairs];
+        load_f32<T, kPairs>(lo, x1);
+        load_f32<T, kPairs>(hi, x2);
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u) {
+            y1[u] = x1[u] * cs[u] - x2[u] * sn[u];
+            y2[u] = x1[u] * sn[u] + x2[u] * cs[u];
+        }
+        store_f32<T, kPairs>(lo, y1);
+        store_f32<T, kPairs>(hi, y2);
+    }
+}
+
+template <typename T, int kPairs>
+hipError_t launch_rope_t(T* x, long long n_seq, int T_len, int d, int pos0, double base,
+                         hipStream_t stream) {
+    const int half = d / 2;
+    const int groups = half / kPairs;
+    const long long slots = (long long)T_len * groups;
+    const long long gx = (slots + kThreads - 1) / kThreads;
+    // split the head rows so the launch has enough workgroups to fill the chip
+    long long gy = (2048 + gx - 1) / gx;
+    if (gy > n_seq) gy = n_seq;
+    if (gy < 1) gy = 1;
+    const int rows_per_chunk = (int)((n_seq + gy - 1) / gy);
+    gy = (n_seq + rows_per_chunk - 1) / rows_per_chunk;
+    const double neg = -log2(base) / (double)half;
+    dim3 grid((unsigned)gx, (unsigned)gy);
+    hipLaunchKernelGGL((rope_kernel<T, kPairs>), grid, dim3(kThreads), 0, stream,
+                       x, n_seq, rows_per_chunk, T_len, d, pos0, neg);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rope(void* x, long long n_seq, int T_len, int d, int pos0, double base,
+                       int dtype, hipStream_t stream) {
+    // four pairs per lane (8-byte bf16 / 16-byte f32 accesses) when the half
+    // head size allows it, else one pair per lane
+    const bool wide = (d / 2) % 4 == 0;
+    if (dtype == 0)
+        return wide ? launch_rope_t<float, 4>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, stream)
+                    : launch_rope_t<float, 1>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, stream);
+    return wide ? launch_rope_t<bf16, 4>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, stream)
+                : launch_rope_t<bf16, 1>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, stream);
+}
+
+}  // namespace rocattn
