@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+                    [--no-also] [--no-cpu] [--cpu-seconds S]
+
+A step is one pass of the hot path over one batch of the workload's seeded
+synthetic inputs, resident in HBM before timing starts:
+    RoPE on q and k (workloads with RoPE), then the fused causal attention
+    forward (prefill), or the split-K decode step (decode workload).
+The headline workload (default 2: bf16 B8 H12 T1024 d64, causal MHA) is timed
+for K steps between HIP events on the stream the kernels run on, after W
+warm-up steps; the JSON line reports causal-adjusted TFLOP/s.
+
+FLOPs (causal-adjusted): 4 * B * Hq * d * N_vis, N_vis = sum_i min(Tk,
+q_offset + i + 1), i.e. two matrix products over the visible (query, key)
+pairs only.  Algorithmic bytes of attention: elt * d * (2 B Hq Tq + 2 B Hkv Tk)
+(q and o once, k and v once per K/V head).  RoPE bytes: read + write of q
+and k.
+
+Also printed in the same line (unless --no-also): the other workloads'
+per-kernel rates, each timed the same way, so every part of the path has a
+live number; and a CPU baseline: the fp64 oracle timed on the host cores
+on a bounded sample of the headline workload.
+
+--calib-copy runs only a plain device copy of a known size (used to scale
+the HBM byte counters of a profiler run).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+KERNEL_SOURCES = {
+    "prefill_bf16": "transformer_causal_self_amd/csrc/attn_prefill_bf16.hip",
+    "decode_bf16": "transformer_causal_self_amd/csrc/attn_decode_bf16.hip",
+    "rope": "transformer_causal_self_amd/csrc/rope.hip",
+    "attn_f32": "transformer_causal_self_amd/csrc/attn_f32.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def n_visible(Tq, Tk, causal, q_offset):
+    if not causal:
+        return Tq * Tk
+    return sum(min(Tk, q_offset + i + 1) for i in range(Tq))
+
+
+def attn_flops(w):
+    return 4.0 * w.B * w.Hq * w.d * n_visible(w.Tq, w.Tk, w.causal, w.q_offset)
+
+
+def elt_bytes(w):
+    return 4 if w.dtype == "f32" else 2
+
+
+def attn_bytes(w):
+    return elt_bytes(w) * w.d * (2.0 * w.B * w.Hq * w.Tq + 2.0 * w.B * w.Hkv * w.Tk)
+
+
+def rope_bytes(w, decode):
+    e = elt_bytes(w)
+    if decode:  # only the new query rows are rotated during the step
+        return 2.0 * e * w.d * w.B * w.Hq * w.Tq
+    return 2.0 * e * w.d * w.Tq * w.B * (w.Hq + w.Hkv)
+
+
+def source_hash(kernel):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload_name):
+    """HBM bytes per launch from the committed profiler counters, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[f"{kernel}:{workload_name}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the current stream around n launches of fn()."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, n, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n  # ms
+
+
+def setup(w, torch, ra, wl, dev):
+    """Device inputs and the step callables of workload w."""
+    q, k, v = wl.inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    od = torch.empty_like(qd)
+    decode = w.Tq == 1 and w.dtype == "bf16"
+    ws_b = ra.attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, w.torch_dtype)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev) if ws_b else None
+    if w.rope and decode:
+        ra.rope_apply(kd, None, pos0=0, base=w.rope_base)  # the cache arrives rotated
+        torch.cuda.synchronize()
+
+    def attn():
+        ra.attn_fwd_ws(qd, kd, vd, od, ws, None, scale=w.scale, causal=w.causal,
+                       q_offset=w.q_offset)
+
+    if w.rope and decode:
+        def rope():
+            ra.rope_apply(qd, None, pos0=w.q_offset, base=w.rope_base)
+    elif w.rope:
+        def rope():
+            ra.rope_apply(qd, kd, pos0=0, base=w.rope_base)
+    else:
+        rope = None
+
+    def step():
+        if rope is not None:
+            rope()
+        attn()
+
+    return dict(step=step, attn=attn, rope=rope, decode=decode)
+
+
+def measure(w, args, torch, ra, wl, dev, steps, warmup):
+    s = setup(w, torch, ra, wl, dev)
+    timer = Timer(torch)
+    ms_step = timer(s["step"], steps, warmup)
+    ms_attn = timer(s["attn"], steps, warmup)
+    out = dict(workload=w.name, ms_per_step=ms_step, attn_ms=ms_attn)
+    fl = attn_flops(w)
+    by = attn_bytes(w)
+    kernel = "decode_bf16" if s["decode"] else ("attn_f32" if w.dtype == "f32" else "prefill_bf16")
+    out["attn_kernel"] = kernel
+    out["attn_tflops"] = fl / (ms_attn * 1e-3) / 1e12
+    out["attn_gbs"] = by / (ms_attn * 1e-3) / 1e9
+    peak_flops = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    out["attn_pct_mfma_peak"] = 100.0 * out["attn_tflops"] / peak_flops
+    out["attn_pct_hbm_peak"] = 100.0 * out["attn_gbs"] / PEAK_HBM_GBS
+    if s["rope"] is not None:
+        ms_rope = timer(s["rope"], steps, warmup)
+        rb = rope_bytes(w, s["decode"])
+        out["rope_ms"] = ms_rope
+        out["rope_gbs"] = rb / (ms_rope * 1e-3) / 1e9
+        out["rope_pct_hbm_peak"] = 100.0 * out["rope_gbs"] / PEAK_HBM_GBS
+    out["step_flops"] = fl
+    out["attn_bytes"] = by
+    del s
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle on the host cores, on a bounded sample of workload w:
+    whole passes over the workload when one pass fits the time budget, else
+    an evenly spread sample of query rows (each with all its visible keys)."""
+    import numpy as np
+
+    import oracle
+    from transformer_causal_self_amd import workloads as wl
+
+    q, k, v = wl.inputs(w)
+    q64 = q.double().numpy(); k64 = k.double().numpy(); v64 = v.double().numpy()
+    del q, k, v
+    orc = oracle.default()
+    if w.rope:
+        k64 = orc.rope(k64, 0, w.rope_base)
+        q64 = orc.rope(q64, w.q_offset, w.rope_base)
+    full_flops = attn_flops(w)
+    # calibrate on a small row sample
+    rng = np.random.default_rng(0)
+    n_rows = w.B * w.Hq * w.Tq
+    probe = min(n_rows, 512)
+    idx = rng.choice(n_rows, size=probe, replace=False)
+    rows = np.stack([idx // (w.Hq * w.Tq), (idx // w.Tq) % w.Hq, idx % w.Tq], axis=1)
+    t0 = time.perf_counter()
+    orc.attn_rows(q64, k64, v64, rows, w.scale, causal=w.causal, q_offset=w.q_offset)
+    t_probe = time.perf_counter() - t0
+    est_full = t_probe * n_rows / probe
+    flops_done = 0.0
+    t_total = 0.0
+    if est_full <= seconds:
+        passes = 0
+        while True:
+            t0 = time.perf_counter()
+            orc.attn(q64, k64, v64, w.scale, causal=w.causal, q_offset=w.q_offset)
+            t_total += time.perf_counter() - t0
+            flops_done += full_flops
+            passes += 1
+            if t_total >= seconds or passes >= 50:
+                break
+        sample = f"{passes} full pass(es) over the workload ({w.B * w.Hq * w.Tq} query rows)"
+    else:
+        n = max(1, int(n_rows * seconds / est_full))
+        idx = np.linspace(0, n_rows - 1, n).astype(np.int64)
+        rows = np.stack([idx // (w.Hq * w.Tq), (idx // w.Tq) % w.Hq, idx % w.Tq], axis=1)
+        t0 = time.perf_counter()
+        orc.attn_rows(q64, k64, v64, rows, w.scale, causal=w.causal, q_offset=w.q_offset)
+        t_total = time.perf_counter() - t0
+        vis = [min(w.Tk, w.q_offset + int(i) + 1) if w.causal else w.Tk for i in rows[:, 2]]
+        flops_done = 4.0 * w.d * float(sum(vis))
+        sample = f"{n} of {n_rows} query rows, evenly spaced, all visible keys each"
+    return {"value": flops_done / t_total / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.threads_used(), "kind": "oracle",
+            "sample": f"{sample}; {t_total:.1f} s of fp64 work"}
+
+
+def calib_copy(torch, dev, nbytes=1 << 30, reps=5):
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": nbytes, "calib_copy_bytes_written": nbytes,
+                      "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-also", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_causal_self_amd as ra
+    from transformer_causal_self_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ra.library()
+    dev = torch.device("cuda:0")
+    if args.calib_copy:
+        calib_copy(torch, dev)
+        return
+
+    w = wl.WORKLOADS[args.workload]
+    head = measure(w, args, torch, ra, wl, dev, args.steps, args.warmup)
+    print(f"# {w.name}: step {head['ms_per_step'] * 1e3:.2f} us, attention "
+          f"{head['attn_ms'] * 1e3:.2f} us = {head['attn_tflops']:.1f} TFLOP/s", file=sys.stderr)
+
+    decode = head["attn_kernel"] == "decode_bf16"
+    step_s = head["ms_per_step"] * 1e-3
+    if decode:
+        metric_val = head["attn_bytes"] / step_s / 1e9
+        unit = "GB/s"
+    else:
+        metric_val = head["step_flops"] / step_s / 1e12
+        unit = "TFLOP/s"
+
+    # roofline of the dominant kernel, from its own event-timed launches
+    kernel = head["attn_kernel"]
+    if decode:
+        achieved = head["attn_gbs"]
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        achieved = head["attn_tflops"]
+        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved,
+                "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
+    roof["kernel"] = kernel
+    roof["launch_us"] = head["attn_ms"] * 1e3
+    roof["algorithmic_bytes"] = head["attn_bytes"]
+    roof["algorithmic_flops"] = head["step_flops"]
+    roof["traffic"] = measured_traffic(kernel, w.name)
+
+    line = {
+        "metric": "causal attention TFLOP/s + % bf16 MFMA peak (prefill); GB/s + % HBM (decode)",
+        "value": metric_val,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded N(0, sigma^2) q/k/v, see transformer_causal_self_amd/workloads.py)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tq": w.Tq,
+                   "Tk": w.Tk, "d_head": w.d, "causal": w.causal, "q_offset": w.q_offset,
+                   "scale": w.scale, "rope": w.rope, "parallelism": "single GPU"},
+        "pct_of_peak": 100.0 * roof["frac"],
+        "roofline": roof,
+    }
+
+    if not args.no_also:
+        also = {}
+        for key in (1, 2, 3, 4, 5):
+            if key == args.workload:
+                continue
+            wo = wl.WORKLOADS[key]
+            r = measure(wo, args, torch, ra, wl, dev, max(10, args.steps // 2), args.warmup)
+            r = {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
+            r["attn_traffic"] = measured_traffic(r["attn_kernel"], wo.name)
+            also[str(key)] = r
+            print(f"# {wo.name}: attention {r['attn_ms'] * 1e3:.2f} us = "
+                  f"{r['attn_tflops']:.1f} TFLOP/s, {r['attn_gbs']:.0f} GB/s", file=sys.stderr)
+        line["also"] = also
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
