@@ -14,20 +14,25 @@
 // Design (one workgroup = 4 waves = 128 query rows of one (b, hq)):
 //  * Each wave owns 32 query rows.  Its Q fragment stays in registers for
 //    the whole kernel as the B operand of v_mfma_f32_32x32x16_bf16.
-//  * Keys are visited in tiles of 64.  K and V tiles are copied from HBM
-//    into LDS with 16-byte loads and shared by the four waves.
+//  * Keys are visited in tiles of 64.  K and V tiles go from HBM straight
+//    into LDS (global_load_lds_dwordx4: no staging registers, no LDS store
+//    instructions) and are shared by the four waves.  Each 16-byte chunk of
+//    a tile row is stored at a position XOR-swizzled by the row, so the
+//    fragment reads below hit distinct LDS banks.
 //  * Scores are formed transposed, S^T = K Q^T (keys on the MFMA rows,
 //    queries on its columns), so in the accumulator layout each lane holds
 //    scores of ONE query row (lane % 32) for 16 keys: the row max and row
 //    sum need no cross-lane work except one v_permlane32_swap between the
 //    two half-waves, and the running max / sum / rescale factor of a row
 //    are per-lane scalars.
-//  * Software pipeline: K runs one tile ahead of V.  While a wave turns the
-//    scores of tile t into weights (VALU) and multiplies them into V(t)
-//    (MFMA), the MFMAs for the scores of tile t+1 are already in flight:
-//    they read K(t+1), which was staged in LDS one iteration earlier, and
-//    depend on nothing the softmax produces.  Global loads run two tiles
-//    (K) and one tile (V) ahead; one barrier per tile.
+//  * Software pipeline: K runs one tile ahead of V.  In the steady state a
+//    tile step is one basic block written in issue order: each score MFMA
+//    of tile t+1 is followed by a slice of the exponentials of tile t, and
+//    each P.V MFMA of tile t by a slice of the row max of tile t+1, so the
+//    matrix cores and the vector ALUs work at the same time within one
+//    wave; fragment reads are issued three MFMAs ahead of their use.
+//    Global loads run two tiles (K) and one tile (V) ahead; one barrier per
+//    tile.
 //  * Softmax in base 2: p = 2^(s * |scale| * log2(e) - m) with the raw
 //    v_exp_f32.  The running max m is only raised when a tile's max exceeds
 //    it by more than 8 (a factor 256), so the output accumulator is
@@ -52,18 +57,25 @@ namespace {
 
 template <int D>
 struct Cfg {
-    static constexpr int BN = 64;                 // keys per tile
+    static constexpr int BN = D == 128 ? 32 : 64;  // keys per tile
     static constexpr int NW = 4;                  // waves per workgroup
     static constexpr int BM = 32 * NW;            // query rows per workgroup
-    static constexpr int SK = D + 8;              // K tile row stride (elements)
-    static constexpr int SV = D + 32;             // V tile row stride (elements)
-    static constexpr int K_ELEMS = BN * SK;
-    static constexpr int V_ELEMS = BN * SV;
-    static constexpr int CHUNKS_ROW = D / 8;      // 16-byte chunks per row
-    static constexpr int ROWS_PASS = 256 / CHUNKS_ROW;
-    static constexpr int PASSES = BN / ROWS_PASS;
-    static_assert(BN % ROWS_PASS == 0, "tile rows must split evenly");
+    static constexpr int NCH = D / 8;             // 16-byte chunks per row
+    static constexpr int TILE = BN * D;           // elements per K or V tile
+    static constexpr int RSTR = 256 / NCH;        // rows filled by one 256-lane copy round
+    static constexpr int NINS = BN / RSTR;        // copy rounds per tile
+    static_assert(BN % RSTR == 0, "tile rows must split evenly");
 };
+
+// XOR swizzles of the 16-byte chunk position within a tile row.
+//  K: sixteen consecutive rows read the same logical chunk (ds_read_b128),
+//     so the rows' chunks must fall in sixteen distinct 16-byte bank groups.
+//  V: four consecutive rows are read 64 bytes each (transpose reads), so the
+//     rows' 64-byte segments must fall in distinct 64-byte bank groups.
+template <int D>
+__device__ inline int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ inline int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 struct Args {
     const bf16* q;
@@ -92,7 +104,37 @@ __device__ inline float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Hides a value from the optimiser, so offsets derived from it are formed
+// next to their use instead of being hoisted out of the key loop as
+// loop-invariant registers.
+__device__ inline int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void copy_tile_fn(
+    const bf16* src, int j0, bf16* dst, unsigned lane_off, int Tk, int cp_r0, int wave) {
+    typedef Cfg<D> C;
+    if (j0 + C::BN <= Tk) {
+        const bf16* base = src + (size_t)j0 * D;  // wave-uniform
+#pragma unroll
+        for (int i = 0; i < C::NINS; ++i)
+            __builtin_amdgcn_global_load_lds(base + (size_t)i * C::RSTR * D + lane_off,
+                                             (lds_void*)(dst + (i * 256 + wave * 64) * 8), 16, 0, 0);
+    } else {  // last, partial tile: rows past the last key re-read the last key
+        const unsigned col = lane_off - (unsigned)(cp_r0 * D);
+#pragma unroll
+        for (int i = 0; i < C::NINS; ++i) {
+            const int row = min(j0 + cp_r0 + i * C::RSTR, Tk - 1);
+            __builtin_amdgcn_global_load_lds(src + (size_t)row * D + col,
+                                             (lds_void*)(dst + (i * 256 + wave * 64) * 8), 16, 0, 0);
+        }
+    }
+}
 
 template <int D>
 struct Tile {
@@ -100,6 +142,8 @@ struct Tile {
     f32x16 s[NKB];
 };
 
+struct Even { static constexpr int value = 0; };
+struct Odd { static constexpr int value = 1; };
 struct Unmasked { static constexpr bool value = false; };
 struct Masked { static constexpr bool value = true; };
 
@@ -107,15 +151,33 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(Args a) {
     typedef Cfg<D> C;
-    constexpr int BN = C::BN, BM = C::BM, SK = C::SK, SV = C::SV;
-    constexpr int NKB = BN / 32;   // 32-key blocks per tile
-    constexpr int NDB = D / 32;    // 32-column blocks of the output
-    constexpr int NQ = D / 16;     // 16-wide d slices of q.k
-    __shared__ __attribute__((aligned(16))) bf16 kbuf[2][C::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) bf16 vbuf[2][C::V_ELEMS];
+    constexpr int BN = C::BN, BM = C::BM;
+    constexpr int NKB = BN / 32;       // 32-key blocks per tile
+    constexpr int NDB = D / 32;        // 32-column blocks of the output
+    constexpr int NQ = D / 16;         // 16-wide d slices of q.k
+    constexpr int NS = NQ * NKB;       // score MFMAs per tile
+    constexpr int NP = NDB * NKB * 2;  // P.V MFMAs per tile
+    constexpr int NE = NKB * 16;       // scores per lane per tile
+    constexpr int EA = NE / NS;        // exponentials per score MFMA
+    constexpr int EB = NE / NP;        // max inputs per P.V MFMA
+    constexpr int AHEAD = D == 128 ? 2 : 3;  // fragment reads in flight
+    // VALU instructions the steady state places after each MFMA: about 3.5
+    // per exponential (fma, exp, half a pack, a sum) in phase A, the
+    // (masked) max in phase B
+    constexpr int VA = (7 * EA + 1) / 2 + 1;
+    constexpr int VB = EB;
+    static_assert(NE % NS == 0 && NE % NP == 0 && (8 % EA == 0), "slices must divide");
+    // four distinct LDS objects, always addressed by compile-time parity, so
+    // the compiler can tell that reads of one buffer do not alias the
+    // asynchronous HBM -> LDS copies into another (and need not wait for them)
+    __shared__ __attribute__((aligned(16))) bf16 kbuf0[C::TILE];
+    __shared__ __attribute__((aligned(16))) bf16 kbuf1[C::TILE];
+    __shared__ __attribute__((aligned(16))) bf16 vbuf0[C::TILE];
+    __shared__ __attribute__((aligned(16))) bf16 vbuf1[C::TILE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int h = lane >> 5, li = lane & 31;
 
     // ---- which (query tile, batch, query head) this workgroup owns
@@ -158,35 +220,49 @@ void prefill_bf16_kernel(Args a) {
         }
     }
 
-    // ---- K/V tile copy: thread -> (row, 16-byte chunk)
+    // ---- K/V tile copy, HBM -> LDS directly.  In copy round i, lane L of
+    //      wave w fills the tile's 16-byte slot i*256 + 64w + L, i.e. row
+    //      r0 + i*RSTR at chunk position cp_p, with the logical chunk that
+    //      the swizzle puts there.  Rows past the last key re-read the last
+    //      key (finite values; those keys are masked).
     const bf16* kh = a.k + (size_t)(b * a.Hkv + hk) * a.Tk * D;
     const bf16* vh = a.v + (size_t)(b * a.Hkv + hk) * a.Tk * D;
-    const int cp_chunk = tid % C::CHUNKS_ROW, cp_row = tid / C::CHUNKS_ROW;
-    auto load_rows = [&](const bf16* src, int j0, uint4* reg) {
-#pragma unroll
-        for (int pp = 0; pp < C::PASSES; ++pp) {
-            const int key = j0 + cp_row + pp * C::ROWS_PASS;
-            reg[pp] = key < a.Tk
-                          ? *reinterpret_cast<const uint4*>(src + (size_t)key * D + cp_chunk * 8)
-                          : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_rows = [&](bf16* dst, int stride, const uint4* reg) {
-#pragma unroll
-        for (int pp = 0; pp < C::PASSES; ++pp)
-            *reinterpret_cast<uint4*>(dst + (cp_row + pp * C::ROWS_PASS) * stride + cp_chunk * 8) =
-                reg[pp];
+    const int cp_slot = wave * 64 + lane;
+    const int cp_r0 = cp_slot / C::NCH, cp_p = cp_slot % C::NCH;
+    const int cp_ck = cp_p ^ swz_k<D>(cp_r0), cp_cv = cp_p ^ swz_v<D>(cp_r0);
+    const unsigned cp_koff = (unsigned)(cp_r0 * D + 8 * cp_ck);  // elements within a tile
+    const unsigned cp_voff = (unsigned)(cp_r0 * D + 8 * cp_cv);
+    auto copy_tile = [&](const bf16* src, int j0, bf16* dst, unsigned lane_off) {
+        copy_tile_fn<D>(src, j0, dst, lane_off, a.Tk, cp_r0, wave);
     };
 
-    // ---- per-lane LDS offsets
-    // K operand (A of S^T): key row 32kb + li, columns 16m + 8h .. +7
-    const int k_off = li * SK + 8 * h;
+    // ---- per-lane fragment offsets in a tile (elements).  In both the row
+    //      term, the swizzled chunk term and the in-chunk term occupy
+    //      disjoint bits, so the offset for slice m (block cb) is the slice-0
+    //      offset XOR 16m (32cb): one register and one v_xor per read.
+    // K operand (A of S^T): key row 32kb + li, logical chunk 2m + h
+    const int koff0 = li * D + 8 * (h ^ swz_k<D>(li));
     // V^T operand via transpose reads: supplying lane (16g + 4r + qq) points
-    // at V[key_base + 4(g/2) + r][32 cb + 16(g%2) + 4qq]
+    // at V[key_base + 4(g/2) + r][32 cb + 16(g%2) + 4qq] (logical column)
     const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
-    const int v_off = (4 * (tg >> 1) + tr) * SV + 16 * (tg & 1) + 4 * tq;
+    const int voff0 = (4 * (tg >> 1) + tr) * D + 16 * (tg & 1) + 4 * tq + 8 * swz_v<D>(tr);
 
-    // ---- visibility limits of this lane's row and of the wave
+    // the same offsets in bytes (the XOR terms double with them)
+    int koff = 2 * koff0, voff = 2 * voff0;  // re-hidden at every tile step
+    auto kfrag = [&](const bf16* Ks, int i) -> bf16x8 {  // score MFMA i = (m, kb)
+        const int m = i / NKB, kb = i % NKB;
+        const char* p = reinterpret_cast<const char*>(Ks + kb * 32 * D) + (koff ^ (32 * m));
+        return *reinterpret_cast<const bf16x8*>(p);
+    };
+    auto vfrag = [&](const bf16* Vs, int j) -> bf16x8 {  // P.V MFMA j = (kb, cc, cb)
+        const int cb = j % NDB, kc = j / NDB;            // kc = 2 kb + cc
+        const char* vp = reinterpret_cast<const char*>(Vs + 16 * kc * D) + (voff ^ (64 * cb));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 16 * D));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    // ---- visibility limits (the wave's are wave-uniform)
     const int kv_end = a.causal ? min(a.Tk, a.q_offset + i0 + BM) : a.Tk;
     const int n_tiles = (kv_end + BN - 1) / BN;
     const int row_lim = a.causal ? min(a.Tk - 1, a.q_offset + iq) : a.Tk - 1;
@@ -202,42 +278,43 @@ void prefill_bf16_kernel(Args a) {
     float m_run = -INFINITY, l_run = 0.f;
     const float cs = a.c;
 
-    // S^T(tile) = K(tile) Q^T from the K tile at Ks
-    auto scores = [&](const bf16* Ks, Tile<D>& T) {
+    // key offset (within the tile) of score element e = 16 kb + r of a lane
+    auto key_of = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3); };
+
+    auto zero_tile = [&](Tile<D>& T) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) T.s[kb][r] = 0.f;
-#pragma unroll
-        for (int m = 0; m < NQ; ++m)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + k_off + kb * 32 * SK + 16 * m);
-                T.s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[m], T.s[kb], 0, 0, 0);
-            }
     };
 
-    // weights of one tile and O^T += V^T P^T
-    auto softmax_pv = [&](Tile<D>& T, const bf16* Vs, int j0, auto masked_tag) {
+    // S^T(tile) = K(tile) Q^T (plain order; edge steps)
+    auto scores = [&](const bf16* Ks, Tile<D>& T) {
+        zero_tile(T);
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            T.s[i % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(Ks, i), qf[i / NKB],
+                                                                   T.s[i % NKB], 0, 0, 0);
+    };
+
+    // masked score element (key past the row's limit) -> -inf
+    auto mask_elem = [&](float s, int e, int lim) { return key_of(e) > lim ? -INFINITY : s; };
+
+    // row max of a tile (masking it first when MASKED), base-2 exponent units
+    auto tile_max = [&](Tile<D>& T, int j0, auto masked_tag) -> float {
         constexpr bool MASKED = decltype(masked_tag)::value;
+        const int lim = row_lim - (j0 + 4 * h);
         float mx = -INFINITY;
-        if constexpr (MASKED) {
-            const int lim = row_lim - (j0 + 4 * h);  // key offsets above lim are masked
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-                    T.s[kb][r] = off > lim ? -INFINITY : T.s[kb][r];
-                }
+        for (int e = 0; e < NE; ++e) {
+            if constexpr (MASKED) T.s[e >> 4][e & 15] = mask_elem(T.s[e >> 4][e & 15], e, lim);
+            mx = fmaxf(mx, T.s[e >> 4][e & 15]);
         }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, T.s[kb][r]);
-        mx = pair_max(mx);
-        const float tmax = mx * cs;
-        // raise the running max only when it grew by more than 2^8
+        return pair_max(mx) * cs;
+    };
+
+    // raise the running max only when the tile's max exceeds it by more than 2^8
+    auto rescale = [&](float tmax) {
         const bool need = tmax > m_run + 8.f;
         if (__any(need)) {
             const float m_new = need ? tmax : m_run;
@@ -249,70 +326,151 @@ void prefill_bf16_kernel(Args a) {
                 for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
             m_run = m_new;
         }
-        const float nm = -m_run;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                bf16x8 pb;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(T.s[kb][8 * cc + e], cs, nm));
-                    l_run += pv;
-                    pb[e] = (bf16)pv;
-                }
-#pragma unroll
-                for (int cb = 0; cb < NDB; ++cb) {
-                    const bf16* vp = Vs + v_off + (32 * kb + 16 * cc) * SV + 32 * cb;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * SV));
-                    const bf16x8 vf = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oacc[cb], 0, 0, 0);
-                }
-            }
     };
 
-    // ---- prologue: K(0), V(0), K(1) into LDS; scores of tile 0
-    uint4 kreg[C::PASSES], vreg[C::PASSES];
-    load_rows(kh, 0, kreg);
-    load_rows(vh, 0, vreg);
-    store_rows(kbuf[0], SK, kreg);
-    store_rows(vbuf[0], SV, vreg);
-    if (n_tiles > 1) {
-        load_rows(kh, BN, kreg);
-        store_rows(kbuf[1], SK, kreg);
-    }
+    // p = 2^(s c - m) for score element e; every 8 elements form one bf16
+    // B operand of the P.V product and one partial row sum
+    float pf0 = 0.f, gpart = 0.f;
+    float gsum = 0.f;
+    bf16x8 pb[NKB][2];
+    auto exp_elem = [&](const Tile<D>& T, int e, float nm) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(T.s[e >> 4][e & 15], cs, nm));
+        if ((e & 1) == 0) {
+            pf0 = p;
+        } else {  // a pair is complete: round it into the operand, add it to the sums
+            pb[e >> 4][(e >> 3) & 1][(e & 7) - 1] = (bf16)pf0;
+            pb[e >> 4][(e >> 3) & 1][e & 7] = (bf16)p;
+            const float s2 = pf0 + p;
+            gpart = (e & 3) == 1 ? s2 : gpart + s2;
+            if ((e & 3) == 3) gsum += gpart;
+        }
+    };
+
+    // O^T += V^T P^T (plain order; edge steps)
+    auto pv_tile = [&](const bf16* Vs) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int cb = j % NDB, kc = j / NDB;
+            oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(Vs, j), pb[kc >> 1][kc & 1],
+                                                               oacc[cb], 0, 0, 0);
+        }
+    };
+
+    // ---- prologue: K(0), V(0), K(1) into LDS; scores and max of tile 0
+    copy_tile(kh, 0, kbuf0, cp_koff);
+    copy_tile(vh, 0, vbuf0, cp_voff);
+    if (n_tiles > 1) copy_tile(kh, BN, kbuf1, cp_koff);
     __syncthreads();
 
     Tile<D> SA, SB;
-    scores(kbuf[0], SA);  // tile 0 is visible to every wave (key 0 is)
+    scores(kbuf0, SA);  // tile 0 is visible to every wave (key 0 is)
+    rescale(BN > wave_full ? tile_max(SA, 0, Masked()) : tile_max(SA, 0, Unmasked()));
 
-    // one pipeline step: softmax/PV of tile t (scores in cur) while the
-    // scores of tile t+1 go into nxt
-    auto step = [&](int t, Tile<D>& cur, Tile<D>& nxt) {
+    // One pipeline step.  On entry `cur` holds the (masked) scores of tile t
+    // and m_run already covers tile t.  The step forms the weights of tile t
+    // and adds P V(t), computes the scores of tile t+1 into `nxt`, and
+    // brings m_run up to date for tile t+1.
+    auto step = [&](int t, Tile<D>& cur, Tile<D>& nxt, auto parity_tag) {
+        constexpr int PAR = decltype(parity_tag)::value;  // t & 1, known at compile time
+        bf16* const k_this = PAR ? kbuf1 : kbuf0;   // held K(t); receives K(t+2)
+        const bf16* const Kn = PAR ? kbuf0 : kbuf1; // K(t+1)
+        const bf16* const Vc = PAR ? vbuf1 : vbuf0; // V(t)
+        bf16* const v_next = PAR ? vbuf0 : vbuf1;   // receives V(t+1)
         const int j0 = t * BN;
+        koff = opaque(2 * koff0);
+        voff = opaque(2 * voff0);
         const bool more_k = t + 2 < n_tiles, more_v = t + 1 < n_tiles;
-        if (more_k) load_rows(kh, j0 + 2 * BN, kreg);
-        if (more_v) load_rows(vh, j0 + BN, vreg);
-        if (more_v && j0 + BN <= wave_last) scores(kbuf[(t + 1) & 1], nxt);
-        if (j0 <= wave_last) {
-            if (j0 + BN > wave_full)
-                softmax_pv(cur, vbuf[t & 1], j0, Masked());
-            else
-                softmax_pv(cur, vbuf[t & 1], j0, Unmasked());
+        if (more_k) copy_tile(kh, j0 + 2 * BN, k_this, cp_koff);
+        if (more_v) copy_tile(vh, j0 + BN, v_next, cp_voff);
+        const bool next_active = more_v && j0 + BN <= wave_last;
+        const bool next_masked = j0 + 2 * BN > wave_full;
+        const float nm = -m_run;
+        gsum = 0.f;
+        auto steady = [&](auto next_mask_tag) {
+            constexpr bool NM = decltype(next_mask_tag)::value;
+            // ---- steady state: one basic block in issue order
+            // phase A: score MFMAs of tile t+1 | exponentials of tile t.
+            // Key block by key block (MFMA i = (kb, m) with kb = i / NQ), so
+            // the second score block starts only once the first half of
+            // tile t is spent: the two tiles never hold all their registers
+            // at once.
+            zero_tile(nxt);
+            auto kfrag_kb = [&](int i) { return kfrag(Kn, (i % NQ) * NKB + i / NQ); };
+            bf16x8 kq[AHEAD];
+#pragma unroll
+            for (int i = 0; i < AHEAD; ++i) kq[i] = kfrag_kb(i);
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const bf16x8 kf = kq[i % AHEAD];
+                if (i + AHEAD < NS) kq[i % AHEAD] = kfrag_kb(i + AHEAD);
+                nxt.s[i / NQ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i % NQ],
+                                                                        nxt.s[i / NQ], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < EA; ++u) exp_elem(cur, i * EA + u, nm);
+            }
+            // keep that order: per score MFMA one fragment read and its
+            // share of the exponential work
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, VA, 0); // VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            }
+            // phase B: P.V MFMAs of tile t | (mask and) row max of tile t+1
+            const int lim = row_lim - (j0 + BN + 4 * h);
+            float mx = -INFINITY;
+            bf16x8 vq[AHEAD];
+#pragma unroll
+            for (int j = 0; j < AHEAD; ++j) vq[j] = vfrag(Vc, j);
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                const bf16x8 vf = vq[j % AHEAD];
+                if (j + AHEAD < NP) vq[j % AHEAD] = vfrag(Vc, j + AHEAD);
+                const int cb = j % NDB, kc = j / NDB;
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kc >> 1][kc & 1], oacc[cb],
+                                                                   0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < EB; ++u) {
+                    const int e = j * EB + u;
+                    float s = nxt.s[e >> 4][e & 15];
+                    if constexpr (NM) s = mask_elem(s, e, lim);
+                    nxt.s[e >> 4][e & 15] = s;
+                    mx = fmaxf(mx, s);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, VB, 1); // VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // LDS (transpose) reads
+            }
+            l_run += gsum;
+            rescale(pair_max(mx) * cs);
+        };
+        if (next_active && !next_masked && j0 + BN <= wave_full) {
+            steady(Unmasked());
+        } else {
+            // ---- edge steps: diagonal tiles, the last tile, skipped tiles
+            if (next_active) scores(Kn, nxt);
+            if (j0 <= wave_last) {
+#pragma unroll
+                for (int e = 0; e < NE; ++e) exp_elem(cur, e, nm);
+                l_run += gsum;
+                pv_tile(Vc);
+            }
+            if (next_active)
+                rescale(next_masked ? tile_max(nxt, j0 + BN, Masked())
+                                    : tile_max(nxt, j0 + BN, Unmasked()));
         }
-        if (more_k) store_rows(kbuf[t & 1], SK, kreg);
-        if (more_v) store_rows(vbuf[(t + 1) & 1], SV, vreg);
         __syncthreads();
     };
 
     int t = 0;
     for (; t + 1 < n_tiles; t += 2) {
-        step(t, SA, SB);
-        step(t + 1, SB, SA);
+        step(t, SA, SB, Even());
+        step(t + 1, SB, SA, Odd());
     }
-    if (t < n_tiles) step(t, SA, SB);
+    if (t < n_tiles) step(t, SA, SB, Even());
 
     // ---- epilogue: O = O^T / l, lane holds columns 32cb + 8g4 + 4h .. +3 of row iq
     const float l_tot = pair_sum(l_run);
