@@ -361,7 +361,11 @@ def test_lse_matches_oracle(dtype, Tq, Tk, qo):
     o, lse = run_attn(q, k, v, 0.0884, q_offset=qo, lse=True)
     want_o, want_lse = oracle.attn(q, k, v, 0.0884, q_offset=qo, return_lse=True)
     assert float(np.max(np.abs(f64(o) - want_o))) <= TOL[dtype]
-    assert float(np.max(np.abs(lse.double().numpy() - want_lse))) <= 1e-4
+    # bf16: the row sum adds the bf16-rounded weights that also feed the P.V
+    # product (V = 1 gives O = 1), each within a relative 2^-9 of the exact
+    # weight, so ln(sum) moves by at most -ln(1 - 2^-9) = 1.955e-3.
+    lse_tol = 1e-4 if dtype == torch.float32 else 2.0e-3
+    assert float(np.max(np.abs(lse.double().numpy() - want_lse))) <= lse_tol
 
 
 def test_bf16_deterministic():

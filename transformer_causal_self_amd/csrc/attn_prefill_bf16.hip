@@ -1,5 +1,6 @@
 // attn_prefill_bf16.hip -- fused causal attention forward, bf16 in/out,
-// float32 accumulation, on the gfx950 matrix cores.  Head size 64 or 128.
+// float32 accumulation, on the gfx950 matrix cores, head size 128 (the
+// kernel is written for 64 too; head size 64 uses attn_prefill_d64.hip).
 //
 // What it computes: for every (batch b, query head hq, query row i)
 //     o_i = sum_j softmax_j(scale * q_i . k_j + M_ij) v_j
@@ -11,43 +12,54 @@
 // T x T score matrix never leaves registers ("Grasping Codes and Math 02" --
 // Flash Attention).
 //
-// Design (one workgroup = 4 waves = 128 query rows of one (b, hq)):
-//  * Each wave owns 32 query rows.  Its Q fragment stays in registers for
-//    the whole kernel as the B operand of v_mfma_f32_32x32x16_bf16.
-//  * Keys are visited in tiles of 64.  K and V tiles go from HBM straight
-//    into LDS (global_load_lds_dwordx4: no staging registers, no LDS store
-//    instructions) and are shared by the four waves.  Each 16-byte chunk of
-//    a tile row is stored at a position XOR-swizzled by the row, so the
-//    fragment reads below hit distinct LDS banks.
+// Design.  One workgroup = 8 waves in two groups of four.  Both groups cover
+// the same 128 query rows (32 per wave), group g of query head 2p + g, so
+// their causal extents are identical and they walk the key tiles in
+// lockstep.  Waves w and w + 4 share a SIMD.
+//  * Ping-pong: a group alternates an MFMA phase (scores of key tile t and
+//    the P.V product of tile t - 1) with a softmax phase (mask, weights,
+//    row sum of tile t).  Group 1 runs one phase behind group 0, and one
+//    s_barrier separates consecutive phases, so on every SIMD one wave feeds
+//    the matrix core while the other keeps the vector ALU busy.
+//  * One wave issues LDS reads and HBM -> LDS copies only so fast (each
+//    blocks its instruction stream for tens of cycles, and an LDS read takes
+//    several hundred cycles to return), so that work is split between the
+//    phases: the softmax phase reads the K fragments of the next tile into
+//    registers and issues this wave's share of the tile copies between its
+//    exponentials; the MFMA phase reads one V^T fragment ahead of each score
+//    MFMA, for the P.V MFMAs that follow.
 //  * Scores are formed transposed, S^T = K Q^T (keys on the MFMA rows,
-//    queries on its columns), so in the accumulator layout each lane holds
-//    scores of ONE query row (lane % 32) for 16 keys: the row max and row
-//    sum need no cross-lane work except one v_permlane32_swap between the
-//    two half-waves, and the running max / sum / rescale factor of a row
-//    are per-lane scalars.
-//  * Software pipeline: K runs one tile ahead of V.  In the steady state a
-//    tile step is one basic block written in issue order: each score MFMA
-//    of tile t+1 is followed by a slice of the exponentials of tile t, and
-//    each P.V MFMA of tile t by a slice of the row max of tile t+1, so the
-//    matrix cores and the vector ALUs work at the same time within one
-//    wave; fragment reads are issued three MFMAs ahead of their use.
-//    Global loads run two tiles (K) and one tile (V) ahead; one barrier per
-//    tile.
+//    queries on its columns; v_mfma_f32_32x32x16_bf16), so each lane holds
+//    scores of ONE query row: the row max and row sum need only one
+//    v_permlane32_swap between the two half-waves, and the running max,
+//    sum and rescale factor of a row are per-lane scalars.
+//  * K and V tiles of 64 keys go from HBM straight into an LDS ring
+//    (global_load_lds_dwordx4; no staging registers, no LDS stores) three
+//    tiles deep, copied by one group of four waves each, about three phases
+//    before use.  When both query heads of a workgroup use the same K/V head
+//    (GQA with an even group size) the two groups share one ring (group 1
+//    copies K, group 0 V), otherwise each group has its own.  Each 16-byte
+//    chunk of a tile row sits at a position XOR-swizzled by the row, so the
+//    fragment reads hit distinct LDS banks.
 //  * Softmax in base 2: p = 2^(s * |scale| * log2(e) - m) with the raw
-//    v_exp_f32.  The running max m is only raised when a tile's max exceeds
-//    it by more than 8 (a factor 256), so the output accumulator is
-//    rescaled rarely; the final division by the row sum cancels whichever m
-//    was used.  A negative scale is applied by negating q on load.
+//    v_exp_f32, first against the running max m as it stands: only when a
+//    row's weights would exceed 2^12 (or on its first tile, where m = -inf)
+//    does the row take the tile's max, rescale its accumulator and
+//    recompute.  The final division by the row sum cancels whichever m was
+//    used.  A negative scale is applied by negating q on load.  The row sum
+//    adds the bf16-rounded weights that feed the P.V product
+//    (v_dot2_f32_bf16 against (1, 1)), so V = 1 gives O = 1.
 //  * P^T, rounded to bf16, is already in the B-operand layout of the second
 //    product O^T += V^T P^T.  The A operand V^T is read from the row-major V
 //    tile with ds_read_b64_tr_b16 (the LDS transpose read of gfx950), whose
 //    four-row gather is matched to the key order of the score accumulator.
-//  * Causal tiles past a wave's last visible key are skipped; only tiles
-//    that straddle the diagonal (or the end of the keys) pay for masking.
+//  * Tiles past a wave's last visible key are skipped (the wave still takes
+//    part in the barriers); only tiles that straddle the diagonal or the end
+//    of the keys pay for masking.
 //  * Workgroups are issued longest-first (largest query tile first), and,
-//    when the number of batch x K/V heads is a multiple of 8, the query
-//    heads that share a K/V head are placed on the same XCD (workgroup id
-//    modulo 8) so their K/V tiles are served from that XCD's L2.
+//    when the number of head pairs is a multiple of 8, consecutive head
+//    pairs (which share K/V heads under GQA) are placed on one XCD
+//    (workgroup id modulo 8) so their K/V tiles are served from its L2.
 #include <math.h>
 
 #include "internal.hpp"
@@ -55,21 +67,27 @@
 namespace rocattn {
 namespace {
 
-template <int D>
+template <int D, bool DUAL>
 struct Cfg {
-    static constexpr int BN = D == 128 ? 32 : 64;  // keys per tile
-    static constexpr int NW = 4;                  // waves per workgroup
-    static constexpr int BM = 32 * NW;            // query rows per workgroup
-    static constexpr int NCH = D / 8;             // 16-byte chunks per row
-    static constexpr int TILE = BN * D;           // elements per K or V tile
-    static constexpr int RSTR = 256 / NCH;        // rows filled by one 256-lane copy round
-    static constexpr int NINS = BN / RSTR;        // copy rounds per tile
-    static_assert(BN % RSTR == 0, "tile rows must split evenly");
+    static constexpr int BN = 64;                        // keys per tile
+    static constexpr int BMG = 128;                      // query rows per group
+    static constexpr int NCH = D / 8;                    // 16-byte chunks per key row
+    static constexpr int TB = BN * D * 2;                // bytes of one K or V tile
+    // ring depths (tiles); a tile is copied by the four waves of one group
+    static constexpr int NK = (DUAL && D == 64) ? 4 : 3;
+    static constexpr int NV = (DUAL && D == 128) ? 2 : 3;
+    static constexpr int NINS = BN * NCH / 256;          // copy instructions per lane per tile
+    static constexpr int RSTR = 256 / NCH;               // tile rows filled by one copy instruction
+    static constexpr int MAXOPS = (DUAL ? 2 : 1) * NINS; // copy instructions per lane per round
+    static constexpr int RING = (NK + NV) * TB;          // K slots, then V slots, of one ring
+    static constexpr int LDS = (DUAL ? 2 : 1) * RING;
+    static_assert(NINS >= 1 && BN % RSTR == 0, "copy instructions must tile the key block");
+    static_assert(LDS <= 160 * 1024, "LDS of one workgroup");
 };
 
 // XOR swizzles of the 16-byte chunk position within a tile row.
 //  K: sixteen consecutive rows read the same logical chunk (ds_read_b128),
-//     so the rows' chunks must fall in sixteen distinct 16-byte bank groups.
+//     so the rows' chunks must fall in distinct 16-byte bank groups.
 //  V: four consecutive rows are read 64 bytes each (transpose reads), so the
 //     rows' 64-byte segments must fall in distinct 64-byte bank groups.
 template <int D>
@@ -85,13 +103,13 @@ struct Args {
     float* lse;
     int B, Hq, Hkv, Tq, Tk;
     int R;         // query heads per K/V head
-    int G;         // B * Hkv
-    int n_qt;      // query tiles per head
+    int HP;        // head pairs per batch entry, ceil(Hq / 2)
+    int n_qt;      // query tiles (of 128 rows) per head
     float c;       // |scale| * log2(e), at least 1e-30 so that -inf * c = -inf
     unsigned neg;  // 0x80008000 when scale < 0 (q is negated on load), else 0
     int causal;
     int q_offset;
-    int xcd;       // 1: group the heads of one K/V head on one XCD
+    int xcd;       // 1: place consecutive head pairs on one XCD
 };
 
 __device__ inline float pair_max(float x) {
@@ -104,108 +122,105 @@ __device__ inline float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Hides a value from the optimiser, so offsets derived from it are formed
-// next to their use instead of being hoisted out of the key loop as
-// loop-invariant registers.
-__device__ inline int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline unsigned lds_addr(const void* p) {
+    return (unsigned)(uintptr_t)(const lds_void*)p;
 }
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+// One 16-byte HBM -> LDS copy per lane: lane L of the wave writes LDS bytes
+// [lds + 16 L, lds + 16 L + 16) with the 16 bytes at sbase + voff.  Written
+// as assembly so the compiler does not guard every later LDS read with a
+// wait for it; the kernel waits itself (wait_vm) before the barrier that
+// publishes the tile.  Nothing else in this kernel uses m0.
+__device__ inline void copy16(const void* sbase, unsigned voff, unsigned lds) {
+    // base and LDS address are wave-uniform; say so, so they live in SGPRs
+    const unsigned long long b = (unsigned long long)sbase;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+    const void* base = (const void*)(((unsigned long long)hi << 32) | lo);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base) : "memory");
+}
 
-template <int D>
-__device__ __attribute__((always_inline)) inline void copy_tile_fn(
-    const bf16* src, int j0, bf16* dst, unsigned lane_off, int Tk, int cp_r0, int wave) {
-    typedef Cfg<D> C;
-    if (j0 + C::BN <= Tk) {
-        const bf16* base = src + (size_t)j0 * D;  // wave-uniform
-#pragma unroll
-        for (int i = 0; i < C::NINS; ++i)
-            __builtin_amdgcn_global_load_lds(base + (size_t)i * C::RSTR * D + lane_off,
-                                             (lds_void*)(dst + (i * 256 + wave * 64) * 8), 16, 0, 0);
-    } else {  // last, partial tile: rows past the last key re-read the last key
-        const unsigned col = lane_off - (unsigned)(cp_r0 * D);
-#pragma unroll
-        for (int i = 0; i < C::NINS; ++i) {
-            const int row = min(j0 + cp_r0 + i * C::RSTR, Tk - 1);
-            __builtin_amdgcn_global_load_lds(src + (size_t)row * D + col,
-                                             (lds_void*)(dst + (i * 256 + wave * 64) * 8), 16, 0, 0);
-        }
+// Wait until at most n of this wave's vector-memory operations are in flight.
+__device__ inline void wait_vm(int n) {
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
     }
 }
 
-template <int D>
-struct Tile {
-    static constexpr int NKB = Cfg<D>::BN / 32;  // 32-key blocks per tile
-    f32x16 s[NKB];
-};
+// Marks a value as read and rewritten here, so its computation stays on this
+// side of the following barrier.
+template <typename T>
+__device__ inline void pin(T& x) {
+    asm volatile("" : "+v"(x));
+}
 
-struct Even { static constexpr int value = 0; };
-struct Odd { static constexpr int value = 1; };
-struct Unmasked { static constexpr bool value = false; };
-struct Masked { static constexpr bool value = true; };
+__device__ inline void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, bool DUAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(Args a) {
-    typedef Cfg<D> C;
-    constexpr int BN = C::BN, BM = C::BM;
+    typedef Cfg<D, DUAL> C;
+    constexpr int BN = C::BN, TB = C::TB, NK = C::NK, NV = C::NV, NINS = C::NINS;
+    constexpr int MAXOPS = C::MAXOPS;
     constexpr int NKB = BN / 32;       // 32-key blocks per tile
     constexpr int NDB = D / 32;        // 32-column blocks of the output
     constexpr int NQ = D / 16;         // 16-wide d slices of q.k
     constexpr int NS = NQ * NKB;       // score MFMAs per tile
-    constexpr int NP = NDB * NKB * 2;  // P.V MFMAs per tile
+    constexpr int NKC = BN / 16;       // 16-key slices of a tile
+    constexpr int NP = NDB * NKC;      // P.V MFMAs per tile
     constexpr int NE = NKB * 16;       // scores per lane per tile
-    constexpr int EA = NE / NS;        // exponentials per score MFMA
-    constexpr int EB = NE / NP;        // max inputs per P.V MFMA
-    constexpr int AHEAD = D == 128 ? 2 : 3;  // fragment reads in flight
-    // VALU instructions the steady state places after each MFMA: about 3.5
-    // per exponential (fma, exp, half a pack, a sum) in phase A, the
-    // (masked) max in phase B
-    constexpr int VA = (7 * EA + 1) / 2 + 1;
-    constexpr int VB = EB;
-    static_assert(NE % NS == 0 && NE % NP == 0 && (8 % EA == 0), "slices must divide");
-    // four distinct LDS objects, always addressed by compile-time parity, so
-    // the compiler can tell that reads of one buffer do not alias the
-    // asynchronous HBM -> LDS copies into another (and need not wait for them)
-    __shared__ __attribute__((aligned(16))) bf16 kbuf0[C::TILE];
-    __shared__ __attribute__((aligned(16))) bf16 kbuf1[C::TILE];
-    __shared__ __attribute__((aligned(16))) bf16 vbuf0[C::TILE];
-    __shared__ __attribute__((aligned(16))) bf16 vbuf1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, wave-uniform
+    const int grp = wave >> 2, wg = wave & 3;
     const int h = lane >> 5, li = lane & 31;
 
-    // ---- which (query tile, batch, query head) this workgroup owns
-    int qt, g, rep;
+    // ---- which (query tile, batch, head pair) this workgroup owns
+    int qt, unit;
     {
         const int w = blockIdx.x;
+        const int P = a.B * a.HP;
         if (a.xcd) {
-            const int x = w & 7, s = w >> 3;
-            const int per = (a.G >> 3) * a.R;
-            const int rank = s / per, rem = s - rank * per;
-            g = x * (a.G >> 3) + rem / a.R;
-            rep = rem % a.R;
+            const int x = w & 7, s = w >> 3, per = P >> 3;
+            const int rank = s / per;
+            unit = x * per + (s - rank * per);
             qt = a.n_qt - 1 - rank;
         } else {
-            const int per = a.G * a.R;
-            const int rank = w / per, rem = w - rank * per;
-            g = rem / a.R;
-            rep = rem % a.R;
+            const int rank = w / P;
+            unit = w - rank * P;
             qt = a.n_qt - 1 - rank;
         }
     }
-    const int b = g / a.Hkv, hk = g - (g / a.Hkv) * a.Hkv;
-    const int hq = hk * a.R + rep;
-    const int i0 = qt * BM;
-    const int i0w = i0 + 32 * wave;
-    const int iq = i0w + li;               // this lane's query row
+    const int b = unit / a.HP, pp = unit - (unit / a.HP) * a.HP;
+    const int hq_raw = 2 * pp + grp;
+    const bool ghost = hq_raw >= a.Hq;          // odd Hq: the last pair has one head
+    const int hq = ghost ? 2 * pp : hq_raw;
+    const int hk = hq / a.R;
+    const int i0 = qt * C::BMG;
+    const int i0w = i0 + 32 * wg;
+    const int iq = i0w + li;                    // this lane's query row
 
-    // ---- Q fragment (B operand): lane holds q[iq][16m + 8h .. +7]
+    // ---- Q fragment (B operand of S^T): lane holds q[iq][16m + 8h .. +7]
     bf16x8 qf[NQ];
     {
         const int row = iq < a.Tq ? iq : a.Tq - 1;
@@ -220,261 +235,313 @@ void prefill_bf16_kernel(Args a) {
         }
     }
 
-    // ---- K/V tile copy, HBM -> LDS directly.  In copy round i, lane L of
-    //      wave w fills the tile's 16-byte slot i*256 + 64w + L, i.e. row
-    //      r0 + i*RSTR at chunk position cp_p, with the logical chunk that
-    //      the swizzle puts there.  Rows past the last key re-read the last
-    //      key (finite values; those keys are masked).
-    const bf16* kh = a.k + (size_t)(b * a.Hkv + hk) * a.Tk * D;
-    const bf16* vh = a.v + (size_t)(b * a.Hkv + hk) * a.Tk * D;
-    const int cp_slot = wave * 64 + lane;
-    const int cp_r0 = cp_slot / C::NCH, cp_p = cp_slot % C::NCH;
-    const int cp_ck = cp_p ^ swz_k<D>(cp_r0), cp_cv = cp_p ^ swz_v<D>(cp_r0);
-    const unsigned cp_koff = (unsigned)(cp_r0 * D + 8 * cp_ck);  // elements within a tile
-    const unsigned cp_voff = (unsigned)(cp_r0 * D + 8 * cp_cv);
-    auto copy_tile = [&](const bf16* src, int j0, bf16* dst, unsigned lane_off) {
-        copy_tile_fn<D>(src, j0, dst, lane_off, a.Tk, cp_r0, wave);
-    };
-
-    // ---- per-lane fragment offsets in a tile (elements).  In both the row
-    //      term, the swizzled chunk term and the in-chunk term occupy
-    //      disjoint bits, so the offset for slice m (block cb) is the slice-0
-    //      offset XOR 16m (32cb): one register and one v_xor per read.
-    // K operand (A of S^T): key row 32kb + li, logical chunk 2m + h
-    const int koff0 = li * D + 8 * (h ^ swz_k<D>(li));
-    // V^T operand via transpose reads: supplying lane (16g + 4r + qq) points
-    // at V[key_base + 4(g/2) + r][32 cb + 16(g%2) + 4qq] (logical column)
-    const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
-    const int voff0 = (4 * (tg >> 1) + tr) * D + 16 * (tg & 1) + 4 * tq + 8 * swz_v<D>(tr);
-
-    // the same offsets in bytes (the XOR terms double with them)
-    int koff = 2 * koff0, voff = 2 * voff0;  // re-hidden at every tile step
-    auto kfrag = [&](const bf16* Ks, int i) -> bf16x8 {  // score MFMA i = (m, kb)
-        const int m = i / NKB, kb = i % NKB;
-        const char* p = reinterpret_cast<const char*>(Ks + kb * 32 * D) + (koff ^ (32 * m));
-        return *reinterpret_cast<const bf16x8*>(p);
-    };
-    auto vfrag = [&](const bf16* Vs, int j) -> bf16x8 {  // P.V MFMA j = (kb, cc, cb)
-        const int cb = j % NDB, kc = j / NDB;            // kc = 2 kb + cc
-        const char* vp = reinterpret_cast<const char*>(Vs + 16 * kc * D) + (voff ^ (64 * cb));
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 16 * D));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-
     // ---- visibility limits (the wave's are wave-uniform)
-    const int kv_end = a.causal ? min(a.Tk, a.q_offset + i0 + BM) : a.Tk;
-    const int n_tiles = (kv_end + BN - 1) / BN;
+    const int kv_end = a.causal ? min(a.Tk, a.q_offset + i0 + C::BMG) : a.Tk;
+    const int n = (kv_end + BN - 1) / BN;       // key tiles of the workgroup
     const int row_lim = a.causal ? min(a.Tk - 1, a.q_offset + iq) : a.Tk - 1;
     const int wave_last = a.causal ? min(a.Tk - 1, a.q_offset + i0w + 31) : a.Tk - 1;
     // keys below wave_full are visible to every row of the wave
     const int wave_full = a.causal ? min(a.Tk, a.q_offset + i0w + 1) : a.Tk;
+    // last tile this wave computes (-1: none)
+    const int last = (ghost || i0w >= a.Tq) ? -1 : wave_last / BN;
+
+    // ---- K/V ring: NK K slots, then NV V slots.  With a shared ring, group 1
+    //      copies the K tiles and group 0 the V tiles; with one ring per
+    //      group, each group copies its own.  Copy round r fills K(r + NK - 1)
+    //      and V(r + NV - 2); a wave issues its part of a round during one of
+    //      its softmax phases (rounds below 0 form the prologue).
+    const unsigned ring = lds_addr(lds) + (DUAL ? (unsigned)(grp * C::RING) : 0u);
+    const bf16* kh = a.k + (size_t)(b * a.Hkv + hk) * a.Tk * D;
+    const bf16* vh = a.v + (size_t)(b * a.Hkv + hk) * a.Tk * D;
+    // copy instruction i of a tile: lane (wg, lane) fills the tile's 16-byte
+    // slot 256 i + 64 wg + lane, i.e. row cp_r0 + i * RSTR at chunk cp_p
+    const int cl = wg * 64 + lane;
+    const int cp_r0 = cl / C::NCH, cp_p = cl % C::NCH;
+    const unsigned cp_kcol = 16u * (unsigned)(cp_p ^ swz_k<D>(cp_r0));
+    const unsigned cp_vcol = 16u * (unsigned)(cp_p ^ swz_v<D>(cp_r0));
+    const unsigned cp_lds = (unsigned)(wg * 64 * 16);
+    // slots are taken modulo the ring depth for any tile index (negative
+    // ones included)
+    auto kslot = [&](int t) { return ring + (unsigned)((((t % NK) + NK) % NK) * TB); };
+    auto vslot = [&](int t) { return ring + (unsigned)((NK + ((t % NV) + NV) % NV) * TB); };
+    auto copy_ins = [&](const bf16* head, int t, unsigned slot, unsigned col, int i) {
+        // a tile outside 0 .. n-1 is never read: its copy re-reads a valid
+        // tile into the slot it would occupy, which holds no live data then
+        const int j0 = min(max(t, 0), n - 1) * BN;
+        const char* base = reinterpret_cast<const char*>(head + (size_t)j0 * D);
+        // rows past the last key re-read the last key (finite; masked)
+        const int row = min(cp_r0 + i * C::RSTR, a.Tk - 1 - j0);
+        copy16(base, (unsigned)row * (unsigned)(D * 2) + col, slot + (unsigned)(i * 256 * 16) + cp_lds);
+    };
+    // Every round issues the same MAXOPS copy instructions per lane (K ones
+    // first), so the number of copies in flight after a given round is a
+    // compile-time constant.
+    auto copy_part = [&](int r, int q0, int q1) {
+        const int tk = r + NK - 1, tv = r + NV - 2;
+        // shared ring: group 1 copies K(tk), group 0 V(tv) (selected, not branched)
+        const bool sk = grp == 1;
+        const bf16* sh = sk ? kh : vh;
+        const int st = sk ? tk : tv;
+        const unsigned ss = sk ? kslot(tk) : vslot(tv);
+        const unsigned sc = sk ? cp_kcol : cp_vcol;
+#pragma unroll
+        for (int q = 0; q < MAXOPS; ++q) {
+            if (q < q0 || q >= q1) continue;
+            if (DUAL) {
+                if (q < NINS) copy_ins(kh, tk, kslot(tk), cp_kcol, q);
+                else copy_ins(vh, tv, vslot(tv), cp_vcol, q - NINS);
+            } else {
+                copy_ins(sh, st, ss, sc, q);
+            }
+        }
+    };
+    // wait until this lane's copies of a round have landed while those of
+    // the `later` rounds issued after it may still be in flight
+    auto wait_rounds_after = [&](int later) { wait_vm(later * MAXOPS); };
+    // the round a wave issues during its local phase u (odd u: a softmax or
+    // idle phase); below 0: none
+    auto round_of = [&](int u) { return (!DUAL && grp == 1) ? (u + 1) >> 1 : (u - 1) >> 1; };
+
+    // ---- per-lane fragment offsets in a tile (bytes).  In both the row
+    //      term, the swizzled chunk term and the in-chunk term occupy
+    //      disjoint bits, so the offset for slice m (block cb) is the slice-0
+    //      offset XOR 32m (64cb).
+    // K operand (A of S^T): key row 32kb + li, logical chunk 2m + h
+    const unsigned koff = 2u * (unsigned)(li * D + 8 * (h ^ swz_k<D>(li)));
+    // V^T operand via transpose reads: supplying lane (16g + 4r + qq) points
+    // at V[key_base + 4(g/2) + r][32 cb + 16(g%2) + 4qq] (logical column)
+    const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
+    const unsigned voff =
+        2u * (unsigned)((4 * (tg >> 1) + tr) * D + 16 * (tg & 1) + 4 * tq + 8 * swz_v<D>(tr));
 
     f32x16 oacc[NDB];
 #pragma unroll
     for (int cb = 0; cb < NDB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 sacc[NKB];
+    bf16x8 pb[NKC];
+    float m_run = -INFINITY, l_a = 0.f, l_b = 0.f;
     const float cs = a.c;
+
+    // K fragments of the next tile, read into registers during the softmax
+    // phase (so the LDS reads of a SIMD are spread over both of its waves)
+    bf16x8 kpre[NS];
+    // One MFMA phase: S^T = K(t) Q^T on the prefetched K fragments (when
+    // `scores`), then O^T += V^T(tv) P^T (when tv >= 0).  The V^T fragment of
+    // P.V MFMA j is read before score MFMA j, so it has the whole score
+    // product to arrive (an LDS read takes several hundred cycles); its
+    // registers take the place of the K fragment just consumed.  Hard
+    // scheduling fences keep that order.
+    auto mfma_phase = [&](bool scores, int tv) {
+        const unsigned vb0 = vslot(tv < 0 ? 0 : tv) + voff;
+        auto vfrag = [&](int j) {
+            const int kc = j / NDB, cb = j % NDB;
+            const unsigned addr = (vb0 + (unsigned)(16 * kc * D * 2)) ^ (64u * cb);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 16u * D));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 vf[NP];
+        if (scores) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                if (tv >= 0 && i < NP) vf[i] = vfrag(i);
+                __builtin_amdgcn_sched_barrier(0);
+                const int m = i / NKB, kb = i % NKB;
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kpre[i], qf[m],
+                                                                   i < NKB ? f32x16{} : sacc[kb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) pin(sacc[kb]);
+        }
+        if (tv >= 0) {
+            constexpr int DONE = NS < NP ? NS : NP;   // fragments already read
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                if (!scores || j >= DONE) vf[j] = vfrag(j);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                const int kc = j / NDB, cb = j % NDB;
+                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pb[kc], oacc[cb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int cb = 0; cb < NDB; ++cb) pin(oacc[cb]);
+        }
+    };
 
     // key offset (within the tile) of score element e = 16 kb + r of a lane
     auto key_of = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3); };
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-    auto zero_tile = [&](Tile<D>& T) {
+    // weights p = 2^(s c - m) of 16-key slice kc in bf16 (the B operand of
+    // P.V) and this lane's part of their sum
+    auto weights_kc = [&](int kc, float m, float& sa, float& sb) {
+        const float nm = -m;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) T.s[kb][r] = 0.f;
-    };
-
-    // S^T(tile) = K(tile) Q^T (plain order; edge steps)
-    auto scores = [&](const bf16* Ks, Tile<D>& T) {
-        zero_tile(T);
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-            T.s[i % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(Ks, i), qf[i / NKB],
-                                                                   T.s[i % NKB], 0, 0, 0);
-    };
-
-    // masked score element (key past the row's limit) -> -inf
-    auto mask_elem = [&](float s, int e, int lim) { return key_of(e) > lim ? -INFINITY : s; };
-
-    // row max of a tile (masking it first when MASKED), base-2 exponent units
-    auto tile_max = [&](Tile<D>& T, int j0, auto masked_tag) -> float {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        const int lim = row_lim - (j0 + 4 * h);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            if constexpr (MASKED) T.s[e >> 4][e & 15] = mask_elem(T.s[e >> 4][e & 15], e, lim);
-            mx = fmaxf(mx, T.s[e >> 4][e & 15]);
+        for (int u = 0; u < 4; ++u) {
+            const int e = 8 * kc + 2 * u;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], cs, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][(e + 1) & 15], cs, nm));
+            bf16x2 pk;
+            pk[0] = (bf16)p0;
+            pk[1] = (bf16)p1;
+            pb[kc][2 * u] = pk[0];
+            pb[kc][2 * u + 1] = pk[1];
+            if (u & 1) sb = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, sb, false);
+            else sa = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, sa, false);
         }
-        return pair_max(mx) * cs;
+    };
+    auto kfrag_read = [&](int t, int i) {
+        const int m = i / NKB, kb = i % NKB;
+        const unsigned addr = (kslot(t) + koff + (unsigned)(kb * 32 * D * 2)) ^ (32u * m);
+        kpre[i] = *(lds_bf16x8*)(uintptr_t)addr;
     };
 
-    // raise the running max only when the tile's max exceeds it by more than 2^8
-    auto rescale = [&](float tmax) {
-        const bool need = tmax > m_run + 8.f;
-        if (__any(need)) {
-            const float m_new = need ? tmax : m_run;
+    // softmax phase of tile t (issuing copy round r): mask, then
+    // per 16-key slice the weights against the running max, with the K
+    // fragment reads of tile t + 1 and the copy instructions spread between
+    // the slices (one wave issues LDS reads and copies only so fast).  Only
+    // when some weight would exceed 2^12 (or on the first tile, where the
+    // running max is -inf) take the row max, raise the running max and
+    // recompute.
+    constexpr int CPC = (MAXOPS + NKC - 1) / NKC;              // copies per slice
+    auto softmax_phase = [&](int t, int r) {
+        const int j0 = t * BN;
+        if (j0 + BN > wave_full) {
+            const int lim = row_lim - (j0 + 4 * h);
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                if (key_of(e) > lim) sacc[e >> 4][e & 15] = -INFINITY;
+        }
+        float sa = 0.f, sb = 0.f;
+        // the K fragment reads go first: an LDS read takes several hundred
+        // cycles to return (a read of a tile this wave will not use is harmless)
+#pragma unroll
+        for (int i = 0; i < NS; ++i) kfrag_read(t + 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+            copy_part(r, kc * CPC, (kc + 1) * CPC);
+            weights_kc(kc, m_run, sa, sb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const bool big = !(sa + sb <= 4096.f);
+        if (__any(big)) {
+            // rows (both half-wave lanes of a row) whose weights got too big
+            // take their tile max; the other rows keep m_run (alpha = 1) and
+            // recompute the very same weights
+            const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)big, (unsigned)big, false, false);
+            const bool row_big = (sw[0] | sw[1]) != 0u;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) mx = fmaxf(mx, sacc[e >> 4][e & 15]);
+            const float tmax = pair_max(mx) * cs;
+            const float m_new = row_big ? fmaxf(m_run, tmax) : m_run;
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
+            l_a *= alpha;
+            l_b *= alpha;
 #pragma unroll
             for (int cb = 0; cb < NDB; ++cb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+                for (int rr = 0; rr < 16; ++rr) oacc[cb][rr] *= alpha;
             m_run = m_new;
+            sa = 0.f;
+            sb = 0.f;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) weights_kc(kc, m_run, sa, sb);
         }
+        l_a += sa;
+        l_b += sb;
+        // the weights, sums and prefetched fragments are finished inside this
+        // phase, not sunk past the barrier into the next one
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) pin(pb[kc]);
+        pin(l_a);
+        pin(l_b);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) pin(kpre[i]);
     };
 
-    // p = 2^(s c - m) for score element e; every 8 elements form one bf16
-    // B operand of the P.V product and one partial row sum
-    float pf0 = 0.f, gpart = 0.f;
-    float gsum = 0.f;
-    bf16x8 pb[NKB][2];
-    auto exp_elem = [&](const Tile<D>& T, int e, float nm) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(T.s[e >> 4][e & 15], cs, nm));
-        if ((e & 1) == 0) {
-            pf0 = p;
-        } else {  // a pair is complete: round it into the operand, add it to the sums
-            pb[e >> 4][(e >> 3) & 1][(e & 7) - 1] = (bf16)pf0;
-            pb[e >> 4][(e >> 3) & 1][e & 7] = (bf16)p;
-            const float s2 = pf0 + p;
-            gpart = (e & 3) == 1 ? s2 : gpart + s2;
-            if ((e & 3) == 3) gsum += gpart;
-        }
-    };
-
-    // O^T += V^T P^T (plain order; edge steps)
-    auto pv_tile = [&](const bf16* Vs) {
+    // ---- prologue: copy rounds 1-NK .. -1; K(0) lands before the first barrier
+    for (int r = 1 - NK; r < 0; ++r) copy_part(r, 0, MAXOPS);
+    if (DUAL || grp == 1) wait_rounds_after(NK - 2);
+    phase_barrier();
+    if (last >= 0) {
 #pragma unroll
-        for (int j = 0; j < NP; ++j) {
-            const int cb = j % NDB, kc = j / NDB;
-            oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(Vs, j), pb[kc >> 1][kc & 1],
-                                                               oacc[cb], 0, 0, 0);
-        }
-    };
-
-    // ---- prologue: K(0), V(0), K(1) into LDS; scores and max of tile 0
-    copy_tile(kh, 0, kbuf0, cp_koff);
-    copy_tile(vh, 0, vbuf0, cp_voff);
-    if (n_tiles > 1) copy_tile(kh, BN, kbuf1, cp_koff);
-    __syncthreads();
-
-    Tile<D> SA, SB;
-    scores(kbuf0, SA);  // tile 0 is visible to every wave (key 0 is)
-    rescale(BN > wave_full ? tile_max(SA, 0, Masked()) : tile_max(SA, 0, Unmasked()));
-
-    // One pipeline step.  On entry `cur` holds the (masked) scores of tile t
-    // and m_run already covers tile t.  The step forms the weights of tile t
-    // and adds P V(t), computes the scores of tile t+1 into `nxt`, and
-    // brings m_run up to date for tile t+1.
-    auto step = [&](int t, Tile<D>& cur, Tile<D>& nxt, auto parity_tag) {
-        constexpr int PAR = decltype(parity_tag)::value;  // t & 1, known at compile time
-        bf16* const k_this = PAR ? kbuf1 : kbuf0;   // held K(t); receives K(t+2)
-        const bf16* const Kn = PAR ? kbuf0 : kbuf1; // K(t+1)
-        const bf16* const Vc = PAR ? vbuf1 : vbuf0; // V(t)
-        bf16* const v_next = PAR ? vbuf0 : vbuf1;   // receives V(t+1)
-        const int j0 = t * BN;
-        koff = opaque(2 * koff0);
-        voff = opaque(2 * voff0);
-        const bool more_k = t + 2 < n_tiles, more_v = t + 1 < n_tiles;
-        if (more_k) copy_tile(kh, j0 + 2 * BN, k_this, cp_koff);
-        if (more_v) copy_tile(vh, j0 + BN, v_next, cp_voff);
-        const bool next_active = more_v && j0 + BN <= wave_last;
-        const bool next_masked = j0 + 2 * BN > wave_full;
-        const float nm = -m_run;
-        gsum = 0.f;
-        auto steady = [&](auto next_mask_tag) {
-            constexpr bool NM = decltype(next_mask_tag)::value;
-            // ---- steady state: one basic block in issue order
-            // phase A: score MFMAs of tile t+1 | exponentials of tile t.
-            // Key block by key block (MFMA i = (kb, m) with kb = i / NQ), so
-            // the second score block starts only once the first half of
-            // tile t is spent: the two tiles never hold all their registers
-            // at once.
-            zero_tile(nxt);
-            auto kfrag_kb = [&](int i) { return kfrag(Kn, (i % NQ) * NKB + i / NQ); };
-            bf16x8 kq[AHEAD];
-#pragma unroll
-            for (int i = 0; i < AHEAD; ++i) kq[i] = kfrag_kb(i);
-#pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                const bf16x8 kf = kq[i % AHEAD];
-                if (i + AHEAD < NS) kq[i % AHEAD] = kfrag_kb(i + AHEAD);
-                nxt.s[i / NQ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[i % NQ],
-                                                                        nxt.s[i / NQ], 0, 0, 0);
-#pragma unroll
-                for (int u = 0; u < EA; ++u) exp_elem(cur, i * EA + u, nm);
-            }
-            // keep that order: per score MFMA one fragment read and its
-            // share of the exponential work
-#pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, VA, 0); // VALU
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-            }
-            // phase B: P.V MFMAs of tile t | (mask and) row max of tile t+1
-            const int lim = row_lim - (j0 + BN + 4 * h);
-            float mx = -INFINITY;
-            bf16x8 vq[AHEAD];
-#pragma unroll
-            for (int j = 0; j < AHEAD; ++j) vq[j] = vfrag(Vc, j);
-#pragma unroll
-            for (int j = 0; j < NP; ++j) {
-                const bf16x8 vf = vq[j % AHEAD];
-                if (j + AHEAD < NP) vq[j % AHEAD] = vfrag(Vc, j + AHEAD);
-                const int cb = j % NDB, kc = j / NDB;
-                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kc >> 1][kc & 1], oacc[cb],
-                                                                   0, 0, 0);
-#pragma unroll
-                for (int u = 0; u < EB; ++u) {
-                    const int e = j * EB + u;
-                    float s = nxt.s[e >> 4][e & 15];
-                    if constexpr (NM) s = mask_elem(s, e, lim);
-                    nxt.s[e >> 4][e & 15] = s;
-                    mx = fmaxf(mx, s);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < NP; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, VB, 1); // VALU
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // LDS (transpose) reads
-            }
-            l_run += gsum;
-            rescale(pair_max(mx) * cs);
-        };
-        if (next_active && !next_masked && j0 + BN <= wave_full) {
-            steady(Unmasked());
-        } else {
-            // ---- edge steps: diagonal tiles, the last tile, skipped tiles
-            if (next_active) scores(Kn, nxt);
-            if (j0 <= wave_last) {
-#pragma unroll
-                for (int e = 0; e < NE; ++e) exp_elem(cur, e, nm);
-                l_run += gsum;
-                pv_tile(Vc);
-            }
-            if (next_active)
-                rescale(next_masked ? tile_max(nxt, j0 + BN, Masked())
-                                    : tile_max(nxt, j0 + BN, Unmasked()));
-        }
-        __syncthreads();
-    };
-
-    int t = 0;
-    for (; t + 1 < n_tiles; t += 2) {
-        step(t, SA, SB, Even());
-        step(t + 1, SB, SA, Odd());
+        for (int i = 0; i < NS; ++i) kfrag_read(0, i);
     }
-    if (t < n_tiles) step(t, SA, SB, Even());
+
+    // ---- phases 0 .. 2n + 1, one barrier between consecutive phases.
+    //      Group g runs MFMA(t) in local phase u = p - g = 2t and softmax(t)
+    //      in u = 2t + 1.  Before softmax(s) of either group K(s + 1) has
+    //      landed (its fragments are read then); before MFMA(s + 1), V(s).
+    //      K(s + 1) is copied in round s + 2 - NK, V(s) in round s + 2 - NV.
+    const int nph = 2 * n + 2;
+    auto end = [&](int p) {
+        if (p + 1 >= nph) return;
+        const int u = p - grp;
+        if (DUAL) {
+            // rounds issued so far: up to s - 1 after an MFMA phase (u = 2s),
+            // up to s after a softmax phase (u = 2s + 1)
+            if (u >= 0 && (u & 1) == 0) wait_rounds_after(NK - 3);   // K(s + 1)
+            else if (u >= 0) wait_rounds_after(NV - 2);               // V(s)
+        } else if (u & 1) {
+            // group 1 has issued rounds up to s = (u + 1) / 2 and needs
+            // K(s + 1); group 0 up to s = (u - 1) / 2 and needs V(s)
+            wait_rounds_after(grp == 1 ? NK - 2 : NV - 2);
+        }
+        phase_barrier();
+    };
+    auto idle = [&](int p) {
+        const int u = p - grp;
+        if (u & 1) {
+            const int r = round_of(u);
+            if (r >= 0) copy_part(r, 0, MAXOPS);
+        }
+        end(p);
+    };
+
+    int p = 0;
+    if (grp == 1) {  // group 1 idles in phase 0
+        idle(0);
+        p = 1;
+    }
+    if (last >= 0) {
+        __builtin_amdgcn_s_setprio(1);
+        mfma_phase(true, -1);
+        __builtin_amdgcn_s_setprio(0);
+        end(p);
+        ++p;
+        softmax_phase(0, round_of(1));
+        end(p);
+        ++p;
+        for (int t = 1; t <= last; ++t) {
+            __builtin_amdgcn_s_setprio(1);
+            mfma_phase(true, t - 1);
+            __builtin_amdgcn_s_setprio(0);
+            end(p);
+            ++p;
+            softmax_phase(t, round_of(2 * t + 1));
+            end(p);
+            ++p;
+        }
+        __builtin_amdgcn_s_setprio(1);
+        mfma_phase(false, last);
+        __builtin_amdgcn_s_setprio(0);
+        end(p);
+        ++p;
+    }
+    for (; p < nph; ++p) idle(p);  // tiles past this wave's rows: keep the ring moving
+    wait_vm(0);                     // no copy into LDS outlives the workgroup
 
     // ---- epilogue: O = O^T / l, lane holds columns 32cb + 8g4 + 4h .. +3 of row iq
-    const float l_tot = pair_sum(l_run);
-    if (iq < a.Tq) {
+    const float l_tot = pair_sum(l_a + l_b);
+    if (!ghost && iq < a.Tq) {
         const float inv = 1.f / l_tot;
         bf16* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Tq + iq) * D;
 #pragma unroll
@@ -491,9 +558,9 @@ void prefill_bf16_kernel(Args a) {
     }
 }
 
-template <int D>
+template <int D, bool DUAL>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-    typedef Cfg<D> C;
+    typedef Cfg<D, DUAL> C;
     Args a;
     a.q = static_cast<const bf16*>(p.q);
     a.k = static_cast<const bf16*>(p.k);
@@ -502,23 +569,26 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     a.lse = p.lse;
     a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Tq = p.Tq; a.Tk = p.Tk;
     a.R = p.Hq / p.Hkv;
-    a.G = p.B * p.Hkv;
-    a.n_qt = (p.Tq + C::BM - 1) / C::BM;
+    a.HP = (p.Hq + 1) / 2;
+    a.n_qt = (p.Tq + C::BMG - 1) / C::BMG;
     a.c = fmaxf(fabsf(p.scale) * kLog2e, 1e-30f);
     a.neg = p.scale < 0.f ? 0x80008000u : 0u;
     a.causal = p.causal;
     a.q_offset = p.causal ? p.q_offset : 0;
-    a.xcd = (a.G % 8 == 0) ? 1 : 0;
-    const long long n = (long long)a.n_qt * a.G * a.R;
-    hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)n), dim3(256), 0, stream, a);
+    const long long units = (long long)a.B * a.HP;
+    a.xcd = (units % 8 == 0) ? 1 : 0;
+    const long long nwg = (long long)a.n_qt * units;
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, DUAL>), dim3((unsigned)nwg), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const FwdParams& p, hipStream_t stream) {
-    if (p.d == 64) return launch_d<64>(p, stream);
-    return launch_d<128>(p, stream);
+hipError_t launch_prefill_bf16_d128(const FwdParams& p, hipStream_t stream) {
+    // the two query heads 2p, 2p + 1 of a workgroup share a K/V head iff the
+    // group size Hq / Hkv is even
+    const bool shared = (p.Hq / p.Hkv) % 2 == 0;
+    return shared ? launch_d<128, false>(p, stream) : launch_d<128, true>(p, stream);
 }
 
 }  // namespace rocattn
