@@ -74,20 +74,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     const size_t kv_head = (size_t)g * a.Tk * D;
     const int hq0 = hk * a.R;
 
-    // ---- query heads as the A operand: lane (rho, quarter) holds
-    //      q[hq0 + rho][DL*quarter + 8m .. +7]; the same channel order is
-    //      used for the key rows, so the products are unchanged.
+    // ---- query heads as the A operand: for MFMA m, lane (rho, quarter)
+    //      holds q[hq0 + rho][32m + 8 quarter .. +7]; key rows are read in
+    //      the same channel order, so the four lanes of a key row load 64
+    //      contiguous bytes per instruction.
     constexpr int NM = D / 32;
-    constexpr int DL = D / 4;
     const int rho = lane & 15, quarter = lane >> 4;
     bf16x8 qa[NM];
     {
         const bool ok = rho < a.R;
         const uint4* src = reinterpret_cast<const uint4*>(
-            a.q + (size_t)(b * a.Hq + hq0 + (ok ? rho : 0)) * D + DL * quarter);
+            a.q + (size_t)(b * a.Hq + hq0 + (ok ? rho : 0)) * D + 8 * quarter);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            uint4 u = src[m];
+            uint4 u = src[4 * m];
             if (!ok) u = make_uint4(0, 0, 0, 0);
             u.x ^= a.neg; u.y ^= a.neg; u.z ^= a.neg; u.w ^= a.neg;
             qa[m] = __builtin_bit_cast(bf16x8, u);
@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
 
     // ---- phase 1: scores of 16 keys per MFMA group
     const int ngroups = (nkeys + 15) >> 4;
-    const bf16* kbase = a.k + kv_head + DL * quarter;
-#pragma unroll 2
+    const bf16* kbase = a.k + kv_head + 8 * quarter;
+#pragma unroll 4
     for (int gi = wave; gi < ngroups; gi += 4) {
         const int kl = gi * 16 + rho;            // key (local) whose row this lane loads
         const bool kvalid = kl < nkeys;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, kp[m]);
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, kp[4 * m]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], kf, acc, 0, 0, 0);
         }
         // acc[r] = score of query head 4*quarter + r against key gi*16 + rho
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
     const bf16* vbase = a.v + kv_head + (size_t)j_begin * D + col;
-#pragma unroll 4
+#pragma unroll 8
     for (int j = wave * KPW + kk; j < nkeys; j += 4 * KPW) {
         const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vbase + (size_t)j * D);
         float vf[8];
@@ -197,14 +197,33 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(CombArgs a) {
     const size_t row = blockIdx.x;             // b * Hq + hq
     const int col = threadIdx.x;
     const float* mlr = a.ml + row * a.S * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < a.S; ++s) M = fmaxf(M, mlr[2 * s]);
-    float den = 0.f, acc = 0.f;
     const float* op = a.o_part + row * a.S * D + col;
-    for (int s = 0; s < a.S; ++s) {
-        const float w = exp2f(mlr[2 * s] - M);
-        den = fmaf(w, mlr[2 * s + 1], den);
-        acc = fmaf(w, op[(size_t)s * D], acc);
+    // the chunks' maxima, sums and partial outputs, loaded together in
+    // batches of 8 (one memory round trip per batch, not per chunk)
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < a.S; s0 += 8) {
+        float mv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mv[u] = s0 + u < a.S ? mlr[2 * (s0 + u)] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
+    }
+    float den = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < a.S; s0 += 8) {
+        float mv[8], lv[8], ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool ok = s0 + u < a.S;
+            mv[u] = ok ? mlr[2 * (s0 + u)] : -INFINITY;
+            lv[u] = ok ? mlr[2 * (s0 + u) + 1] : 0.f;
+            ov[u] = ok ? op[(size_t)(s0 + u) * D] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float w = exp2f(mv[u] - M);
+            den = fmaf(w, lv[u], den);
+            acc = fmaf(w, ov[u], acc);
+        }
     }
     a.o[row * D + col] = (bf16)(acc / den);
     if (a.lse && col == 0) a.lse[row] = (M + log2f(den)) * kLn2;
