@@ -2,7 +2,7 @@
 """Benchmark of the causal attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
-                    [--no-also] [--no-cpu] [--cpu-seconds S]
+                    [--no-also] [--no-cpu] [--cpu-seconds S] [--eager]
 
 A step is one pass of the hot path over one batch of the workload's seeded
 synthetic inputs, resident in HBM before timing starts:
@@ -10,7 +10,12 @@ synthetic inputs, resident in HBM before timing starts:
     forward (prefill), or the split-K decode step (decode workload).
 The headline workload (default 2: bf16 B8 H12 T1024 d64, causal MHA) is timed
 for K steps between HIP events on the stream the kernels run on, after W
-warm-up steps; the JSON line reports causal-adjusted TFLOP/s.
+warm-up steps; the JSON line reports causal-adjusted TFLOP/s.  The K steps
+are replays of a HIP graph holding 10 steps (--eager: direct launches), so
+short kernels are not timed against Python launch overhead; before timing, a
+one-step graph is replayed three times (inputs restored, outputs poisoned in
+between) and must reproduce the eager step bit for bit, else the workload is
+timed eagerly.
 
 FLOPs (causal-adjusted): 4 * B * Hq * d * N_vis, N_vis = sum_i min(Tk,
 q_offset + i + 1), i.e. two matrix products over the visible (query, key)
@@ -43,7 +48,8 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCES = {
-    "prefill_bf16": "transformer_causal_self_amd/csrc/attn_prefill_bf16.hip",
+    "prefill_bf16_d128": "transformer_causal_self_amd/csrc/attn_prefill_bf16.hip",
+    "prefill_bf16_d64": "transformer_causal_self_amd/csrc/attn_prefill_d64.hip",
     "decode_bf16": "transformer_causal_self_amd/csrc/attn_decode_bf16.hip",
     "rope": "transformer_causal_self_amd/csrc/rope.hip",
     "attn_f32": "transformer_causal_self_amd/csrc/attn_f32.hip",
@@ -95,10 +101,18 @@ def measured_traffic(kernel, workload_name):
 
 
 class Timer:
-    """HIP events on the current stream around n launches of fn()."""
+    """HIP events around n runs of fn() on the current stream.
 
-    def __init__(self, torch):
+    By default the runs are captured into a HIP graph (REPS runs per graph)
+    and the graph is replayed, so the timed region is GPU work back to back
+    rather than Python launch overhead between short kernels.  --eager times
+    direct launches instead."""
+
+    REPS = 10
+
+    def __init__(self, torch, eager=False):
         self.torch = torch
+        self.eager = eager
 
     def __call__(self, fn, n, warmup):
         torch = self.torch
@@ -107,12 +121,62 @@ class Timer:
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        if self.eager:
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n  # ms
+        reps = min(self.REPS, n)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        n_replay = max(1, n // reps)
         e0.record()
-        for _ in range(n):
-            fn()
+        for _ in range(n_replay):
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n  # ms
+        del g
+        return e0.elapsed_time(e1) / (n_replay * reps)  # ms
+
+
+def check_graph_replay(torch, fn, outputs, inputs, replays=3):
+    """A graph of one fn() replayed several times, with eager work and
+    synchronisation between replays, gives the eager result bit for bit
+    (inputs that fn changes in place are restored before each run)."""
+    saved = [x.clone() for x in inputs]
+
+    def restore():
+        for x, y in zip(inputs, saved):
+            x.copy_(y)
+
+    restore()
+    fn()
+    torch.cuda.synchronize()
+    want = [x.clone() for x in outputs]
+    g = torch.cuda.CUDAGraph()
+    restore()
+    with torch.cuda.graph(g):
+        fn()
+    ok = True
+    pure_outputs = [x for x in outputs if not any(x is y for y in inputs)]
+    for _ in range(replays):
+        restore()
+        for x in pure_outputs:
+            x.fill_(float("nan") if x.is_floating_point() else 0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ok = ok and all(torch.equal(x, y) for x, y in zip(outputs, want))
+    restore()
+    torch.cuda.synchronize()
+    del g
+    return ok
 
 
 def setup(w, torch, ra, wl, dev):
@@ -146,18 +210,31 @@ def setup(w, torch, ra, wl, dev):
             rope()
         attn()
 
-    return dict(step=step, attn=attn, rope=rope, decode=decode)
+    return dict(step=step, attn=attn, rope=rope, decode=decode, q=qd, k=kd, v=vd, o=od)
 
 
 def measure(w, args, torch, ra, wl, dev, steps, warmup):
     s = setup(w, torch, ra, wl, dev)
-    timer = Timer(torch)
+    timer = Timer(torch, eager=args.eager)
+    graph_ok = None
+    if not args.eager:
+        graph_ok = check_graph_replay(torch, s["step"], [s["o"], s["q"], s["k"]],
+                                      [s["q"], s["k"], s["v"]])
+        if not graph_ok:
+            print(f"# {w.name}: graph replay differs from eager launches; timing eagerly",
+                  file=sys.stderr)
+            timer = Timer(torch, eager=True)
     ms_step = timer(s["step"], steps, warmup)
     ms_attn = timer(s["attn"], steps, warmup)
-    out = dict(workload=w.name, ms_per_step=ms_step, attn_ms=ms_attn)
+    out = dict(workload=w.name, ms_per_step=ms_step, attn_ms=ms_attn,
+               timing="eager launches" if timer.eager else "HIP graph replay",
+               graph_replay_matches_eager=graph_ok)
+    if not timer.eager:  # the same steps launched directly, for comparison
+        out["ms_per_step_eager"] = Timer(torch, eager=True)(s["step"], steps, warmup)
     fl = attn_flops(w)
     by = attn_bytes(w)
-    kernel = "decode_bf16" if s["decode"] else ("attn_f32" if w.dtype == "f32" else "prefill_bf16")
+    kernel = ("decode_bf16" if s["decode"] else "attn_f32" if w.dtype == "f32"
+              else f"prefill_bf16_d{w.d}")
     out["attn_kernel"] = kernel
     out["attn_tflops"] = fl / (ms_attn * 1e-3) / 1e12
     out["attn_gbs"] = by / (ms_attn * 1e-3) / 1e9
@@ -252,6 +329,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time direct launches instead of HIP graph replays")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -322,6 +401,9 @@ def main():
                    "scale": w.scale, "rope": w.rope, "parallelism": "single GPU"},
         "pct_of_peak": 100.0 * roof["frac"],
         "roofline": roof,
+        "timing": head["timing"],
+        "ms_per_step_eager": head.get("ms_per_step_eager"),
+        "graph_replay_matches_eager": head["graph_replay_matches_eager"],
     }
 
     if not args.no_also:
