@@ -164,6 +164,13 @@ def test_attn_f32_shapes(B, Hq, Hkv, Tq, Tk, d, causal, qo, scale):
     (1, 2, 1, 150, 150, 64, True, 0, -0.125),       # negative temperature
     (1, 2, 1, 150, 150, 128, True, 0, 0.0),         # scale 0: prefix means
     (1, 2, 2, 190, 190, 128, True, 0, 0.5),         # peaky softmax
+    (2, 6, 2, 300, 300, 128, True, 0, 0.0884),      # 3 query heads per K/V head: pairs span K/V heads
+    (1, 3, 1, 200, 200, 128, True, 0, 0.0884),      # odd head count: a lone head in the last pair
+    (1, 5, 5, 130, 130, 128, True, 0, 0.0884),      # odd head count, one query head per K/V head
+    (1, 4, 2, 100, 357, 64, True, 257, 0.125),      # d 64: chunk appended to a cache
+    (1, 2, 1, 1000, 1000, 64, True, 0, 0.125),      # d 64: many tiles, ragged last tile
+    (1, 2, 1, 70, 1030, 64, False, 0, 0.125),       # d 64: no mask, ragged keys
+    (1, 4, 2, 70, 1030, 128, False, 0, 0.0884),     # d 128: no mask, ragged keys
 ])
 def test_attn_bf16_shapes(B, Hq, Hkv, Tq, Tk, d, causal, qo, scale):
     say("bf16", B, Hq, Hkv, Tq, Tk, d, causal, qo, scale)
