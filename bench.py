@@ -49,7 +49,7 @@ PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCES = {
     "prefill_bf16_d128": "transformer_causal_self_amd/csrc/attn_prefill_bf16.hip",
-    "prefill_bf16_d64": "transformer_causal_self_amd/csrc/attn_prefill_d64.hip",
+    "prefill_bf16_d64": "transformer_causal_self_amd/csrc/attn_prefill_bf16.hip",
     "decode_bf16": "transformer_causal_self_amd/csrc/attn_decode_bf16.hip",
     "rope": "transformer_causal_self_amd/csrc/rope.hip",
     "attn_f32": "transformer_causal_self_amd/csrc/attn_f32.hip",

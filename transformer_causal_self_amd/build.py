@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "librocattn.so")
-SOURCES = ["api.cpp", "attn_f32.hip", "attn_prefill_bf16.hip", "attn_prefill_d64.hip",
+SOURCES = ["api.cpp", "attn_f32.hip", "attn_prefill_bf16.hip",
            "attn_decode_bf16.hip", "rope.hip"]
 
 ARCH = "gfx950"

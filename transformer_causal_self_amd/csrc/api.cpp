@@ -85,8 +85,7 @@ int launch(const FwdParams& p, int dtype, hipStream_t stream, void* ws, size_t w
     else if (uses_decode(dtype, p.Tq, p.Hq, p.Hkv, p.d))
         e = rocattn::launch_decode_bf16(p, ws, ws_bytes, stream);
     else
-        e = p.d == 128 ? rocattn::launch_prefill_bf16_d128(p, stream)
-                       : rocattn::launch_prefill_bf16_d64(p, stream);
+        e = rocattn::launch_prefill_bf16(p, stream);
     return e == hipSuccess ? ROCATTN_OK : ROCATTN_ERR_HIP;
 }
 

@@ -1,6 +1,5 @@
 // attn_prefill_bf16.hip -- fused causal attention forward, bf16 in/out,
-// float32 accumulation, on the gfx950 matrix cores, head size 128 (the
-// kernel is written for 64 too; head size 64 uses attn_prefill_d64.hip).
+// float32 accumulation, on the gfx950 matrix cores, head sizes 64 and 128.
 //
 // What it computes: for every (batch b, query head hq, query row i)
 //     o_i = sum_j softmax_j(scale * q_i . k_j + M_ij) v_j
@@ -12,54 +11,48 @@
 // T x T score matrix never leaves registers ("Grasping Codes and Math 02" --
 // Flash Attention).
 //
-// Design.  One workgroup = 8 waves in two groups of four.  Both groups cover
-// the same 128 query rows (32 per wave), group g of query head 2p + g, so
-// their causal extents are identical and they walk the key tiles in
-// lockstep.  Waves w and w + 4 share a SIMD.
-//  * Ping-pong: a group alternates an MFMA phase (scores of key tile t and
-//    the P.V product of tile t - 1) with a softmax phase (mask, weights,
-//    row sum of tile t).  Group 1 runs one phase behind group 0, and one
-//    s_barrier separates consecutive phases, so on every SIMD one wave feeds
-//    the matrix core while the other keeps the vector ALU busy.
-//  * One wave issues LDS reads and HBM -> LDS copies only so fast (each
-//    blocks its instruction stream for tens of cycles, and an LDS read takes
-//    several hundred cycles to return), so that work is split between the
-//    phases: the softmax phase reads the K fragments of the next tile into
-//    registers and issues this wave's share of the tile copies between its
-//    exponentials; the MFMA phase reads one V^T fragment ahead of each score
-//    MFMA, for the P.V MFMAs that follow.
-//  * Scores are formed transposed, S^T = K Q^T (keys on the MFMA rows,
-//    queries on its columns; v_mfma_f32_32x32x16_bf16), so each lane holds
-//    scores of ONE query row: the row max and row sum need only one
-//    v_permlane32_swap between the two half-waves, and the running max,
-//    sum and rescale factor of a row are per-lane scalars.
-//  * K and V tiles of 64 keys go from HBM straight into an LDS ring
-//    (global_load_lds_dwordx4; no staging registers, no LDS stores) three
-//    tiles deep, copied by one group of four waves each, about three phases
-//    before use.  When both query heads of a workgroup use the same K/V head
-//    (GQA with an even group size) the two groups share one ring (group 1
-//    copies K, group 0 V), otherwise each group has its own.  Each 16-byte
+// Design (one workgroup = 4 waves = 128 query rows of one (b, hq); several
+// workgroups per CU):
+//  * Each wave owns 32 query rows; its Q fragment stays in registers as the
+//    B operand of v_mfma_f32_32x32x16_bf16.  The kernel is kept small so
+//    that several waves share each SIMD (four at head size 64, about 120
+//    VGPRs; three at head size 128, about 145): the latency of LDS reads,
+//    copies and barriers is hidden by the other waves rather than by a
+//    software pipeline inside one wave.  Measured faster than a two-group
+//    ping-pong kernel with a three-tile ring (two workgroups per CU) at both
+//    head sizes, and than 64-row waves at head size 64.
+//  * Keys are visited in tiles of 64 (head size 64) or 32 (head size 128).
+//    K and V tiles go from HBM straight into two LDS rings of two tiles
+//    (global_load_lds_dwordx4: two 16-byte copies per lane fill a tile at
+//    either head size), issued one tile ahead.  Each 16-byte
 //    chunk of a tile row sits at a position XOR-swizzled by the row, so the
-//    fragment reads hit distinct LDS banks.
+//    fragment reads hit distinct banks.
+//  * Scores are formed transposed, S^T = K Q^T (keys on the MFMA rows,
+//    queries on its columns), so each lane holds 16 scores of one query row
+//    per 32-key block: the row max and row sum need no cross-lane work except
+//    one v_permlane32_swap between the two half-waves.
+//  * Tile step t: scores of tile t (K fragments from LDS), mask when the
+//    tile straddles the diagonal, weights, P.V (V^T fragments from LDS);
+//    one barrier per tile.
 //  * Softmax in base 2: p = 2^(s * |scale| * log2(e) - m) with the raw
-//    v_exp_f32, first against the running max m as it stands: only when a
-//    row's weights would exceed 2^12 (or on its first tile, where m = -inf)
-//    does the row take the tile's max, rescale its accumulator and
-//    recompute.  The final division by the row sum cancels whichever m was
-//    used.  A negative scale is applied by negating q on load.  The row sum
-//    adds the bf16-rounded weights that feed the P.V product
-//    (v_dot2_f32_bf16 against (1, 1)), so V = 1 gives O = 1.
+//    v_exp_f32, against the running max m as it stands (no per-tile row
+//    max): only when a row's weights would exceed 2^12 does the row take
+//    the tile's max, rescale its accumulator and recompute.  The running
+//    max starts at tile 0's max; the final division by the row sum cancels
+//    whichever m was used.  A negative scale is applied by negating q on
+//    load.  The row sum adds the bf16-rounded weights that feed the P.V
+//    product (v_dot2_f32_bf16 against (1, 1)), so V = 1 gives O = 1.
 //  * P^T, rounded to bf16, is already in the B-operand layout of the second
 //    product O^T += V^T P^T.  The A operand V^T is read from the row-major V
 //    tile with ds_read_b64_tr_b16 (the LDS transpose read of gfx950), whose
 //    four-row gather is matched to the key order of the score accumulator.
 //  * Tiles past a wave's last visible key are skipped (the wave still takes
-//    part in the barriers); only tiles that straddle the diagonal or the end
-//    of the keys pay for masking.
+//    part in the barriers and copies); only tiles that straddle the
+//    diagonal or the end of the keys pay for masking.
 //  * Workgroups are issued longest-first (largest query tile first), and,
-//    when the number of head pairs is a multiple of 8, consecutive head
-//    pairs (which share K/V heads under GQA) are placed on one XCD
-//    (workgroup id modulo 8) so their K/V tiles are served from its L2.
+//    when the number of batch x K/V heads is a multiple of 8, the query
+//    heads that share a K/V head are placed on the same XCD (workgroup id
+//    modulo 8) so their K/V tiles are served from that XCD's L2.
 #include <math.h>
 
 #include "internal.hpp"
@@ -67,27 +60,33 @@
 namespace rocattn {
 namespace {
 
-template <int D, bool DUAL>
+// Tile shape and occupancy per head size (chosen by measurement):
+//   d = 64:  64-key tiles, four waves per SIMD (about 120 VGPRs)
+//   d = 128: 32-key tiles, three waves per SIMD (about 145 VGPRs)
+template <int D>
 struct Cfg {
-    static constexpr int BN = 64;                        // keys per tile
-    static constexpr int BMG = 128;                      // query rows per group
-    static constexpr int NCH = D / 8;                    // 16-byte chunks per key row
-    static constexpr int TB = BN * D * 2;                // bytes of one K or V tile
-    // ring depths (tiles); a tile is copied by the four waves of one group
-    static constexpr int NK = (DUAL && D == 64) ? 4 : 3;
-    static constexpr int NV = (DUAL && D == 128) ? 2 : 3;
-    static constexpr int NINS = BN * NCH / 256;          // copy instructions per lane per tile
-    static constexpr int RSTR = 256 / NCH;               // tile rows filled by one copy instruction
-    static constexpr int MAXOPS = (DUAL ? 2 : 1) * NINS; // copy instructions per lane per round
-    static constexpr int RING = (NK + NV) * TB;          // K slots, then V slots, of one ring
-    static constexpr int LDS = (DUAL ? 2 : 1) * RING;
-    static_assert(NINS >= 1 && BN % RSTR == 0, "copy instructions must tile the key block");
-    static_assert(LDS <= 160 * 1024, "LDS of one workgroup");
+    static constexpr int BN = D == 64 ? 64 : 32;    // keys per tile
+    static constexpr int WPE = D == 64 ? 4 : 3;     // waves per SIMD
+    static constexpr int NW = 4;                    // waves per workgroup
+    static constexpr int RB = 1;                    // 32-row blocks per wave (the code allows more)
+    static constexpr int BM = NW * RB * 32;         // query rows per workgroup
+    static constexpr int NCH = D / 8;               // 16-byte chunks per key row
+    static constexpr int TB = BN * D * 2;           // bytes of one K or V tile
+    static constexpr int NRING = 2;                 // tiles per ring
+    static constexpr int NQ = D / 16;               // 16-wide d slices of q.k
+    static constexpr int NDB = D / 32;              // 32-column blocks of the output
+    static constexpr int NKC = BN / 16;             // 16-key slices of a tile
+    static constexpr int NKB = BN / 32;             // 32-key blocks of a tile
+    static constexpr int NE = 16 * NKB;             // scores per lane per row block and tile
+    static constexpr int CPL = NW * 64;             // lanes of a workgroup (all of them copy)
+    static constexpr int NINS = BN * NCH / CPL;     // 16-byte copies per lane per tile
+    static constexpr int RSTR = CPL / NCH;          // tile rows filled by one copy instruction
+    static_assert(BN % 32 == 0 && NINS >= 1, "tiles of whole 32-key blocks");
 };
 
 // XOR swizzles of the 16-byte chunk position within a tile row.
-//  K: sixteen consecutive rows read the same logical chunk (ds_read_b128),
-//     so the rows' chunks must fall in distinct 16-byte bank groups.
+//  K: the rows of a fragment read the same logical chunk (ds_read_b128), so
+//     the rows' chunks must fall in distinct 16-byte bank groups.
 //  V: four consecutive rows are read 64 bytes each (transpose reads), so the
 //     rows' 64-byte segments must fall in distinct 64-byte bank groups.
 template <int D>
@@ -103,13 +102,13 @@ struct Args {
     float* lse;
     int B, Hq, Hkv, Tq, Tk;
     int R;         // query heads per K/V head
-    int HP;        // head pairs per batch entry, ceil(Hq / 2)
-    int n_qt;      // query tiles (of 128 rows) per head
+    int G;         // B * Hkv
+    int n_qt;      // query tiles (of BM rows) per head
     float c;       // |scale| * log2(e), at least 1e-30 so that -inf * c = -inf
     unsigned neg;  // 0x80008000 when scale < 0 (q is negated on load), else 0
     int causal;
     int q_offset;
-    int xcd;       // 1: place consecutive head pairs on one XCD
+    int xcd;       // 1: group the heads of one K/V head on one XCD
 };
 
 __device__ inline float pair_max(float x) {
@@ -134,7 +133,7 @@ __device__ inline unsigned lds_addr(const void* p) {
 // One 16-byte HBM -> LDS copy per lane: lane L of the wave writes LDS bytes
 // [lds + 16 L, lds + 16 L + 16) with the 16 bytes at sbase + voff.  Written
 // as assembly so the compiler does not guard every later LDS read with a
-// wait for it; the kernel waits itself (wait_vm) before the barrier that
+// wait for it; the kernel waits itself (wait_vm*) before the barrier that
 // publishes the tile.  Nothing else in this kernel uses m0.
 __device__ inline void copy16(const void* sbase, unsigned voff, unsigned lds) {
     // base and LDS address are wave-uniform; say so, so they live in SGPRs
@@ -146,421 +145,306 @@ __device__ inline void copy16(const void* sbase, unsigned voff, unsigned lds) {
                  :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base) : "memory");
 }
 
-// Wait until at most n of this wave's vector-memory operations are in flight.
-__device__ inline void wait_vm(int n) {
-    switch (n) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-        case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    }
+// Wait until at most N (0) of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ inline void wait_vm() {
+    if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Marks a value as read and rewritten here, so its computation stays on this
-// side of the following barrier.
-template <typename T>
-__device__ inline void pin(T& x) {
-    asm volatile("" : "+v"(x));
-}
+template <int D>
+struct Scores {
+    f32x16 s[Cfg<D>::RB][Cfg<D>::NKB];
+};
 
-__device__ inline void phase_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int D, bool DUAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_bf16_kernel(Args a) {
-    typedef Cfg<D, DUAL> C;
-    constexpr int BN = C::BN, TB = C::TB, NK = C::NK, NV = C::NV, NINS = C::NINS;
-    constexpr int MAXOPS = C::MAXOPS;
-    constexpr int NKB = BN / 32;       // 32-key blocks per tile
-    constexpr int NDB = D / 32;        // 32-column blocks of the output
-    constexpr int NQ = D / 16;         // 16-wide d slices of q.k
-    constexpr int NS = NQ * NKB;       // score MFMAs per tile
-    constexpr int NKC = BN / 16;       // 16-key slices of a tile
-    constexpr int NP = NDB * NKC;      // P.V MFMAs per tile
-    constexpr int NE = NKB * 16;       // scores per lane per tile
-    __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+template <int D>
+__global__ __launch_bounds__(Cfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(Cfg<D>::WPE, Cfg<D>::WPE)))
+void prefill_kernel(Args a) {
+    typedef Cfg<D> C;
+    constexpr int BN = C::BN, NW = C::NW, RB = C::RB, BM = C::BM, NCH = C::NCH, TB = C::TB;
+    constexpr int NRING = C::NRING, NQ = C::NQ, NDB = C::NDB, NKC = C::NKC, NKB = C::NKB;
+    constexpr int NE = C::NE, CPL = C::CPL, NINS = C::NINS, RSTR = C::RSTR;
+    (void)NW;
+    __shared__ __attribute__((aligned(1024))) char lds[2 * NRING * TB];  // K ring, then V ring
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, wave-uniform
-    const int grp = wave >> 2, wg = wave & 3;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int h = lane >> 5, li = lane & 31;
 
-    // ---- which (query tile, batch, head pair) this workgroup owns
-    int qt, unit;
+    // ---- which (query tile, batch, query head) this workgroup owns
+    int qt, g, rep;
     {
         const int w = blockIdx.x;
-        const int P = a.B * a.HP;
         if (a.xcd) {
-            const int x = w & 7, s = w >> 3, per = P >> 3;
-            const int rank = s / per;
-            unit = x * per + (s - rank * per);
+            const int x = w & 7, s = w >> 3;
+            const int per = (a.G >> 3) * a.R;
+            const int rank = s / per, rem = s - rank * per;
+            g = x * (a.G >> 3) + rem / a.R;
+            rep = rem % a.R;
             qt = a.n_qt - 1 - rank;
         } else {
-            const int rank = w / P;
-            unit = w - rank * P;
+            const int per = a.G * a.R;
+            const int rank = w / per, rem = w - rank * per;
+            g = rem / a.R;
+            rep = rem % a.R;
             qt = a.n_qt - 1 - rank;
         }
     }
-    const int b = unit / a.HP, pp = unit - (unit / a.HP) * a.HP;
-    const int hq_raw = 2 * pp + grp;
-    const bool ghost = hq_raw >= a.Hq;          // odd Hq: the last pair has one head
-    const int hq = ghost ? 2 * pp : hq_raw;
-    const int hk = hq / a.R;
-    const int i0 = qt * C::BMG;
-    const int i0w = i0 + 32 * wg;
-    const int iq = i0w + li;                    // this lane's query row
+    const int b = g / a.Hkv, hk = g - (g / a.Hkv) * a.Hkv;
+    const int hq = hk * a.R + rep;
+    const int i0 = qt * BM;
+    const int i0w = i0 + 32 * RB * wave;      // first row of this wave
+    int iq[RB];                               // this lane's query rows
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) iq[rb] = i0w + 32 * rb + li;
 
-    // ---- Q fragment (B operand of S^T): lane holds q[iq][16m + 8h .. +7]
-    bf16x8 qf[NQ];
-    {
-        const int row = iq < a.Tq ? iq : a.Tq - 1;
+    // ---- Q fragments (B operand): lane holds q[iq[rb]][16m + 8h .. +7]
+    bf16x8 qf[RB][NQ];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int row = iq[rb] < a.Tq ? iq[rb] : a.Tq - 1;
         const uint4* src = reinterpret_cast<const uint4*>(
             a.q + ((size_t)(b * a.Hq + hq) * a.Tq + row) * D + 8 * h);
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
             uint4 u = src[2 * m];
-            if (iq >= a.Tq) u = make_uint4(0, 0, 0, 0);
+            if (iq[rb] >= a.Tq) u = make_uint4(0, 0, 0, 0);
             u.x ^= a.neg; u.y ^= a.neg; u.z ^= a.neg; u.w ^= a.neg;
-            qf[m] = __builtin_bit_cast(bf16x8, u);
+            qf[rb][m] = __builtin_bit_cast(bf16x8, u);
         }
     }
 
     // ---- visibility limits (the wave's are wave-uniform)
-    const int kv_end = a.causal ? min(a.Tk, a.q_offset + i0 + C::BMG) : a.Tk;
-    const int n = (kv_end + BN - 1) / BN;       // key tiles of the workgroup
-    const int row_lim = a.causal ? min(a.Tk - 1, a.q_offset + iq) : a.Tk - 1;
-    const int wave_last = a.causal ? min(a.Tk - 1, a.q_offset + i0w + 31) : a.Tk - 1;
+    const int kv_end = a.causal ? min(a.Tk, a.q_offset + i0 + BM) : a.Tk;
+    const int n = (kv_end + BN - 1) / BN;    // key tiles of the workgroup
+    int row_lim[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) row_lim[rb] = a.causal ? min(a.Tk - 1, a.q_offset + iq[rb]) : a.Tk - 1;
+    const int wave_last = a.causal ? min(a.Tk - 1, a.q_offset + i0w + 32 * RB - 1) : a.Tk - 1;
     // keys below wave_full are visible to every row of the wave
     const int wave_full = a.causal ? min(a.Tk, a.q_offset + i0w + 1) : a.Tk;
-    // last tile this wave computes (-1: none)
-    const int last = (ghost || i0w >= a.Tq) ? -1 : wave_last / BN;
+    const int last = i0w >= a.Tq ? -1 : wave_last / BN;  // last tile this wave computes
 
-    // ---- K/V ring: NK K slots, then NV V slots.  With a shared ring, group 1
-    //      copies the K tiles and group 0 the V tiles; with one ring per
-    //      group, each group copies its own.  Copy round r fills K(r + NK - 1)
-    //      and V(r + NV - 2); a wave issues its part of a round during one of
-    //      its softmax phases (rounds below 0 form the prologue).
-    const unsigned ring = lds_addr(lds) + (DUAL ? (unsigned)(grp * C::RING) : 0u);
+    // ---- K/V rings.  Copy of tile t: lane (wave, lane) fills the tile's
+    //      16-byte slot 64 wave + lane, i.e. row cp_r0 at chunk position
+    //      cp_p, with the logical chunk the swizzle puts there.  A tile at or
+    //      past n is never read: its copy re-reads tile n-1 into the slot it
+    //      would occupy, which holds no live data then.  Rows past the last
+    //      key re-read the last key (finite values; those keys are masked).
+    const unsigned kring = lds_addr(lds), vring = kring + NRING * TB;
     const bf16* kh = a.k + (size_t)(b * a.Hkv + hk) * a.Tk * D;
     const bf16* vh = a.v + (size_t)(b * a.Hkv + hk) * a.Tk * D;
-    // copy instruction i of a tile: lane (wg, lane) fills the tile's 16-byte
-    // slot 256 i + 64 wg + lane, i.e. row cp_r0 + i * RSTR at chunk cp_p
-    const int cl = wg * 64 + lane;
-    const int cp_r0 = cl / C::NCH, cp_p = cl % C::NCH;
+    const int cl = wave * 64 + lane;
+    const int cp_r0 = cl / NCH, cp_p = cl % NCH;
     const unsigned cp_kcol = 16u * (unsigned)(cp_p ^ swz_k<D>(cp_r0));
     const unsigned cp_vcol = 16u * (unsigned)(cp_p ^ swz_v<D>(cp_r0));
-    const unsigned cp_lds = (unsigned)(wg * 64 * 16);
-    // slots are taken modulo the ring depth for any tile index (negative
-    // ones included)
-    auto kslot = [&](int t) { return ring + (unsigned)((((t % NK) + NK) % NK) * TB); };
-    auto vslot = [&](int t) { return ring + (unsigned)((NK + ((t % NV) + NV) % NV) * TB); };
-    auto copy_ins = [&](const bf16* head, int t, unsigned slot, unsigned col, int i) {
-        // a tile outside 0 .. n-1 is never read: its copy re-reads a valid
-        // tile into the slot it would occupy, which holds no live data then
-        const int j0 = min(max(t, 0), n - 1) * BN;
-        const char* base = reinterpret_cast<const char*>(head + (size_t)j0 * D);
-        // rows past the last key re-read the last key (finite; masked)
-        const int row = min(cp_r0 + i * C::RSTR, a.Tk - 1 - j0);
-        copy16(base, (unsigned)row * (unsigned)(D * 2) + col, slot + (unsigned)(i * 256 * 16) + cp_lds);
-    };
-    // Every round issues the same MAXOPS copy instructions per lane (K ones
-    // first), so the number of copies in flight after a given round is a
-    // compile-time constant.
-    auto copy_part = [&](int r, int q0, int q1) {
-        const int tk = r + NK - 1, tv = r + NV - 2;
-        // shared ring: group 1 copies K(tk), group 0 V(tv) (selected, not branched)
-        const bool sk = grp == 1;
-        const bf16* sh = sk ? kh : vh;
-        const int st = sk ? tk : tv;
-        const unsigned ss = sk ? kslot(tk) : vslot(tv);
-        const unsigned sc = sk ? cp_kcol : cp_vcol;
+    const unsigned cp_lds = (unsigned)(wave * 64 * 16);
+    auto kslot = [&](int t) { return kring + (unsigned)((t % NRING) * TB); };
+    auto vslot = [&](int t) { return vring + (unsigned)((t % NRING) * TB); };
+    auto copy_tile = [&](const bf16* head, int t, unsigned slot, unsigned col) {
+        const int j0 = min(t, n - 1) * BN;
 #pragma unroll
-        for (int q = 0; q < MAXOPS; ++q) {
-            if (q < q0 || q >= q1) continue;
-            if (DUAL) {
-                if (q < NINS) copy_ins(kh, tk, kslot(tk), cp_kcol, q);
-                else copy_ins(vh, tv, vslot(tv), cp_vcol, q - NINS);
-            } else {
-                copy_ins(sh, st, ss, sc, q);
-            }
+        for (int i = 0; i < NINS; ++i) {
+            const int row = min(cp_r0 + i * RSTR, a.Tk - 1 - j0);
+            copy16(head + (size_t)j0 * D, (unsigned)row * (unsigned)(D * 2) + col,
+                   slot + (unsigned)(i * CPL * 16) + cp_lds);
         }
     };
-    // wait until this lane's copies of a round have landed while those of
-    // the `later` rounds issued after it may still be in flight
-    auto wait_rounds_after = [&](int later) { wait_vm(later * MAXOPS); };
-    // the round a wave issues during its local phase u (odd u: a softmax or
-    // idle phase); below 0: none
-    auto round_of = [&](int u) { return (!DUAL && grp == 1) ? (u + 1) >> 1 : (u - 1) >> 1; };
 
-    // ---- per-lane fragment offsets in a tile (bytes).  In both the row
-    //      term, the swizzled chunk term and the in-chunk term occupy
-    //      disjoint bits, so the offset for slice m (block cb) is the slice-0
-    //      offset XOR 32m (64cb).
-    // K operand (A of S^T): key row 32kb + li, logical chunk 2m + h
+    // ---- per-lane fragment offsets in a tile (bytes).  The row term, the
+    //      swizzled chunk term and the in-chunk term occupy disjoint bits, so
+    //      slice m (block cb) is the slice-0 offset XOR 32m (64cb).
+    // K operand (A of S^T): key row li, logical chunk 2m + h
     const unsigned koff = 2u * (unsigned)(li * D + 8 * (h ^ swz_k<D>(li)));
     // V^T operand via transpose reads: supplying lane (16g + 4r + qq) points
     // at V[key_base + 4(g/2) + r][32 cb + 16(g%2) + 4qq] (logical column)
     const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
     const unsigned voff =
         2u * (unsigned)((4 * (tg >> 1) + tr) * D + 16 * (tg & 1) + 4 * tq + 8 * swz_v<D>(tr));
-
-    f32x16 oacc[NDB];
-#pragma unroll
-    for (int cb = 0; cb < NDB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
-    f32x16 sacc[NKB];
-    bf16x8 pb[NKC];
-    float m_run = -INFINITY, l_a = 0.f, l_b = 0.f;
-    const float cs = a.c;
-
-    // K fragments of the next tile, read into registers during the softmax
-    // phase (so the LDS reads of a SIMD are spread over both of its waves)
-    bf16x8 kpre[NS];
-    // One MFMA phase: S^T = K(t) Q^T on the prefetched K fragments (when
-    // `scores`), then O^T += V^T(tv) P^T (when tv >= 0).  The V^T fragment of
-    // P.V MFMA j is read before score MFMA j, so it has the whole score
-    // product to arrive (an LDS read takes several hundred cycles); its
-    // registers take the place of the K fragment just consumed.  Hard
-    // scheduling fences keep that order.
-    auto mfma_phase = [&](bool scores, int tv) {
-        const unsigned vb0 = vslot(tv < 0 ? 0 : tv) + voff;
-        auto vfrag = [&](int j) {
-            const int kc = j / NDB, cb = j % NDB;
-            const unsigned addr = (vb0 + (unsigned)(16 * kc * D * 2)) ^ (64u * cb);
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
-            const i16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 16u * D));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        bf16x8 vf[NP];
-        if (scores) {
-#pragma unroll
-            for (int i = 0; i < NS; ++i) {
-                if (tv >= 0 && i < NP) vf[i] = vfrag(i);
-                __builtin_amdgcn_sched_barrier(0);
-                const int m = i / NKB, kb = i % NKB;
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kpre[i], qf[m],
-                                                                   i < NKB ? f32x16{} : sacc[kb], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) pin(sacc[kb]);
-        }
-        if (tv >= 0) {
-            constexpr int DONE = NS < NP ? NS : NP;   // fragments already read
-#pragma unroll
-            for (int j = 0; j < NP; ++j) {
-                if (!scores || j >= DONE) vf[j] = vfrag(j);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < NP; ++j) {
-                const int kc = j / NDB, cb = j % NDB;
-                oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pb[kc], oacc[cb], 0, 0, 0);
-            }
-#pragma unroll
-            for (int cb = 0; cb < NDB; ++cb) pin(oacc[cb]);
-        }
+    auto kfrag = [&](int t, int kb, int m) {
+        return *(lds_bf16x8*)(uintptr_t)((kslot(t) + koff + (unsigned)(kb * 32 * D * 2)) ^ (32u * m));
+    };
+    auto vfrag = [&](int t, int cb, int kc) {
+        const unsigned addr = (vslot(t) + voff + (unsigned)(16 * kc * D * 2)) ^ (64u * cb);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 16u * D));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    // key offset (within the tile) of score element e = 16 kb + r of a lane
-    auto key_of = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3); };
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-
-    // weights p = 2^(s c - m) of 16-key slice kc in bf16 (the B operand of
-    // P.V) and this lane's part of their sum
-    auto weights_kc = [&](int kc, float m, float& sa, float& sb) {
-        const float nm = -m;
+    f32x16 oacc[RB][NDB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = 8 * kc + 2 * u;
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][e & 15], cs, nm));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 4][(e + 1) & 15], cs, nm));
-            bf16x2 pk;
-            pk[0] = (bf16)p0;
-            pk[1] = (bf16)p1;
-            pb[kc][2 * u] = pk[0];
-            pb[kc][2 * u + 1] = pk[1];
-            if (u & 1) sb = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, sb, false);
-            else sa = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, sa, false);
-        }
-    };
-    auto kfrag_read = [&](int t, int i) {
-        const int m = i / NKB, kb = i % NKB;
-        const unsigned addr = (kslot(t) + koff + (unsigned)(kb * 32 * D * 2)) ^ (32u * m);
-        kpre[i] = *(lds_bf16x8*)(uintptr_t)addr;
-    };
-
-    // softmax phase of tile t (issuing copy round r): mask, then
-    // per 16-key slice the weights against the running max, with the K
-    // fragment reads of tile t + 1 and the copy instructions spread between
-    // the slices (one wave issues LDS reads and copies only so fast).  Only
-    // when some weight would exceed 2^12 (or on the first tile, where the
-    // running max is -inf) take the row max, raise the running max and
-    // recompute.
-    constexpr int CPC = (MAXOPS + NKC - 1) / NKC;              // copies per slice
-    auto softmax_phase = [&](int t, int r) {
-        const int j0 = t * BN;
-        if (j0 + BN > wave_full) {
-            const int lim = row_lim - (j0 + 4 * h);
-#pragma unroll
-            for (int e = 0; e < NE; ++e)
-                if (key_of(e) > lim) sacc[e >> 4][e & 15] = -INFINITY;
-        }
-        float sa = 0.f, sb = 0.f;
-        // the K fragment reads go first: an LDS read takes several hundred
-        // cycles to return (a read of a tile this wave will not use is harmless)
-#pragma unroll
-        for (int i = 0; i < NS; ++i) kfrag_read(t + 1, i);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            copy_part(r, kc * CPC, (kc + 1) * CPC);
-            weights_kc(kc, m_run, sa, sb);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const bool big = !(sa + sb <= 4096.f);
-        if (__any(big)) {
-            // rows (both half-wave lanes of a row) whose weights got too big
-            // take their tile max; the other rows keep m_run (alpha = 1) and
-            // recompute the very same weights
-            const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)big, (unsigned)big, false, false);
-            const bool row_big = (sw[0] | sw[1]) != 0u;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < NE; ++e) mx = fmaxf(mx, sacc[e >> 4][e & 15]);
-            const float tmax = pair_max(mx) * cs;
-            const float m_new = row_big ? fmaxf(m_run, tmax) : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_a *= alpha;
-            l_b *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < NDB; ++cb)
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) oacc[cb][rr] *= alpha;
-            m_run = m_new;
-            sa = 0.f;
-            sb = 0.f;
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) weights_kc(kc, m_run, sa, sb);
-        }
-        l_a += sa;
-        l_b += sb;
-        // the weights, sums and prefetched fragments are finished inside this
-        // phase, not sunk past the barrier into the next one
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) pin(pb[kc]);
-        pin(l_a);
-        pin(l_b);
-#pragma unroll
-        for (int i = 0; i < NS; ++i) pin(kpre[i]);
-    };
-
-    // ---- prologue: copy rounds 1-NK .. -1; K(0) lands before the first barrier
-    for (int r = 1 - NK; r < 0; ++r) copy_part(r, 0, MAXOPS);
-    if (DUAL || grp == 1) wait_rounds_after(NK - 2);
-    phase_barrier();
-    if (last >= 0) {
-#pragma unroll
-        for (int i = 0; i < NS; ++i) kfrag_read(0, i);
-    }
-
-    // ---- phases 0 .. 2n + 1, one barrier between consecutive phases.
-    //      Group g runs MFMA(t) in local phase u = p - g = 2t and softmax(t)
-    //      in u = 2t + 1.  Before softmax(s) of either group K(s + 1) has
-    //      landed (its fragments are read then); before MFMA(s + 1), V(s).
-    //      K(s + 1) is copied in round s + 2 - NK, V(s) in round s + 2 - NV.
-    const int nph = 2 * n + 2;
-    auto end = [&](int p) {
-        if (p + 1 >= nph) return;
-        const int u = p - grp;
-        if (DUAL) {
-            // rounds issued so far: up to s - 1 after an MFMA phase (u = 2s),
-            // up to s after a softmax phase (u = 2s + 1)
-            if (u >= 0 && (u & 1) == 0) wait_rounds_after(NK - 3);   // K(s + 1)
-            else if (u >= 0) wait_rounds_after(NV - 2);               // V(s)
-        } else if (u & 1) {
-            // group 1 has issued rounds up to s = (u + 1) / 2 and needs
-            // K(s + 1); group 0 up to s = (u - 1) / 2 and needs V(s)
-            wait_rounds_after(grp == 1 ? NK - 2 : NV - 2);
-        }
-        phase_barrier();
-    };
-    auto idle = [&](int p) {
-        const int u = p - grp;
-        if (u & 1) {
-            const int r = round_of(u);
-            if (r >= 0) copy_part(r, 0, MAXOPS);
-        }
-        end(p);
-    };
-
-    int p = 0;
-    if (grp == 1) {  // group 1 idles in phase 0
-        idle(0);
-        p = 1;
-    }
-    if (last >= 0) {
-        __builtin_amdgcn_s_setprio(1);
-        mfma_phase(true, -1);
-        __builtin_amdgcn_s_setprio(0);
-        end(p);
-        ++p;
-        softmax_phase(0, round_of(1));
-        end(p);
-        ++p;
-        for (int t = 1; t <= last; ++t) {
-            __builtin_amdgcn_s_setprio(1);
-            mfma_phase(true, t - 1);
-            __builtin_amdgcn_s_setprio(0);
-            end(p);
-            ++p;
-            softmax_phase(t, round_of(2 * t + 1));
-            end(p);
-            ++p;
-        }
-        __builtin_amdgcn_s_setprio(1);
-        mfma_phase(false, last);
-        __builtin_amdgcn_s_setprio(0);
-        end(p);
-        ++p;
-    }
-    for (; p < nph; ++p) idle(p);  // tiles past this wave's rows: keep the ring moving
-    wait_vm(0);                     // no copy into LDS outlives the workgroup
-
-    // ---- epilogue: O = O^T / l, lane holds columns 32cb + 8g4 + 4h .. +3 of row iq
-    const float l_tot = pair_sum(l_a + l_b);
-    if (!ghost && iq < a.Tq) {
-        const float inv = 1.f / l_tot;
-        bf16* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Tq + iq) * D;
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < NDB; ++cb)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                bf16x4 val;
+            for (int r = 0; r < 16; ++r) oacc[rb][cb][r] = 0.f;
+    float m_run[RB], l_run[RB];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[cb][4 * g4 + e] * inv);
-                *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * g4 + 4 * h) = val;
+    for (int rb = 0; rb < RB; ++rb) { m_run[rb] = -INFINITY; l_run[rb] = 0.f; }
+    const float cs = a.c;
+    bf16x8 pb[RB][NKC];
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+
+    // key offset (within the tile, before + 4h) of score element e
+    auto key_of = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3); };
+
+    // S^T(tile t) = K(t) Q^T, plain order
+    auto scores = [&](int t, Scores<D>& S) {
+#pragma unroll
+        for (int m = 0; m < NQ; ++m)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8 kf = kfrag(t, kb, m);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    S.s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        kf, qf[rb][m], m == 0 ? f32x16{} : S.s[rb][kb], 0, 0, 0);
             }
-        if (a.lse && h == 0)
-            a.lse[(size_t)(b * a.Hq + hq) * a.Tq + iq] = (m_run + log2f(l_tot)) * kLn2;
+    };
+    auto mask_scores = [&](Scores<D>& S, int t) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int lim = row_lim[rb] - (t * BN + 4 * h);
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                if (key_of(e) > lim) S.s[rb][e >> 4][e & 15] = -INFINITY;
+        }
+    };
+    // p = 2^(s c - m) for the score pair (e, e + 1) of row block rb, rounded
+    // to bf16 into the B operand of P.V; the row sum adds the rounded weights
+    auto exp_pair = [&](const Scores<D>& S, int rb, int e, float nm, float& sa, float& sb) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(S.s[rb][e >> 4][e & 15], cs, nm));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(S.s[rb][e >> 4][(e + 1) & 15], cs, nm));
+        bf16x2 pk;
+        pk[0] = (bf16)p0;
+        pk[1] = (bf16)p1;
+        pb[rb][e >> 3][e & 7] = pk[0];
+        pb[rb][e >> 3][(e & 7) + 1] = pk[1];
+        if (e & 2) sb = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, sb, false);
+        else sa = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, sa, false);
+    };
+    // After the weights of a tile were formed against the running max: when
+    // some weight would exceed 2^12, the rows concerned (both half-wave
+    // lanes of a row) take the tile's max, rescale, and recompute (the other
+    // rows get the very same weights); then add the tile to the row sums.
+    auto fix_weights = [&](const Scores<D>& S, float (&sa)[RB], float (&sb)[RB]) {
+        bool big[RB], any = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            big[rb] = !(sa[rb] + sb[rb] <= 4096.f);
+            any = any || big[rb];
+        }
+        if (__any(any)) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)big[rb], (unsigned)big[rb], false, false);
+                const bool row_big = (sw[0] | sw[1]) != 0u;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < NE; ++e) mx = fmaxf(mx, S.s[rb][e >> 4][e & 15]);
+                const float tmax = pair_max(mx) * cs;
+                const float m_new = row_big ? fmaxf(m_run[rb], tmax) : m_run[rb];
+                const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+                l_run[rb] *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < NDB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[rb][cb][r] *= alpha;
+                m_run[rb] = m_new;
+                sa[rb] = 0.f;
+                sb[rb] = 0.f;
+#pragma unroll
+                for (int e = 0; e < NE; e += 2) exp_pair(S, rb, e, -m_run[rb], sa[rb], sb[rb]);
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) l_run[rb] += sa[rb] + sb[rb];
+    };
+
+    // ---- prologue: copies of tiles 0 .. NRING-2; tile 0 lands before the barrier
+#pragma unroll
+    for (int t = 0; t < NRING - 1; ++t) {
+        copy_tile(kh, t, kslot(t), cp_kcol);
+        copy_tile(vh, t, vslot(t), cp_vcol);
+    }
+    wait_vm<(NRING - 2) * 2 * NINS>();
+    __syncthreads();
+
+    // One tile step: issue the copies of tile t + NRING - 1 (into the slots
+    // of tile t - 1, read in step t - 1), then scores, weights and P V of
+    // tile t.  At its end tile t + 1 has landed.  Overlap of the matrix and
+    // vector work comes from the other workgroups on the CU.
+    Scores<D> S;
+    bool first = true;
+    for (int t = 0; t < n; ++t) {
+        copy_tile(kh, t + NRING - 1, kslot(t + NRING - 1), cp_kcol);
+        copy_tile(vh, t + NRING - 1, vslot(t + NRING - 1), cp_vcol);
+        if (t <= last) {
+            scores(t, S);
+            if ((t + 1) * BN > wave_full) mask_scores(S, t);
+            if (first) {  // the running max starts at tile 0's max
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < NE; ++e) mx = fmaxf(mx, S.s[rb][e >> 4][e & 15]);
+                    m_run[rb] = pair_max(mx) * cs;
+                }
+                first = false;
+            }
+            float sa[RB], sb[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                sa[rb] = 0.f;
+                sb[rb] = 0.f;
+#pragma unroll
+                for (int e = 0; e < NE; e += 2) exp_pair(S, rb, e, -m_run[rb], sa[rb], sb[rb]);
+            }
+            fix_weights(S, sa, sb);
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int cb = 0; cb < NDB; ++cb) {
+                    const bf16x8 vf = vfrag(t, cb, kc);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        oacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[rb][kc], oacc[rb][cb],
+                                                                              0, 0, 0);
+                }
+        }
+        wait_vm<(NRING - 2) * 2 * NINS>();   // tile t + 1 has landed
+        __syncthreads();
+    }
+    wait_vm<0>();   // no copy into LDS outlives the workgroup
+
+    // ---- epilogue: O = O^T / l; lane holds columns 32cb + 8g4 + 4h .. +3 of row iq[rb]
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const float l_tot = pair_sum(l_run[rb]);
+        if (iq[rb] < a.Tq) {
+            const float inv = 1.f / l_tot;
+            bf16* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Tq + iq[rb]) * D;
+#pragma unroll
+            for (int cb = 0; cb < NDB; ++cb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    bf16x4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[rb][cb][4 * g4 + e] * inv);
+                    *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * g4 + 4 * h) = val;
+                }
+            if (a.lse && h == 0)
+                a.lse[(size_t)(b * a.Hq + hq) * a.Tq + iq[rb]] = (m_run[rb] + log2f(l_tot)) * kLn2;
+        }
     }
 }
 
-template <int D, bool DUAL>
+template <int D>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-    typedef Cfg<D, DUAL> C;
+    typedef Cfg<D> C;
     Args a;
     a.q = static_cast<const bf16*>(p.q);
     a.k = static_cast<const bf16*>(p.k);
@@ -569,26 +453,22 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     a.lse = p.lse;
     a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Tq = p.Tq; a.Tk = p.Tk;
     a.R = p.Hq / p.Hkv;
-    a.HP = (p.Hq + 1) / 2;
-    a.n_qt = (p.Tq + C::BMG - 1) / C::BMG;
+    a.G = p.B * p.Hkv;
+    a.n_qt = (p.Tq + C::BM - 1) / C::BM;
     a.c = fmaxf(fabsf(p.scale) * kLog2e, 1e-30f);
     a.neg = p.scale < 0.f ? 0x80008000u : 0u;
     a.causal = p.causal;
     a.q_offset = p.causal ? p.q_offset : 0;
-    const long long units = (long long)a.B * a.HP;
-    a.xcd = (units % 8 == 0) ? 1 : 0;
-    const long long nwg = (long long)a.n_qt * units;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, DUAL>), dim3((unsigned)nwg), dim3(512), 0, stream, a);
+    a.xcd = (a.G % 8 == 0) ? 1 : 0;
+    const long long nwg = (long long)a.n_qt * a.G * a.R;
+    hipLaunchKernelGGL((prefill_kernel<D>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill_bf16_d128(const FwdParams& p, hipStream_t stream) {
-    // the two query heads 2p, 2p + 1 of a workgroup share a K/V head iff the
-    // group size Hq / Hkv is even
-    const bool shared = (p.Hq / p.Hkv) % 2 == 0;
-    return shared ? launch_d<128, false>(p, stream) : launch_d<128, true>(p, stream);
+hipError_t launch_prefill_bf16(const FwdParams& p, hipStream_t stream) {
+    return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
 }
 
 }  // namespace rocattn

@@ -31,10 +31,9 @@ struct FwdParams {
     int q_offset;
 };
 
-// Prefill (any Tq) bf16 MFMA kernels: d == 128 (two-group ping-pong) and
-// d == 64 (four waves, two workgroups per CU).
-hipError_t launch_prefill_bf16_d128(const FwdParams& p, hipStream_t stream);
-hipError_t launch_prefill_bf16_d64(const FwdParams& p, hipStream_t stream);
+// Prefill (any Tq) bf16 MFMA kernel, d in {64, 128}: four-wave workgroups of
+// 128 query rows, several workgroups per CU.
+hipError_t launch_prefill_bf16(const FwdParams& p, hipStream_t stream);
 
 // Split-K decode (Tq == 1) bf16 kernels; d in {64, 128}, Hq / Hkv <= 16.
 bool decode_bf16_supported(int Hq, int Hkv, int d);
