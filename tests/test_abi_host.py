@@ -112,3 +112,7 @@ def test_binding_refuses_cpu_tensors():
         rocattn.attn_fwd(q, q, q)
     with pytest.raises(ValueError, match="GPU tensor"):
         rocattn.rope_apply(q)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rocattn.bind_attn_fwd_ws(q, q, q, q)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rocattn.bind_rope_apply(q)

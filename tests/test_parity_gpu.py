@@ -386,6 +386,37 @@ def test_bf16_deterministic():
                        run_attn(qd, kd, vd, 0.0884, q_offset=3999))
 
 
+@pytest.mark.parametrize("Tq", [1, 300])
+def test_bound_calls_repeat_the_plain_calls(Tq):
+    """A Bound call (arguments marshalled once) launches the very work the
+    plain call does, each time it is called."""
+    say(f"bound calls Tq={Tq}")
+    q, k, v = wl.random_qkv(2, 8, 2, Tq, 700, 128, dtype=torch.bfloat16, seed=73)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    qo = 700 - Tq
+    nb = ra.attn_workspace_bytes(2, 8, 2, Tq, 700, 128, torch.bfloat16)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    want = torch.empty_like(qd)
+    ra.attn_fwd_ws(qd, kd, vd, want, ws, None, 0.0884, True, qo)
+    o = torch.full_like(qd, float("nan"))
+    call = ra.bind_attn_fwd_ws(qd, kd, vd, o, ws, None, 0.0884, True, qo)
+    for _ in range(3):
+        o.fill_(float("nan"))
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(o, want)
+    # RoPE in place: two bound calls rotate twice, like two plain calls
+    k2 = kd.clone()
+    ra.rope_apply(k2, None, pos0=5)
+    ra.rope_apply(k2, None, pos0=5)
+    k3 = kd.clone()
+    rot = ra.bind_rope_apply(k3, None, pos0=5)
+    rot()
+    rot()
+    torch.cuda.synchronize()
+    assert torch.equal(k2, k3)
+
+
 def test_decode_with_caller_workspace_matches_internal():
     say("decode ws vs internal")
     q, k, v = wl.random_qkv(4, 16, 4, 1, 3000, 128, dtype=torch.bfloat16, seed=71)

@@ -12,6 +12,12 @@ or a call is made with CPU tensors, the call raises.
     attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype)
     rope_apply(q, k=None, pos0=0, base=10000.0)
     status_string(code)
+    bind_attn_fwd_ws(...), bind_rope_apply(...)   -> Bound
+
+A Bound is one of these calls with its arguments checked and marshalled
+once: calling it launches the same work again on the stream it was bound
+to, with only the C call left in Python (for launch loops whose kernels are
+shorter than the argument checks).
 """
 from __future__ import annotations
 
@@ -141,10 +147,23 @@ def attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype) -> int:
     return int(library().attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype))
 
 
-def attn_fwd_ws(q, k, v, o, workspace=None, lse=None, scale=None, causal=True, q_offset=0,
-                stream=None):
-    """attn_fwd with a caller-owned workspace (a uint8 GPU tensor, or None when
-    attn_workspace_bytes() is 0) and an optional float32 lse [B, Hq, Tq]."""
+class Bound:
+    """A C-ABI entry point with its arguments marshalled once.  The tensors
+    whose pointers it holds are kept alive by it; calling it repeats the
+    launch on the stream it was bound to and raises on a non-zero status."""
+
+    __slots__ = ("name", "fn", "args", "keep")
+
+    def __init__(self, name, fn, args, keep):
+        self.name, self.fn, self.args, self.keep = name, fn, args, keep
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != OK:
+            raise RocattnError(self.name, st)
+
+
+def _attn_fwd_ws_call(q, k, v, o, workspace, lse, scale, causal, q_offset, stream):
     import torch
     B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt = _fwd_args(q, k, v, o, scale, causal, q_offset)
     ws_bytes = 0
@@ -155,15 +174,28 @@ def attn_fwd_ws(q, k, v, o, workspace=None, lse=None, scale=None, causal=True, q
         _check_dev("lse", lse, torch.float32)
         if tuple(lse.shape) != (B, Hq, Tq):
             raise ValueError("lse must be [B, Hq, Tq]")
-    st = library().attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, d, sc, ca,
-                               qo, dt, _stream(q, stream), _ptr(workspace), ws_bytes, _ptr(lse))
-    if st != OK:
-        raise RocattnError("attn_fwd_ws", st)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt,
+            _stream(q, stream), _ptr(workspace), ws_bytes, _ptr(lse))
+    return Bound("attn_fwd_ws", library().attn_fwd_ws, args, (q, k, v, o, workspace, lse))
+
+
+def attn_fwd_ws(q, k, v, o, workspace=None, lse=None, scale=None, causal=True, q_offset=0,
+                stream=None):
+    """attn_fwd with a caller-owned workspace (a uint8 GPU tensor, or None when
+    attn_workspace_bytes() is 0) and an optional float32 lse [B, Hq, Tq]."""
+    _attn_fwd_ws_call(q, k, v, o, workspace, lse, scale, causal, q_offset, stream)()
     return o
 
 
-def rope_apply(q, k=None, pos0=0, base=10000.0, stream=None):
-    """Rotate q (and k) in place by position pos0 + t (split-half pairing)."""
+def bind_attn_fwd_ws(q, k, v, o, workspace=None, lse=None, scale=None, causal=True, q_offset=0,
+                     stream=None) -> Bound:
+    """attn_fwd_ws's checks and marshalling now; the launch each time the
+    returned Bound is called (on the current stream as of this call when
+    stream is None)."""
+    return _attn_fwd_ws_call(q, k, v, o, workspace, lse, scale, causal, q_offset, stream)
+
+
+def _rope_call(q, k, pos0, base, stream):
     _check_dev("q", q)
     if q.dim() != 4:
         raise ValueError("q must be [B, Hq, T, d]")
@@ -174,8 +206,18 @@ def rope_apply(q, k=None, pos0=0, base=10000.0, stream=None):
         if k.dim() != 4 or k.shape[0] != B or k.shape[2] != T or k.shape[3] != d:
             raise ValueError("k must be [B, Hkv, T, d] with q's B, T and d")
         Hkv = k.shape[1]
-    st = library().rope_apply(_ptr(q), _ptr(k), B, Hq, Hkv, T, d, int(pos0), float(base),
-                              _dtype_code(q), _stream(q, stream))
-    if st != OK:
-        raise RocattnError("rope_apply", st)
+    args = (_ptr(q), _ptr(k), B, Hq, Hkv, T, d, int(pos0), float(base), _dtype_code(q),
+            _stream(q, stream))
+    return Bound("rope_apply", library().rope_apply, args, (q, k))
+
+
+def rope_apply(q, k=None, pos0=0, base=10000.0, stream=None):
+    """Rotate q (and k) in place by position pos0 + t (split-half pairing)."""
+    _rope_call(q, k, pos0, base, stream)()
     return q, k
+
+
+def bind_rope_apply(q, k=None, pos0=0, base=10000.0, stream=None) -> Bound:
+    """rope_apply's checks and marshalling now; the launch (in place, so each
+    call rotates again) each time the returned Bound is called."""
+    return _rope_call(q, k, pos0, base, stream)

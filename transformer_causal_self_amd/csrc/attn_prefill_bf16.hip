@@ -177,9 +177,17 @@ void prefill_kernel(Args a) {
     // ---- which (query tile, batch, query head) this workgroup owns
     int qt, g, rep;
     {
-        const int w = blockIdx.x;
+        // Workgroup w runs on XCD w % 8, as the (w / 8)-th of that XCD, and
+        // an XCD hands its workgroups round-robin to its 32 CUs.  Sizes go
+        // longest-first; reversing every other run of 32 evens out the sum
+        // each CU receives.
+        const int nwg = a.n_qt * a.G * a.R;
+        const int x = blockIdx.x & 7;
+        const int per_x = (nwg - x + 7) >> 3;
+        int s = blockIdx.x >> 3;
+        if ((s >> 5) & 1) s = min(per_x, (s | 31) + 1) - 1 - (s & 31);
+        const int w = 8 * s + x;
         if (a.xcd) {
-            const int x = w & 7, s = w >> 3;
             const int per = (a.G >> 3) * a.R;
             const int rank = s / per, rem = s - rank * per;
             g = x * (a.G >> 3) + rem / a.R;
