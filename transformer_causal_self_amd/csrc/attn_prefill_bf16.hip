@@ -154,6 +154,11 @@ __device__ inline void wait_vm() {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
+
 template <int D>
 struct Scores {
     f32x16 s[Cfg<D>::RB][Cfg<D>::NKB];
@@ -252,6 +257,19 @@ void prefill_kernel(Args a) {
     const unsigned cp_lds = (unsigned)(wave * 64 * 16);
     auto kslot = [&](int t) { return kring + (unsigned)((t % NRING) * TB); };
     auto vslot = [&](int t) { return vring + (unsigned)((t % NRING) * TB); };
+    // Offsets of the copies of a tile that lies wholly inside the keys: the
+    // same for every such tile (only the scalar source base moves).
+    unsigned cpk[NINS], cpv[NINS];
+#pragma unroll
+    for (int i = 0; i < NINS; ++i) {
+        cpk[i] = (unsigned)(cp_r0 + i * RSTR) * (unsigned)(D * 2) + cp_kcol;
+        cpv[i] = (unsigned)(cp_r0 + i * RSTR) * (unsigned)(D * 2) + cp_vcol;
+    }
+    auto copy_full = [&](const bf16* head, int t, unsigned slot, const unsigned (&off)[NINS]) {
+#pragma unroll
+        for (int i = 0; i < NINS; ++i)
+            copy16(head + (size_t)t * BN * D, off[i], slot + (unsigned)(i * CPL * 16) + cp_lds);
+    };
     auto copy_tile = [&](const bf16* head, int t, unsigned slot, unsigned col) {
         const int j0 = min(t, n - 1) * BN;
 #pragma unroll
@@ -272,11 +290,20 @@ void prefill_kernel(Args a) {
     const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
     const unsigned voff =
         2u * (unsigned)((4 * (tg >> 1) + tr) * D + 16 * (tg & 1) + 4 * tq + 8 * swz_v<D>(tr));
-    auto kfrag = [&](int t, int kb, int m) {
-        return *(lds_bf16x8*)(uintptr_t)((kslot(t) + koff + (unsigned)(kb * 32 * D * 2)) ^ (32u * m));
+    // The ring bases are 1024-byte aligned and the slot, block and slice
+    // strides are multiples of 1024, so the XOR (bits 5-7) commutes with
+    // adding them: every fragment read is a per-lane base plus a constant
+    // offset once the slot is known at compile time (P = slot).
+    unsigned kaddr[NQ], vaddr[NDB];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) kaddr[m] = kring + (koff ^ (32u * m));
+#pragma unroll
+    for (int cb = 0; cb < NDB; ++cb) vaddr[cb] = vring + (voff ^ (64u * cb));
+    auto kfrag = [&](int P, int kb, int m) {
+        return *(lds_bf16x8*)(uintptr_t)(kaddr[m] + (unsigned)(P * TB + kb * 32 * D * 2));
     };
-    auto vfrag = [&](int t, int cb, int kc) {
-        const unsigned addr = (vslot(t) + voff + (unsigned)(16 * kc * D * 2)) ^ (64u * cb);
+    auto vfrag = [&](int P, int cb, int kc) {
+        const unsigned addr = vaddr[cb] + (unsigned)(P * TB + 16 * kc * D * 2);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 16u * D));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -299,13 +326,13 @@ void prefill_kernel(Args a) {
     // key offset (within the tile, before + 4h) of score element e
     auto key_of = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3); };
 
-    // S^T(tile t) = K(t) Q^T, plain order
-    auto scores = [&](int t, Scores<D>& S) {
+    // S^T(tile in slot P) = K Q^T, plain order
+    auto scores = [&](int P, Scores<D>& S) {
 #pragma unroll
         for (int m = 0; m < NQ; ++m)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8 kf = kfrag(t, kb, m);
+                const bf16x8 kf = kfrag(P, kb, m);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     S.s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -381,17 +408,26 @@ void prefill_kernel(Args a) {
     wait_vm<(NRING - 2) * 2 * NINS>();
     __syncthreads();
 
-    // One tile step: issue the copies of tile t + NRING - 1 (into the slots
-    // of tile t - 1, read in step t - 1), then scores, weights and P V of
-    // tile t.  At its end tile t + 1 has landed.  Overlap of the matrix and
-    // vector work comes from the other workgroups on the CU.
+    // One tile step: issue the copies of tile t + 1 (into the slots of tile
+    // t - 1, read in step t - 1), then scores, weights and P V of tile t.  At
+    // its end tile t + 1 has landed.  Overlap of the matrix and vector work
+    // comes from the other workgroups on the CU.  Steps come in pairs so that
+    // the ring slot of each (t % 2) is a compile-time constant.
+    static_assert(NRING == 2, "the step pairs assume a two-tile ring");
     Scores<D> S;
     bool first = true;
-    for (int t = 0; t < n; ++t) {
-        copy_tile(kh, t + NRING - 1, kslot(t + NRING - 1), cp_kcol);
-        copy_tile(vh, t + NRING - 1, vslot(t + NRING - 1), cp_vcol);
+    auto step = [&](int t, auto slot) {
+        constexpr int P = decltype(slot)::value;
+        const int tc = t + 1;
+        if (tc < n && (tc + 1) * BN <= a.Tk) {
+            copy_full(kh, tc, kring + (unsigned)((1 - P) * TB), cpk);
+            copy_full(vh, tc, vring + (unsigned)((1 - P) * TB), cpv);
+        } else {
+            copy_tile(kh, tc, kring + (unsigned)((1 - P) * TB), cp_kcol);
+            copy_tile(vh, tc, vring + (unsigned)((1 - P) * TB), cp_vcol);
+        }
         if (t <= last) {
-            scores(t, S);
+            scores(P, S);
             if ((t + 1) * BN > wave_full) mask_scores(S, t);
             if (first) {  // the running max starts at tile 0's max
 #pragma unroll
@@ -416,15 +452,19 @@ void prefill_kernel(Args a) {
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int cb = 0; cb < NDB; ++cb) {
-                    const bf16x8 vf = vfrag(t, cb, kc);
+                    const bf16x8 vf = vfrag(P, cb, kc);
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
                         oacc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[rb][kc], oacc[rb][cb],
                                                                               0, 0, 0);
                 }
         }
-        wait_vm<(NRING - 2) * 2 * NINS>();   // tile t + 1 has landed
+        wait_vm<0>();   // tile t + 1 has landed
         __syncthreads();
+    };
+    for (int t = 0; t < n; t += 2) {
+        step(t, IC<0>{});
+        if (t + 1 < n) step(t + 1, IC<1>{});
     }
     wait_vm<0>();   // no copy into LDS outlives the workgroup
 
