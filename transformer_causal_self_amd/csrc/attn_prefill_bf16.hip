@@ -257,18 +257,15 @@ void prefill_kernel(Args a) {
     const unsigned cp_lds = (unsigned)(wave * 64 * 16);
     auto kslot = [&](int t) { return kring + (unsigned)((t % NRING) * TB); };
     auto vslot = [&](int t) { return vring + (unsigned)((t % NRING) * TB); };
-    // Offsets of the copies of a tile that lies wholly inside the keys: the
-    // same for every such tile (only the scalar source base moves).
-    unsigned cpk[NINS], cpv[NINS];
-#pragma unroll
-    for (int i = 0; i < NINS; ++i) {
-        cpk[i] = (unsigned)(cp_r0 + i * RSTR) * (unsigned)(D * 2) + cp_kcol;
-        cpv[i] = (unsigned)(cp_r0 + i * RSTR) * (unsigned)(D * 2) + cp_vcol;
-    }
-    auto copy_full = [&](const bf16* head, int t, unsigned slot, const unsigned (&off)[NINS]) {
+    // Offset of the copies of a tile that lies wholly inside the keys: the
+    // same for every such tile and copy instruction (the swizzle repeats
+    // every RSTR rows; only the scalar source base moves).
+    const unsigned cpk = (unsigned)cp_r0 * (unsigned)(D * 2) + cp_kcol;
+    const unsigned cpv = (unsigned)cp_r0 * (unsigned)(D * 2) + cp_vcol;
+    auto copy_full = [&](const bf16* head, int t, unsigned slot, unsigned off) {
 #pragma unroll
         for (int i = 0; i < NINS; ++i)
-            copy16(head + (size_t)t * BN * D, off[i], slot + (unsigned)(i * CPL * 16) + cp_lds);
+            copy16(head + ((size_t)t * BN + (size_t)i * RSTR) * D, off, slot + (unsigned)(i * CPL * 16) + cp_lds);
     };
     auto copy_tile = [&](const bf16* head, int t, unsigned slot, unsigned col) {
         const int j0 = min(t, n - 1) * BN;
