@@ -132,6 +132,35 @@ int attn_fwd_ws(const void* q, const void* k, const void* v, void* o,
                 void* workspace, size_t ws_bytes, float* lse);
 
 /*
+ * attn_fwd_strided -- attn_fwd_ws on tensors laid out with arbitrary
+ * batch / head / token strides, e.g. [B][T][H][d] ("BTHD") inputs sliced
+ * from a fused projection and an output written straight in the
+ * [B][T][H*d] order the heads are merged in ("Transformer Math and
+ * Implementation Deep Dive" -- the transpose(1, 2).contiguous().view(B, T, C)
+ * merge; "The Transformer architecture" -- Scaled dot-product attention,
+ * y.transpose(1, 2)).
+ *
+ *   strides   host array of 12 element strides, in the order
+ *             q(b, h, t), k(b, h, t), v(b, h, t), o(b, h, t); read during the
+ *             call only.  The d_head elements of a row are contiguous.
+ *             Element (b, h, t, c) of q is q[b*sq_b + h*sq_h + t*sq_t + c].
+ *   other arguments as attn_fwd_ws; lse (if given) stays dense [B][Hq][Tq].
+ *
+ * Every stride is >= 0 and (stride * element size) % 16 == 0.  Inputs may
+ * overlap each other (q, k and v may be views of one buffer, a zero stride
+ * broadcasts); o's rows must not share elements (ordered by stride, each
+ * level of size > 1 must step over the whole extent of the levels inside
+ * it) and o's address range must not overlap the inputs' (ERR_SHAPE).
+ * bf16 key and value token strides are at most 2^24 elements (ERR_SHAPE).
+ * Results are bit-identical to attn_fwd_ws on the same values laid out
+ * densely.  Returns a rocattn_status.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
+                     const long long* strides, int B, int Hq, int Hkv, int Tq, int Tk,
+                     int d_head, float scale, int causal, int q_offset, int dtype,
+                     void* stream, void* workspace, size_t ws_bytes, float* lse);
+
+/*
  * rope_apply -- rotary position embedding, in place, on q and (optionally) k.
  *
  * Token t (0 <= t < T) sits at position pos0 + t (pos0 = cache.pos for a

@@ -116,3 +116,37 @@ def test_binding_refuses_cpu_tensors():
         rocattn.bind_attn_fwd_ws(q, q, q, q)
     with pytest.raises(ValueError, match="GPU tensor"):
         rocattn.bind_rope_apply(q)
+
+
+def strided(q=A, k=Bp, v=C, o=D, st=None, B=1, Hq=4, Hkv=2, Tq=16, Tk=16, d=64, dtype=BF16,
+            lse=None):
+    # dense [B][H][T][d] strides unless overridden (a dict of index -> value)
+    dense = [Hq * Tq * d, Tq * d, d, Hkv * Tk * d, Tk * d, d, Hkv * Tk * d, Tk * d, d,
+             Hq * Tq * d, Tq * d, d]
+    for i, x in (st or {}).items():
+        dense[i] = x
+    arr = (ctypes.c_longlong * 12)(*dense)
+    return rocattn.library().attn_fwd_strided(q, k, v, o, arr, B, Hq, Hkv, Tq, Tk, d, 0.125, 1, 0,
+                                              dtype, None, None, 0, lse)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(dtype=3), -3), (dict(d=96), -4), (dict(B=0), -2),
+    (dict(q=A + 2), -7),
+    (dict(st={2: 68}), -7),               # q token stride: 136 bytes, not a multiple of 16
+    (dict(st={5: -64}), -2),              # negative key stride
+    (dict(st={11: 0}), -2),               # output rows on top of each other
+    (dict(st={11: 32}), -2),              # output rows overlap (stride < d)
+    (dict(st={10: 512}), -2),             # o's heads 512 apart, 16 rows of 64 each: they overlap
+    (dict(o=A + 4096), -2),               # o inside q's span
+    (dict(st={5: (1 << 24) + 8}), -2),    # bf16 key token stride past 2^24
+    (dict(lse=0x7F000002), -7),
+])
+def test_attn_fwd_strided_rejects(kw, status):
+    assert strided(**kw) == status
+
+
+def test_attn_fwd_strided_null_strides():
+    lib = rocattn.library()
+    assert lib.attn_fwd_strided(A, Bp, C, D, None, 1, 4, 2, 16, 16, 64, 0.125, 1, 0, BF16,
+                                None, None, 0, None) == -1

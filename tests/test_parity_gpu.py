@@ -423,3 +423,95 @@ def test_decode_with_caller_workspace_matches_internal():
     a = run_attn(q, k, v, 0.0884, q_offset=2999)
     b, _ = run_attn(q, k, v, 0.0884, q_offset=2999, lse=True)
     assert torch.equal(a, b)
+
+
+# ---- strided layouts (attn_fwd_strided): the kernels read and write rows at
+#      any batch / head / token strides; the values must equal the dense call
+#      bit for bit, and the oracle within the tolerance.
+
+def _dense_and_strided(q, k, v, scale, causal, q_offset, make_views, lse=False):
+    """GPU result on dense tensors and on the strided views make_views builds
+    (it returns q, k, v views holding the same values, and an output view)."""
+    qd, kd, vd = gpu(q, k, v)
+    B, Hq, Tq, d = q.shape
+    nb = ra.attn_workspace_bytes(B, Hq, k.shape[1], Tq, k.shape[2], d, q.dtype)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=DEV) if nb else None
+    want = torch.empty_like(qd)
+    lw = torch.empty(B, Hq, Tq, dtype=torch.float32, device=DEV) if lse else None
+    ra.attn_fwd_ws(qd, kd, vd, want, ws, lw, scale, causal, q_offset)
+    qs, ks, vs, os_ = make_views(qd, kd, vd)
+    os_.fill_(float("nan"))
+    lg = torch.empty(B, Hq, Tq, dtype=torch.float32, device=DEV) if lse else None
+    ra.attn_fwd_ws(qs, ks, vs, os_, ws, lg, scale, causal, q_offset)
+    torch.cuda.synchronize()
+    return want.cpu(), os_.cpu(), (lw.cpu() if lse else None), (lg.cpu() if lse else None)
+
+
+def _bthd(x):
+    """The same values held as [B, T, H, d] memory, viewed as [B, H, T, d]."""
+    return x.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,Tq,Tk,d,causal,qo", [
+    (torch.bfloat16, 2, 8, 2, 300, 300, 64, True, 0),
+    (torch.bfloat16, 1, 8, 4, 257, 257, 128, True, 0),
+    (torch.bfloat16, 2, 8, 2, 100, 700, 128, True, 600),
+    (torch.bfloat16, 2, 6, 6, 90, 333, 64, False, 0),
+    (torch.bfloat16, 3, 16, 4, 1, 2000, 128, True, 1999),   # decode
+    (torch.float32, 2, 4, 2, 70, 70, 64, True, 0),
+])
+def test_bthd_layout_bit_exact(dtype, B, Hq, Hkv, Tq, Tk, d, causal, qo):
+    say("bthd", dtype, B, Hq, Hkv, Tq, Tk, d, causal, qo)
+    q, k, v = wl.random_qkv(B, Hq, Hkv, Tq, Tk, d, dtype=dtype, seed=81)
+
+    def views(qd, kd, vd):
+        o = torch.empty(B, Tq, Hq, d, dtype=dtype, device=DEV).transpose(1, 2)
+        return _bthd(qd), _bthd(kd), _bthd(vd), o
+
+    scale = d ** -0.5
+    want, got, lw, lg = _dense_and_strided(q, k, v, scale, causal, qo, views, lse=True)
+    assert torch.equal(got, want)
+    assert torch.equal(lg, lw)
+    err = float(np.max(np.abs(f64(got) - oracle.attn(q, k, v, scale, causal=causal,
+                                                      q_offset=qo))))
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("Tq,Tk,qo", [(512, 512, 0), (1, 1500, 1499), (64, 1000, 936)])
+def test_fused_qkv_views_bit_exact(Tq, Tk, qo):
+    """q, k and v sliced from one [B, T, Hq + 2 Hkv, d] buffer (a fused
+    projection), output written as [B, T, Hq * d]."""
+    B, Hq, Hkv, d = 2, 8, 2, 128
+    say("fused qkv", Tq, Tk, qo)
+    q, k, v = wl.random_qkv(B, Hq, Hkv, Tq, Tk, d, dtype=torch.bfloat16, seed=83)
+
+    def views(qd, kd, vd):
+        # keys and values live in a cache buffer [B, Tk, 2 Hkv, d]; the new
+        # queries in their own [B, Tq, Hq, d] projection output
+        kv = torch.empty(B, Tk, 2 * Hkv, d, dtype=torch.bfloat16, device=DEV)
+        kv[:, :, :Hkv] = kd.transpose(1, 2)
+        kv[:, :, Hkv:] = vd.transpose(1, 2)
+        qb = torch.empty(B, Tq, Hq + 8, d, dtype=torch.bfloat16, device=DEV)   # padded heads
+        qb[:, :, :Hq] = qd.transpose(1, 2)
+        o = torch.empty(B, Tq, Hq * d, dtype=torch.bfloat16, device=DEV)
+        o4 = o.view(B, Tq, Hq, d).transpose(1, 2)
+        return (qb[:, :, :Hq].transpose(1, 2), kv[:, :, :Hkv].transpose(1, 2),
+                kv[:, :, Hkv:].transpose(1, 2), o4)
+
+    want, got, _, _ = _dense_and_strided(q, k, v, 0.0884, True, qo, views)
+    assert torch.equal(got, want)
+
+
+def test_kv_broadcast_over_batch_bit_exact():
+    """A zero batch stride shares one K/V across the batch."""
+    say("kv broadcast")
+    B, Hq, Hkv, T, d = 3, 4, 2, 200, 64
+    q, k1, v1 = wl.random_qkv(B, Hq, Hkv, T, T, d, dtype=torch.bfloat16, seed=85)
+    k = k1[:1].expand(B, -1, -1, -1).contiguous()
+    v = v1[:1].expand(B, -1, -1, -1).contiguous()
+
+    def views(qd, kd, vd):
+        return qd, kd[:1].expand(B, -1, -1, -1), vd[:1].expand(B, -1, -1, -1), torch.empty_like(qd)
+
+    want, got, _, _ = _dense_and_strided(q, k, v, 0.125, True, 0, views)
+    assert torch.equal(got, want)

@@ -9,6 +9,8 @@ or a call is made with CPU tensors, the call raises.
 
     attn_fwd(q, k, v, o=None, scale=None, causal=True, q_offset=0)
     attn_fwd_ws(q, k, v, o, workspace, lse=None, scale=None, causal=True, q_offset=0)
+        (tensors that are views with contiguous rows, e.g. [B, T, H, d] memory
+        transposed to [B, H, T, d], go to attn_fwd_strided)
     attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype)
     rope_apply(q, k=None, pos0=0, base=10000.0)
     status_string(code)
@@ -29,8 +31,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "librocattn.so")
 
 # the C ABI, as declared in include/rocattn.h
-SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_workspace_bytes", "rope_apply",
-           "attn_status_string")
+SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_strided", "attn_workspace_bytes",
+           "rope_apply", "attn_status_string")
 
 F32, BF16 = 0, 1
 OK = 0
@@ -64,6 +66,9 @@ def library() -> ctypes.CDLL:
         lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
         lib.attn_fwd_ws.restype = i
         lib.attn_fwd_ws.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, vp, sz, vp]
+        lib.attn_fwd_strided.restype = i
+        lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, ctypes.POINTER(ctypes.c_longlong),
+                                         i, i, i, i, i, i, f, i, i, i, vp, vp, sz, vp]
         lib.attn_workspace_bytes.restype = sz
         lib.attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.rope_apply.restype = i
@@ -87,13 +92,17 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16 only")
 
 
-def _check_dev(name, t, dtype=None):
+def _check_dev(name, t, dtype=None, rows=False):
+    """rows=True accepts any strides with contiguous rows (last dimension)."""
     if t is None:
         raise ValueError(f"{name} is required")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (got device {t.device}); "
                          "there is no CPU implementation")
-    if not t.is_contiguous():
+    if rows:
+        if t.dim() == 0 or (t.stride(-1) != 1 and t.shape[-1] > 1):
+            raise ValueError(f"{name} must have contiguous rows (last stride 1)")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
@@ -112,9 +121,9 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def _fwd_args(q, k, v, o, scale, causal, q_offset):
+def _fwd_args(q, k, v, o, scale, causal, q_offset, rows=False):
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        _check_dev(n, t, q.dtype)
+        _check_dev(n, t, q.dtype, rows)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.shape != q.shape:
         raise ValueError("q, o: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]")
     B, Hq, Tq, d = q.shape
@@ -128,10 +137,17 @@ def _fwd_args(q, k, v, o, scale, causal, q_offset):
 
 
 def attn_fwd(q, k, v, o=None, scale=None, causal=True, q_offset=0, stream=None):
-    """softmax(scale q k^T + M) v on the GPU; returns o ([B, Hq, Tq, d])."""
+    """softmax(scale q k^T + M) v on the GPU; returns o ([B, Hq, Tq, d]).
+    Views with contiguous rows (e.g. [B, T, H, d] tensors transposed to
+    [B, H, T, d]) go through attn_fwd_strided."""
     import torch
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if not all(t.is_contiguous() for t in (q, k, v, o)):
+        nb = attn_workspace_bytes(q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2],
+                                  q.shape[3], q.dtype)
+        ws = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+        return attn_fwd_ws(q, k, v, o, ws, None, scale, causal, q_offset, stream)
     B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt = _fwd_args(q, k, v, o, scale, causal, q_offset)
     st = library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, d, sc, ca,
                             qo, dt, _stream(q, stream))
@@ -165,7 +181,9 @@ class Bound:
 
 def _attn_fwd_ws_call(q, k, v, o, workspace, lse, scale, causal, q_offset, stream):
     import torch
-    B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt = _fwd_args(q, k, v, o, scale, causal, q_offset)
+    dense = all(t is not None and t.is_contiguous() for t in (q, k, v, o))
+    B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt = _fwd_args(q, k, v, o, scale, causal, q_offset,
+                                                      rows=not dense)
     ws_bytes = 0
     if workspace is not None:
         _check_dev("workspace", workspace)
@@ -174,9 +192,15 @@ def _attn_fwd_ws_call(q, k, v, o, workspace, lse, scale, causal, q_offset, strea
         _check_dev("lse", lse, torch.float32)
         if tuple(lse.shape) != (B, Hq, Tq):
             raise ValueError("lse must be [B, Hq, Tq]")
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt,
+    if dense:
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt,
+                _stream(q, stream), _ptr(workspace), ws_bytes, _ptr(lse))
+        return Bound("attn_fwd_ws", library().attn_fwd_ws, args, (q, k, v, o, workspace, lse))
+    strides = (ctypes.c_longlong * 12)(*[st for t in (q, k, v, o) for st in t.stride()[:3]])
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), strides, B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt,
             _stream(q, stream), _ptr(workspace), ws_bytes, _ptr(lse))
-    return Bound("attn_fwd_ws", library().attn_fwd_ws, args, (q, k, v, o, workspace, lse))
+    return Bound("attn_fwd_strided", library().attn_fwd_strided, args,
+                 (q, k, v, o, workspace, lse, strides))
 
 
 def attn_fwd_ws(q, k, v, o, workspace=None, lse=None, scale=None, causal=True, q_offset=0,

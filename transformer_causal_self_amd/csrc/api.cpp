@@ -98,7 +98,91 @@ FwdParams make_params(const void* q, const void* k, const void* v, void* o, floa
     p.scale = scale;
     p.causal = causal ? 1 : 0;
     p.q_offset = causal ? q_offset : 0;
+    // dense [B][H][T][d]
+    p.qs = {(long long)Hq * Tq * d, (long long)Tq * d, d};
+    p.os = p.qs;
+    p.ks = {(long long)Hkv * Tk * d, (long long)Tk * d, d};
+    p.vs = p.ks;
     return p;
+}
+
+// Largest element offset + d of a [n0][n1][n2][d] tensor with strides s, or
+// -1 when a stride is negative or the extent passes 2^62.
+long long extent(int n0, int n1, int n2, int d, const rocattn::Strides& s) {
+    if (s.b < 0 || s.h < 0 || s.t < 0) return -1;
+    const long long lim = 1LL << 62;
+    long long e = d;
+    const long long n[3] = {n0, n1, n2}, st[3] = {s.b, s.h, s.t};
+    for (int i = 0; i < 3; ++i) {
+        if (st[i] != 0 && (n[i] - 1) > (lim - e) / st[i]) return -1;
+        e += (n[i] - 1) * st[i];
+    }
+    return e;
+}
+
+// Rows of o never share an element: ordered by stride, each level of size > 1
+// steps at least over the whole extent of the levels inside it.
+bool rows_disjoint(int n0, int n1, int n2, int d, const rocattn::Strides& s) {
+    long long sz[3] = {n0, n1, n2}, st[3] = {s.b, s.h, s.t};
+    for (int i = 0; i < 3; ++i)          // sort by stride, ascending
+        for (int j = i + 1; j < 3; ++j)
+            if (st[j] < st[i]) {
+                long long x = st[i]; st[i] = st[j]; st[j] = x;
+                x = sz[i]; sz[i] = sz[j]; sz[j] = x;
+            }
+    long long inner = d;                 // extent of the levels inside the current one
+    for (int i = 0; i < 3; ++i) {
+        if (sz[i] <= 1) continue;
+        if (st[i] < inner) return false;
+        inner = st[i] * (sz[i] - 1) + inner;
+    }
+    return true;
+}
+
+int check_strided(const void* q, const void* k, const void* v, const void* o, int B, int Hq,
+                  int Hkv, int Tq, int Tk, int d, float scale, int causal, int q_offset,
+                  int dtype, const float* lse, const rocattn::Strides (&st)[4]) {
+    if (dtype != ROCATTN_F32 && dtype != ROCATTN_BF16) return ROCATTN_ERR_DTYPE;
+    if (!q || !k || !v || !o) return ROCATTN_ERR_NULL;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || d <= 0) return ROCATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ROCATTN_ERR_SHAPE;
+    if (dtype == ROCATTN_BF16) {
+        if (d != 64 && d != 128) return ROCATTN_ERR_HEADDIM;
+    } else {
+        if (d > 256 || d % 4 != 0) return ROCATTN_ERR_HEADDIM;
+        if (Hq > 65535 || B > 65535) return ROCATTN_ERR_SHAPE;
+    }
+    if (causal && q_offset < 0) return ROCATTN_ERR_OFFSET;
+    if (causal && (long long)q_offset + Tq > INT_MAX) return ROCATTN_ERR_OFFSET;
+    if (!isfinite(scale)) return ROCATTN_ERR_SCALE;
+    const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ROCATTN_ERR_ALIGN;
+    for (const auto& x : st)
+        if ((x.b * (long long)elt) % 16 || (x.h * (long long)elt) % 16 || (x.t * (long long)elt) % 16)
+            return ROCATTN_ERR_ALIGN;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ROCATTN_ERR_ALIGN;
+    const long long eq = extent(B, Hq, Tq, d, st[0]), ek = extent(B, Hkv, Tk, d, st[1]);
+    const long long ev = extent(B, Hkv, Tk, d, st[2]), eo = extent(B, Hq, Tq, d, st[3]);
+    if (eq < 0 || ek < 0 || ev < 0 || eo < 0) return ROCATTN_ERR_SHAPE;
+    if (!rows_disjoint(B, Hq, Tq, d, st[3])) return ROCATTN_ERR_SHAPE;
+    // the bf16 kernels address a 64-row key/value tile with 32-bit byte
+    // offsets, and every kernel keeps token strides in 32 bits
+    if (dtype == ROCATTN_BF16 && (st[1].t > (1LL << 24) || st[2].t > (1LL << 24)))
+        return ROCATTN_ERR_SHAPE;
+    for (const auto& x : st)
+        if (x.t > INT_MAX) return ROCATTN_ERR_SHAPE;
+    if (count4(B, Hq, (Tq + 127) / 128, 1) > INT_MAX) return ROCATTN_ERR_SHAPE;
+    const size_t ob = (size_t)eo * elt;
+    if (overlaps(o, ob, q, (size_t)eq * elt) || overlaps(o, ob, k, (size_t)ek * elt) ||
+        overlaps(o, ob, v, (size_t)ev * elt))
+        return ROCATTN_ERR_SHAPE;
+    if (lse) {
+        const size_t lb = (size_t)B * Hq * Tq * sizeof(float);
+        if (overlaps(lse, lb, q, (size_t)eq * elt) || overlaps(lse, lb, k, (size_t)ek * elt) ||
+            overlaps(lse, lb, v, (size_t)ev * elt) || overlaps(lse, lb, o, ob))
+            return ROCATTN_ERR_SHAPE;
+    }
+    return ROCATTN_OK;
 }
 
 }  // namespace
@@ -152,6 +236,39 @@ ROCATTN_API int attn_fwd_ws(const void* q, const void* k, const void* v, void* o
     }
     const FwdParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d_head, scale, causal,
                                     q_offset);
+    return launch(p, dtype, static_cast<hipStream_t>(stream), workspace, ws_bytes);
+}
+
+ROCATTN_API int attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
+                                 const long long* strides, int B, int Hq, int Hkv, int Tq,
+                                 int Tk, int d_head, float scale, int causal, int q_offset,
+                                 int dtype, void* stream, void* workspace, size_t ws_bytes,
+                                 float* lse) {
+    if (!strides) return ROCATTN_ERR_NULL;
+    const rocattn::Strides st[4] = {{strides[0], strides[1], strides[2]},
+                                    {strides[3], strides[4], strides[5]},
+                                    {strides[6], strides[7], strides[8]},
+                                    {strides[9], strides[10], strides[11]}};
+    int status = check_strided(q, k, v, o, B, Hq, Hkv, Tq, Tk, d_head, scale, causal, q_offset,
+                               dtype, lse, st);
+    if (status != ROCATTN_OK) return status;
+    const size_t wsb = workspace_for(B, Hq, Hkv, Tq, Tk, d_head, dtype);
+    if (wsb > 0) {
+        if (!workspace || ws_bytes < wsb) return ROCATTN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return ROCATTN_ERR_ALIGN;
+        const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
+        const size_t eq = (size_t)extent(B, Hq, Tq, d_head, st[0]) * elt;
+        const size_t ek = (size_t)extent(B, Hkv, Tk, d_head, st[1]) * elt;
+        const size_t ev = (size_t)extent(B, Hkv, Tk, d_head, st[2]) * elt;
+        const size_t eo = (size_t)extent(B, Hq, Tq, d_head, st[3]) * elt;
+        if (overlaps(workspace, wsb, q, eq) || overlaps(workspace, wsb, k, ek) ||
+            overlaps(workspace, wsb, v, ev) || overlaps(workspace, wsb, o, eo) ||
+            (lse && overlaps(workspace, wsb, lse, (size_t)B * Hq * Tq * sizeof(float))))
+            return ROCATTN_ERR_SHAPE;
+    }
+    FwdParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d_head, scale, causal,
+                              q_offset);
+    p.qs = st[0]; p.ks = st[1]; p.vs = st[2]; p.os = st[3];
     return launch(p, dtype, static_cast<hipStream_t>(stream), workspace, ws_bytes);
 }
 

@@ -48,6 +48,7 @@ struct DecArgs {
     int S;           // chunks per (batch, K/V head)
     float c;         // |scale| * log2(e)
     unsigned neg;    // sign flip for q when scale < 0
+    Strides qs, ks, vs;   // element strides (batch, head, token)
 };
 
 struct CombArgs {
@@ -56,6 +57,8 @@ struct CombArgs {
     bf16* o;
     float* lse;
     int S;
+    int Hq;
+    Strides os;
 };
 
 template <int D, int RP>  // RP: query heads per K/V head, padded to 4, 8 or 16
@@ -71,7 +74,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     const int b = g / a.Hkv, hk = g - (g / a.Hkv) * a.Hkv;
     const int j_begin = s * a.C;
     const int nkeys = min(a.kv_len, j_begin + a.C) - j_begin;   // >= 1
-    const size_t kv_head = (size_t)g * a.Tk * D;
     const int hq0 = hk * a.R;
 
     // ---- query heads as the A operand: for MFMA m, lane (rho, quarter)
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     {
         const bool ok = rho < a.R;
         const uint4* src = reinterpret_cast<const uint4*>(
-            a.q + (size_t)(b * a.Hq + hq0 + (ok ? rho : 0)) * D + 8 * quarter);
+            a.q + b * a.qs.b + (hq0 + (ok ? rho : 0)) * a.qs.h + 8 * quarter);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             uint4 u = src[4 * m];
@@ -96,13 +98,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
 
     // ---- phase 1: scores of 16 keys per MFMA group
     const int ngroups = (nkeys + 15) >> 4;
-    const bf16* kbase = a.k + kv_head + 8 * quarter;
+    const bf16* kbase = a.k + b * a.ks.b + hk * a.ks.h + 8 * quarter;
 #pragma unroll 4
     for (int gi = wave; gi < ngroups; gi += 4) {
         const int kl = gi * 16 + rho;            // key (local) whose row this lane loads
         const bool kvalid = kl < nkeys;
         const uint4* kp = reinterpret_cast<const uint4*>(
-            kbase + (size_t)(j_begin + (kvalid ? kl : 0)) * D);
+            kbase + (j_begin + (kvalid ? kl : 0)) * a.ks.t);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
@@ -150,10 +152,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     for (int r = 0; r < RP; ++r)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
-    const bf16* vbase = a.v + kv_head + (size_t)j_begin * D + col;
+    const bf16* vbase = a.v + b * a.vs.b + hk * a.vs.h + j_begin * a.vs.t + col;
 #pragma unroll 8
     for (int j = wave * KPW + kk; j < nkeys; j += 4 * KPW) {
-        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vbase + (size_t)j * D);
+        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vbase + j * a.vs.t);
         float vf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vf[e] = (float)vv[e];
@@ -225,7 +227,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(CombArgs a) {
             acc = fmaf(w, ov[u], acc);
         }
     }
-    a.o[row * D + col] = (bf16)(acc / den);
+    const int b = (int)(row / a.Hq), hq = (int)(row - (size_t)b * a.Hq);
+    a.o[b * a.os.b + hq * a.os.h + col] = (bf16)(acc / den);
     if (a.lse && col == 0) a.lse[row] = (M + log2f(den)) * kLn2;
 }
 
@@ -276,6 +279,7 @@ hipError_t launch_dec_d(const FwdParams& p, float* o_part, float* ml, int C, int
     a.C = C; a.S = S;
     a.c = fabsf(p.scale) * kLog2e;
     a.neg = p.scale < 0.f ? 0x80008000u : 0u;
+    a.qs = p.qs; a.ks = p.ks; a.vs = p.vs;
     const int grid = p.B * p.Hkv * S;
     const int rp = pad_r(a.R);
     hipError_t e = rp == 4 ? launch_split<D, 4>(a, grid, stream)
@@ -288,6 +292,8 @@ hipError_t launch_dec_d(const FwdParams& p, float* o_part, float* ml, int C, int
     c.o = static_cast<bf16*>(p.o);
     c.lse = p.lse;
     c.S = S;
+    c.Hq = p.Hq;
+    c.os = p.os;
     hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(p.B * p.Hq), dim3(D), 0, stream, c);
     return hipGetLastError();
 }

@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
     const float* qg = static_cast<const float*>(p.q);
     const float* kg = static_cast<const float*>(p.k);
     const float* vg = static_cast<const float*>(p.v);
-    const size_t q_row = ((size_t)(b * p.Hq + hq) * p.Tq + (row_ok ? i : 0)) * d;
+    const long long q_row = b * p.qs.b + hq * p.qs.h + (long long)(row_ok ? i : 0) * p.qs.t;
+    const long long o_row = b * p.os.b + hq * p.os.h + (long long)(row_ok ? i : 0) * p.os.t;
 
     float qr[DQ], acc[DQ];
 #pragma unroll
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
     }
     float m = -INFINITY, l = 0.f;
 
-    const size_t kv_base = (size_t)(b * p.Hkv + hk) * p.Tk * d;
+    const long long k_base = b * p.ks.b + hk * p.ks.h, v_base = b * p.vs.b + hk * p.vs.h;
     const int row_pos = p.q_offset + i;                  // absolute position of this row
     const int kv_end = p.causal ? min(p.Tk, p.q_offset + qt * kRows + kRows) : p.Tk;
 
@@ -66,8 +67,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
             const int j = j0 + jj;
             float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
             if (j < p.Tk) {
-                kk = *reinterpret_cast<const float4*>(kg + kv_base + (size_t)j * d + cc);
-                vv = *reinterpret_cast<const float4*>(vg + kv_base + (size_t)j * d + cc);
+                kk = *reinterpret_cast<const float4*>(kg + k_base + j * p.ks.t + cc);
+                vv = *reinterpret_cast<const float4*>(vg + v_base + j * p.vs.t + cc);
             }
             *reinterpret_cast<float4*>(Ks + e) = kk;
             *reinterpret_cast<float4*>(Vs + e) = vv;
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
         const float inv = 1.f / l;
 #pragma unroll
         for (int c = 0; c < DQ; ++c)
-            if (c < dq) og[q_row + part * dq + c] = acc[c] * inv;
+            if (c < dq) og[o_row + part * dq + c] = acc[c] * inv;
         if (p.lse && part == 0)
             p.lse[(size_t)(b * p.Hq + hq) * p.Tq + i] = m + logf(l);
     }

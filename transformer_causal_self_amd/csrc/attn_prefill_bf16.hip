@@ -109,6 +109,9 @@ struct Args {
     int causal;
     int q_offset;
     int xcd;       // 1: group the heads of one K/V head on one XCD
+    // element strides between batches and heads, and (32-bit) between tokens
+    long long qsb, qsh, ksb, ksh, vsb, vsh, osb, osh;
+    int qst, kst, vst, ost;
 };
 
 __device__ inline float pair_max(float x) {
@@ -164,7 +167,9 @@ struct Scores {
     f32x16 s[Cfg<D>::RB][Cfg<D>::NKB];
 };
 
-template <int D>
+// DENSE: q, k, v and o are dense [B][H][T][D], so every token stride is the
+// compile-time D (the strided instantiation reads the strides from Args).
+template <int D, bool DENSE>
 __global__ __launch_bounds__(Cfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(Cfg<D>::WPE, Cfg<D>::WPE)))
 void prefill_kernel(Args a) {
     typedef Cfg<D> C;
@@ -220,7 +225,7 @@ void prefill_kernel(Args a) {
     for (int rb = 0; rb < RB; ++rb) {
         const int row = iq[rb] < a.Tq ? iq[rb] : a.Tq - 1;
         const uint4* src = reinterpret_cast<const uint4*>(
-            a.q + ((size_t)(b * a.Hq + hq) * a.Tq + row) * D + 8 * h);
+            a.q + b * a.qsb + hq * a.qsh + (long long)row * (DENSE ? D : a.qst) + 8 * h);
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
             uint4 u = src[2 * m];
@@ -248,8 +253,9 @@ void prefill_kernel(Args a) {
     //      would occupy, which holds no live data then.  Rows past the last
     //      key re-read the last key (finite values; those keys are masked).
     const unsigned kring = lds_addr(lds), vring = kring + NRING * TB;
-    const bf16* kh = a.k + (size_t)(b * a.Hkv + hk) * a.Tk * D;
-    const bf16* vh = a.v + (size_t)(b * a.Hkv + hk) * a.Tk * D;
+    const bf16* kh = a.k + b * a.ksb + hk * a.ksh;
+    const bf16* vh = a.v + b * a.vsb + hk * a.vsh;
+    const int kst = DENSE ? D : a.kst, vst = DENSE ? D : a.vst;   // elements between key rows
     const int cl = wave * 64 + lane;
     const int cp_r0 = cl / NCH, cp_p = cl % NCH;
     const unsigned cp_kcol = 16u * (unsigned)(cp_p ^ swz_k<D>(cp_r0));
@@ -260,19 +266,19 @@ void prefill_kernel(Args a) {
     // Offset of the copies of a tile that lies wholly inside the keys: the
     // same for every such tile and copy instruction (the swizzle repeats
     // every RSTR rows; only the scalar source base moves).
-    const unsigned cpk = (unsigned)cp_r0 * (unsigned)(D * 2) + cp_kcol;
-    const unsigned cpv = (unsigned)cp_r0 * (unsigned)(D * 2) + cp_vcol;
-    auto copy_full = [&](const bf16* head, int t, unsigned slot, unsigned off) {
+    const unsigned cpk = (unsigned)cp_r0 * (unsigned)(kst * 2) + cp_kcol;
+    const unsigned cpv = (unsigned)cp_r0 * (unsigned)(vst * 2) + cp_vcol;
+    auto copy_full = [&](const bf16* head, int rs, int t, unsigned slot, unsigned off) {
 #pragma unroll
         for (int i = 0; i < NINS; ++i)
-            copy16(head + ((size_t)t * BN + (size_t)i * RSTR) * D, off, slot + (unsigned)(i * CPL * 16) + cp_lds);
+            copy16(head + (long long)(t * BN + i * RSTR) * rs, off, slot + (unsigned)(i * CPL * 16) + cp_lds);
     };
-    auto copy_tile = [&](const bf16* head, int t, unsigned slot, unsigned col) {
+    auto copy_tile = [&](const bf16* head, int rs, int t, unsigned slot, unsigned col) {
         const int j0 = min(t, n - 1) * BN;
 #pragma unroll
         for (int i = 0; i < NINS; ++i) {
             const int row = min(cp_r0 + i * RSTR, a.Tk - 1 - j0);
-            copy16(head + (size_t)j0 * D, (unsigned)row * (unsigned)(D * 2) + col,
+            copy16(head + (long long)j0 * rs, (unsigned)row * (unsigned)(rs * 2) + col,
                    slot + (unsigned)(i * CPL * 16) + cp_lds);
         }
     };
@@ -399,8 +405,8 @@ void prefill_kernel(Args a) {
     // ---- prologue: copies of tiles 0 .. NRING-2; tile 0 lands before the barrier
 #pragma unroll
     for (int t = 0; t < NRING - 1; ++t) {
-        copy_tile(kh, t, kslot(t), cp_kcol);
-        copy_tile(vh, t, vslot(t), cp_vcol);
+        copy_tile(kh, kst, t, kslot(t), cp_kcol);
+        copy_tile(vh, vst, t, vslot(t), cp_vcol);
     }
     wait_vm<(NRING - 2) * 2 * NINS>();
     __syncthreads();
@@ -417,11 +423,11 @@ void prefill_kernel(Args a) {
         constexpr int P = decltype(slot)::value;
         const int tc = t + 1;
         if (tc < n && (tc + 1) * BN <= a.Tk) {
-            copy_full(kh, tc, kring + (unsigned)((1 - P) * TB), cpk);
-            copy_full(vh, tc, vring + (unsigned)((1 - P) * TB), cpv);
+            copy_full(kh, kst, tc, kring + (unsigned)((1 - P) * TB), cpk);
+            copy_full(vh, vst, tc, vring + (unsigned)((1 - P) * TB), cpv);
         } else {
-            copy_tile(kh, tc, kring + (unsigned)((1 - P) * TB), cp_kcol);
-            copy_tile(vh, tc, vring + (unsigned)((1 - P) * TB), cp_vcol);
+            copy_tile(kh, kst, tc, kring + (unsigned)((1 - P) * TB), cp_kcol);
+            copy_tile(vh, vst, tc, vring + (unsigned)((1 - P) * TB), cp_vcol);
         }
         if (t <= last) {
             scores(P, S);
@@ -471,7 +477,7 @@ void prefill_kernel(Args a) {
         const float l_tot = pair_sum(l_run[rb]);
         if (iq[rb] < a.Tq) {
             const float inv = 1.f / l_tot;
-            bf16* orow = a.o + ((size_t)(b * a.Hq + hq) * a.Tq + iq[rb]) * D;
+            bf16* orow = a.o + b * a.osb + hq * a.osh + (long long)iq[rb] * (DENSE ? D : a.ost);
 #pragma unroll
             for (int cb = 0; cb < NDB; ++cb)
 #pragma unroll
@@ -489,6 +495,7 @@ void prefill_kernel(Args a) {
 
 template <int D>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+    const bool dense = p.qs.t == D && p.ks.t == D && p.vs.t == D && p.os.t == D;
     typedef Cfg<D> C;
     Args a;
     a.q = static_cast<const bf16*>(p.q);
@@ -505,8 +512,15 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     a.causal = p.causal;
     a.q_offset = p.causal ? p.q_offset : 0;
     a.xcd = (a.G % 8 == 0) ? 1 : 0;
+    a.qsb = p.qs.b; a.qsh = p.qs.h; a.qst = (int)p.qs.t;
+    a.ksb = p.ks.b; a.ksh = p.ks.h; a.kst = (int)p.ks.t;
+    a.vsb = p.vs.b; a.vsh = p.vs.h; a.vst = (int)p.vs.t;
+    a.osb = p.os.b; a.osh = p.os.h; a.ost = (int)p.os.t;
     const long long nwg = (long long)a.n_qt * a.G * a.R;
-    hipLaunchKernelGGL((prefill_kernel<D>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
+    if (dense)
+        hipLaunchKernelGGL((prefill_kernel<D, true>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 

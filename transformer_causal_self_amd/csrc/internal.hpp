@@ -18,17 +18,24 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Element strides of a [B][H][T][d] tensor between batches, heads and
+// tokens; the d elements of a row are always contiguous.
+struct Strides {
+    long long b, h, t;
+};
+
 // Everything a forward launch needs, validated by the host API.
 struct FwdParams {
     const void* q;
     const void* k;
     const void* v;
     void* o;
-    float* lse;      // may be null
+    float* lse;      // may be null; always dense [B][Hq][Tq]
     int B, Hq, Hkv, Tq, Tk, d;
     float scale;
     int causal;
     int q_offset;
+    Strides qs, ks, vs, os;
 };
 
 // Prefill (any Tq) bf16 MFMA kernel, d in {64, 128}: four-wave workgroups of
