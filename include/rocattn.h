@@ -185,6 +185,27 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
 int rope_apply(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head,
                int pos0, double base, int dtype, void* stream);
 
+/* Channel pairing of rope_apply_ex. */
+typedef enum {
+    ROCATTN_ROPE_SPLIT_HALF = 0,   /* pair p = channels (p, p + d/2) */
+    ROCATTN_ROPE_ADJACENT = 1      /* pair p = channels (2p, 2p + 1) */
+} rocattn_rope_pairing;
+
+/*
+ * rope_apply_ex -- rope_apply with a choice of channel pairing: split-half
+ * ("The Transformer architecture" -- Now: RoPE, apply_rope, the convention
+ * rope_apply uses) or adjacent pairs (2p, 2p + 1) ("Transformer" (ai-notes)
+ * -- RoPE, where each consecutive pair of channels is one plane).  The two
+ * conventions differ by a fixed permutation of the channels, so a model must
+ * use the one its weights were trained with.  Pair p turns by the same angle
+ * theta_p in both:
+ *     adjacent:  x'[2p] = x[2p] cos - x[2p+1] sin,  x'[2p+1] = x[2p] sin + x[2p+1] cos.
+ * Other arguments, rounding and support as rope_apply; an unknown pairing
+ * returns ROCATTN_ERR_SHAPE.
+ */
+int rope_apply_ex(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head, int pos0,
+                  double base, int dtype, void* stream, int pairing);
+
 /* attn_status_string -- static English text for a status code. */
 const char* attn_status_string(int status);
 

@@ -150,3 +150,12 @@ def test_attn_fwd_strided_null_strides():
     lib = rocattn.library()
     assert lib.attn_fwd_strided(A, Bp, C, D, None, 1, 4, 2, 16, 16, 64, 0.125, 1, 0, BF16,
                                 None, None, 0, None) == -1
+
+
+def test_rope_apply_ex_rejects_unknown_pairing():
+    lib = rocattn.library()
+    for pairing in (2, -1):
+        assert lib.rope_apply_ex(A, Bp, 1, 4, 2, 8, 64, 0, 10000.0, BF16, None, pairing) == -2
+    with pytest.raises(ValueError, match="pairing"):
+        import torch
+        rocattn.rope_apply(torch.zeros(1, 1, 1, 4, device="meta"), pairing="interleaved")

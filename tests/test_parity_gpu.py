@@ -88,6 +88,37 @@ def test_rope_matches_oracle(dtype, d, pos0):
         assert np.all(diff <= rope_tol(want, dtype)), float(diff.max())
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [2, 6, 64, 128])
+@pytest.mark.parametrize("pos0", [0, 16300])
+def test_rope_adjacent_matches_oracle(dtype, d, pos0):
+    say("rope adjacent", dtype, d, pos0)
+    q, k, _ = wl.random_qkv(2, 4, 2, 37, 37, d, dtype=dtype, seed=20 + d + pos0)
+    qd, kd = gpu(q, k)
+    ra.rope_apply(qd, kd, pos0=pos0, base=10000.0, pairing="adjacent")
+    torch.cuda.synchronize()
+    for got, x in ((qd, q), (kd, k)):
+        want = oracle.rope(x, pos0=pos0, base=10000.0, pairing="adjacent")
+        diff = np.abs(f64(got) - want)
+        assert np.all(diff <= rope_tol(want, dtype)), float(diff.max())
+
+
+def test_rope_adjacent_is_split_half_on_interleaved_channels():
+    """Adjacent pairing on channels (x0, y0, x1, y1, ...) equals split-half
+    pairing on (x0, x1, ..., y0, y1, ...), bit for bit (same angles, same
+    float32 arithmetic per pair)."""
+    say("rope adjacent vs split permuted")
+    d = 128
+    q, _, _ = wl.random_qkv(2, 3, 1, 50, 50, d, dtype=torch.bfloat16, seed=23)
+    perm = torch.cat([torch.arange(0, d, 2), torch.arange(1, d, 2)])   # adjacent -> split order
+    qa = q.clone().cuda()
+    qs = q[..., perm].contiguous().cuda()
+    ra.rope_apply(qa, None, pos0=321, pairing="adjacent")
+    ra.rope_apply(qs, None, pos0=321, pairing="split")
+    torch.cuda.synchronize()
+    assert torch.equal(qa[..., perm].cpu(), qs.cpu())
+
+
 def test_rope_q_only_and_other_base():
     say("rope q only, base 5e5")
     q, k, _ = wl.random_qkv(1, 3, 1, 5, 5, 128, dtype=torch.bfloat16, seed=77)

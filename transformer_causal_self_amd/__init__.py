@@ -12,7 +12,7 @@ or a call is made with CPU tensors, the call raises.
         (tensors that are views with contiguous rows, e.g. [B, T, H, d] memory
         transposed to [B, H, T, d], go to attn_fwd_strided)
     attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype)
-    rope_apply(q, k=None, pos0=0, base=10000.0)
+    rope_apply(q, k=None, pos0=0, base=10000.0, pairing="split"|"adjacent")
     status_string(code)
     bind_attn_fwd_ws(...), bind_rope_apply(...)   -> Bound
 
@@ -32,7 +32,7 @@ LIBRARY = os.path.join(HERE, "librocattn.so")
 
 # the C ABI, as declared in include/rocattn.h
 SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_strided", "attn_workspace_bytes",
-           "rope_apply", "attn_status_string")
+           "rope_apply", "rope_apply_ex", "attn_status_string")
 
 F32, BF16 = 0, 1
 OK = 0
@@ -73,6 +73,8 @@ def library() -> ctypes.CDLL:
         lib.attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.rope_apply.restype = i
         lib.rope_apply.argtypes = [vp, vp, i, i, i, i, i, i, ctypes.c_double, i, vp]
+        lib.rope_apply_ex.restype = i
+        lib.rope_apply_ex.argtypes = [vp, vp, i, i, i, i, i, i, ctypes.c_double, i, vp, i]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [i]
         _lib = lib
@@ -219,7 +221,12 @@ def bind_attn_fwd_ws(q, k, v, o, workspace=None, lse=None, scale=None, causal=Tr
     return _attn_fwd_ws_call(q, k, v, o, workspace, lse, scale, causal, q_offset, stream)
 
 
-def _rope_call(q, k, pos0, base, stream):
+PAIRING = {"split": 0, "adjacent": 1}
+
+
+def _rope_call(q, k, pos0, base, stream, pairing="split"):
+    if pairing not in PAIRING:
+        raise ValueError(f"pairing must be one of {sorted(PAIRING)}")
     _check_dev("q", q)
     if q.dim() != 4:
         raise ValueError("q must be [B, Hq, T, d]")
@@ -231,17 +238,18 @@ def _rope_call(q, k, pos0, base, stream):
             raise ValueError("k must be [B, Hkv, T, d] with q's B, T and d")
         Hkv = k.shape[1]
     args = (_ptr(q), _ptr(k), B, Hq, Hkv, T, d, int(pos0), float(base), _dtype_code(q),
-            _stream(q, stream))
-    return Bound("rope_apply", library().rope_apply, args, (q, k))
+            _stream(q, stream), PAIRING[pairing])
+    return Bound("rope_apply_ex", library().rope_apply_ex, args, (q, k))
 
 
-def rope_apply(q, k=None, pos0=0, base=10000.0, stream=None):
-    """Rotate q (and k) in place by position pos0 + t (split-half pairing)."""
-    _rope_call(q, k, pos0, base, stream)()
+def rope_apply(q, k=None, pos0=0, base=10000.0, stream=None, pairing="split"):
+    """Rotate q (and k) in place by position pos0 + t; pairing "split"
+    (channels p, p + d/2) or "adjacent" (channels 2p, 2p + 1)."""
+    _rope_call(q, k, pos0, base, stream, pairing)()
     return q, k
 
 
-def bind_rope_apply(q, k=None, pos0=0, base=10000.0, stream=None) -> Bound:
+def bind_rope_apply(q, k=None, pos0=0, base=10000.0, stream=None, pairing="split") -> Bound:
     """rope_apply's checks and marshalling now; the launch (in place, so each
     call rotates again) each time the returned Bound is called."""
-    return _rope_call(q, k, pos0, base, stream)
+    return _rope_call(q, k, pos0, base, stream, pairing)

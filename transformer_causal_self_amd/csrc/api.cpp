@@ -272,8 +272,10 @@ ROCATTN_API int attn_fwd_strided(const void* q, const void* k, const void* v, vo
     return launch(p, dtype, static_cast<hipStream_t>(stream), workspace, ws_bytes);
 }
 
-ROCATTN_API int rope_apply(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head, int pos0,
-                           double base, int dtype, void* stream) {
+ROCATTN_API int rope_apply_ex(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head,
+                              int pos0, double base, int dtype, void* stream, int pairing) {
+    if (pairing != ROCATTN_ROPE_SPLIT_HALF && pairing != ROCATTN_ROPE_ADJACENT)
+        return ROCATTN_ERR_SHAPE;
     if (dtype != ROCATTN_F32 && dtype != ROCATTN_BF16) return ROCATTN_ERR_DTYPE;
     if (!q) return ROCATTN_ERR_NULL;
     if (B <= 0 || Hq <= 0 || T <= 0 || d_head <= 0) return ROCATTN_ERR_SHAPE;
@@ -288,12 +290,18 @@ ROCATTN_API int rope_apply(void* q, void* k, int B, int Hq, int Hkv, int T, int 
     const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
     if (k && overlaps(q, (size_t)nq * elt, k, (size_t)nk * elt)) return ROCATTN_ERR_SHAPE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (rocattn::launch_rope(q, (long long)B * Hq, T, d_head, pos0, base, dtype, s) != hipSuccess)
+    if (rocattn::launch_rope(q, (long long)B * Hq, T, d_head, pos0, base, dtype, pairing, s) != hipSuccess)
         return ROCATTN_ERR_HIP;
-    if (k && rocattn::launch_rope(k, (long long)B * Hkv, T, d_head, pos0, base, dtype, s) !=
+    if (k && rocattn::launch_rope(k, (long long)B * Hkv, T, d_head, pos0, base, dtype, pairing, s) !=
                  hipSuccess)
         return ROCATTN_ERR_HIP;
     return ROCATTN_OK;
+}
+
+ROCATTN_API int rope_apply(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head, int pos0,
+                           double base, int dtype, void* stream) {
+    return rope_apply_ex(q, k, B, Hq, Hkv, T, d_head, pos0, base, dtype, stream,
+                         ROCATTN_ROPE_SPLIT_HALF);
 }
 
 ROCATTN_API const char* attn_status_string(int status) {

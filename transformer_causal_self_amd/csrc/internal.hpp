@@ -51,9 +51,10 @@ hipError_t launch_decode_bf16(const FwdParams& p, void* workspace, size_t ws_byt
 // Generic float32 kernel; d <= 256, d % 4 == 0.
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 
-// RoPE in place; dtype 0 = f32, 1 = bf16.  x has nvec = rows of d elements,
-// grouped as [nrow_groups][T][d] with token t at position pos0 + t.
+// RoPE in place; dtype 0 = f32, 1 = bf16; pairing 0 = split-half, 1 =
+// adjacent.  x holds n_seq sequences of T rows of d elements ([n_seq][T][d])
+// with token t at position pos0 + t.
 hipError_t launch_rope(void* x, long long n_seq, int T, int d, int pos0, double base,
-                       int dtype, hipStream_t stream);
+                       int dtype, int pairing, hipStream_t stream);
 
 }  // namespace rocattn

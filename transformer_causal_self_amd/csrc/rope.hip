@@ -3,7 +3,8 @@
 // Token t of a sequence sits at position pos = pos0 + t ("The Transformer
 // architecture" -- Hands-on: RoPE is sliced from cache.pos).  Channel pair p
 // of a head vector is (p, p + d/2) (split-half pairing, "The Transformer
-// architecture" -- Now: RoPE, apply_rope) and turns by
+// architecture" -- Now: RoPE, apply_rope) or (2p, 2p + 1) (adjacent
+// pairing, "Transformer" (ai-notes) -- RoPE), and turns by
 // theta_p = pos * base^(-2p/d) ("Transformer" (ai-notes) -- RoPE) through
 // [[cos, -sin], [sin, cos]].
 //
@@ -45,7 +46,8 @@ __device__ inline void store_f32(T* dst, const float* f) {
 }
 
 // grid.x: (token, pair-group) slots; grid.y: chunks of the n_seq head rows.
-template <typename T, int kPairs>  // kPairs channel pairs per lane
+// ADJ: adjacent pairing (the lane's 2 kPairs channels are contiguous).
+template <typename T, int kPairs, bool ADJ>  // kPairs channel pairs per lane
 __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long long n_seq,
                                                         int rows_per_chunk, int T_len, int d,
                                                         int pos0, double neg_log2_base_over_half) {
@@ -71,27 +73,30 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long 
     const long long r0 = (long long)blockIdx.y * rows_per_chunk;
     const long long r1 = min(n_seq, r0 + rows_per_chunk);
     const size_t row_stride = (size_t)T_len * d;
-    T* base = x + (size_t)t * d + p0;
+    T* base = x + (size_t)t * d + (ADJ ? 2 * p0 : p0);
 #pragma unroll 4
     for (long long r = r0; r < r1; ++r) {
+        // split-half: the kPairs first halves, then the kPairs second halves;
+        // adjacent: 2 kPairs contiguous channels, pair u = (2u, 2u + 1)
         T* lo = base + (size_t)r * row_stride;
-        T* hi = lo + half;
-        float x1[kPairs], x2[kPairs], y1[kPairs], y2[kPairs];
-        load_f32<T, kPairs>(lo, x1);
-        load_f32<T, kPairs>(hi, x2);
+        T* hi = lo + (ADJ ? kPairs : half);
+        float e[2 * kPairs], y[2 * kPairs];
+        load_f32<T, kPairs>(lo, e);
+        load_f32<T, kPairs>(hi, e + kPairs);
 #pragma unroll
         for (int u = 0; u < kPairs; ++u) {
-            y1[u] = x1[u] * cs[u] - x2[u] * sn[u];
-            y2[u] = x1[u] * sn[u] + x2[u] * cs[u];
+            const int i1 = ADJ ? 2 * u : u, i2 = ADJ ? 2 * u + 1 : u + kPairs;
+            y[i1] = e[i1] * cs[u] - e[i2] * sn[u];
+            y[i2] = e[i1] * sn[u] + e[i2] * cs[u];
         }
-        store_f32<T, kPairs>(lo, y1);
-        store_f32<T, kPairs>(hi, y2);
+        store_f32<T, kPairs>(lo, y);
+        store_f32<T, kPairs>(hi, y + kPairs);
     }
 }
 
 template <typename T, int kPairs>
 hipError_t launch_rope_t(T* x, long long n_seq, int T_len, int d, int pos0, double base,
-                         hipStream_t stream) {
+                         int pairing, hipStream_t stream) {
     const int half = d / 2;
     const int groups = half / kPairs;
     const long long slots = (long long)T_len * groups;
@@ -104,23 +109,27 @@ hipError_t launch_rope_t(T* x, long long n_seq, int T_len, int d, int pos0, doub
     gy = (n_seq + rows_per_chunk - 1) / rows_per_chunk;
     const double neg = -log2(base) / (double)half;
     dim3 grid((unsigned)gx, (unsigned)gy);
-    hipLaunchKernelGGL((rope_kernel<T, kPairs>), grid, dim3(kThreads), 0, stream,
-                       x, n_seq, rows_per_chunk, T_len, d, pos0, neg);
+    if (pairing)
+        hipLaunchKernelGGL((rope_kernel<T, kPairs, true>), grid, dim3(kThreads), 0, stream,
+                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg);
+    else
+        hipLaunchKernelGGL((rope_kernel<T, kPairs, false>), grid, dim3(kThreads), 0, stream,
+                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_rope(void* x, long long n_seq, int T_len, int d, int pos0, double base,
-                       int dtype, hipStream_t stream) {
+                       int dtype, int pairing, hipStream_t stream) {
     // four pairs per lane (8-byte bf16 / 16-byte f32 accesses) when the half
     // head size allows it, else one pair per lane
     const bool wide = (d / 2) % 4 == 0;
     if (dtype == 0)
-        return wide ? launch_rope_t<float, 4>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, stream)
-                    : launch_rope_t<float, 1>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, stream);
-    return wide ? launch_rope_t<bf16, 4>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, stream)
-                : launch_rope_t<bf16, 1>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, stream);
+        return wide ? launch_rope_t<float, 4>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, pairing, stream)
+                    : launch_rope_t<float, 1>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, pairing, stream);
+    return wide ? launch_rope_t<bf16, 4>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, pairing, stream)
+                : launch_rope_t<bf16, 1>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, pairing, stream);
 }
 
 }  // namespace rocattn
