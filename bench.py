@@ -268,6 +268,61 @@ def measure(w, args, torch, ra, wl, dev, steps=None, warmup=None):
     return out
 
 
+CACHED_STEPS = [
+    # name, B, Hq, Hkv, Tn, Tmax, pos, d
+    ("decode_step_bf16_B32_Hq32_Hkv8_pos8191_Tmax8192_d128", 32, 32, 8, 1, 8192, 8191, 128),
+    ("chunked_prefill_bf16_B1_Hq32_Hkv8_Tn512_pos3584_Tmax4096_d128", 1, 32, 8, 512, 4096, 3584, 128),
+]
+
+
+def measure_cached_steps(torch, ra, wl, dev):
+    """attn_decode_step (RoPE on the new rows, cache append, attention in two
+    launches plus the split-K combine) against the same step as separate
+    calls (rope_apply on q and on the new keys, two cache copies, attention
+    over the cache prefix).  Inputs are seeded draws; each timed call rotates
+    q again in place, which leaves the amount of work unchanged."""
+    out = {}
+    for name, B, Hq, Hkv, Tn, Tmax, pos, d in CACHED_STEPS:
+        q, kn, vn = (x.to(dev) for x in wl.random_qkv(B, Hq, Hkv, Tn, Tn, d, seed=2001))
+        _, kc, vc = (x.to(dev) for x in wl.random_qkv(1, 1, Hkv * B, 1, Tmax, d, seed=2002))
+        kc = kc.view(B, Hkv, Tmax, d).contiguous()
+        vc = vc.view(B, Hkv, Tmax, d).contiguous()
+        o = torch.empty_like(q)
+        scale = 1.0 / (d ** 0.5)
+        nb = ra.attn_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d, torch.bfloat16)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        fused = ra.bind_attn_decode_step(q, kn, vn, kc, vc, pos, o, scale=scale, workspace=ws)
+        k2 = kn.clone()
+        rope_q = ra.bind_rope_apply(q, None, pos0=pos)
+        rope_k = ra.bind_rope_apply(k2, None, pos0=pos)
+        kview, vview = kc[:, :, :pos + Tn], vc[:, :, :pos + Tn]
+        attn = ra.bind_attn_fwd_ws(q, kview, vview, o, ws, None, scale=scale, causal=True,
+                                   q_offset=pos)
+
+        def unfused():
+            rope_q()
+            rope_k()
+            kc[:, :, pos:pos + Tn].copy_(k2)
+            vc[:, :, pos:pos + Tn].copy_(vn)
+            attn()
+
+        timer = Timer(torch)
+        t_est = timer(fused, 3, 1) * 1e-3
+        warm, steps = max(5, int(0.03 / t_est)), max(10, int(0.05 / t_est))
+        ms_f = timer(fused, steps, warm)
+        ms_u = timer(unfused, steps, warm)
+        kv_bytes = 2.0 * 2 * d * B * Hkv * (pos + Tn)       # cache read once per K/V head
+        flops = 4.0 * B * Hq * d * n_visible(Tn, pos + Tn, True, pos)
+        out[name] = {"ms_per_step": round(ms_f, 4), "ms_per_step_separate_calls": round(ms_u, 4),
+                     "cache_gbs": round(kv_bytes / (ms_f * 1e-3) / 1e9, 1),
+                     "tflops": round(flops / (ms_f * 1e-3) / 1e12, 2)}
+        print(f"# {name}: fused step {ms_f * 1e3:.1f} us, separate calls {ms_u * 1e3:.1f} us",
+              file=sys.stderr)
+        del q, kn, vn, kc, vc, o, ws, k2, kview, vview
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, seconds):
     """The fp64 oracle on the host cores, on a bounded sample of workload w:
     whole passes over the workload when one pass fits the time budget, else
@@ -433,6 +488,7 @@ def main():
             print(f"# {wo.name}: attention {r['attn_ms'] * 1e3:.2f} us = "
                   f"{r['attn_tflops']:.1f} TFLOP/s, {r['attn_gbs']:.0f} GB/s", file=sys.stderr)
         line["also"] = also
+        line["cached_steps"] = measure_cached_steps(torch, ra, wl, dev)
 
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -206,6 +206,44 @@ typedef enum {
 int rope_apply_ex(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head, int pos0,
                   double base, int dtype, void* stream, int pairing);
 
+/*
+ * attn_decode_step -- one cached generation step, Tn new tokens per
+ * sequence ("The Transformer architecture" -- Hands-on: the new keys and
+ * values are written into the cache along the token axis at cache.pos, RoPE
+ * is sliced from cache.pos, and the new query rows sit at cache.pos + i;
+ * "Transformer" (ai-notes) -- Notes on compute: with a KV cache each new
+ * token costs one pass over the cached keys):
+ *
+ *   1. q (the new query rows) is rotated in place at positions pos + t;
+ *   2. k_new is rotated at positions pos + t and written into k_cache at
+ *      tokens pos .. pos + Tn - 1; v_new is copied into v_cache there;
+ *   3. o = attention of the rotated q over cache tokens 0 .. pos + Tn - 1,
+ *      causal, q_offset = pos (row i sees tokens <= pos + i).
+ * Steps 1-2 are one launch; step 3 is the attention of attn_fwd_ws (the
+ * split-K decode kernels for bf16 Tn == 1, else the prefill kernel).
+ *
+ *   q         [B][Hq][Tn][d_head], rotated in place (read, then written).
+ *   k_new, v_new  [B][Hkv][Tn][d_head], read only (k_new is not rotated in
+ *             place: its rotated rows go to the cache).
+ *   k_cache, v_cache  [B][Hkv][Tmax][d_head]; tokens pos .. pos + Tn - 1 are
+ *             overwritten, tokens < pos are read, tokens >= pos + Tn are
+ *             neither read nor written.
+ *   o         [B][Hq][Tn][d_head], fully overwritten.
+ *   pos       cache.pos: tokens already in the cache (0 <= pos, pos + Tn <= Tmax,
+ *             else ERR_OFFSET).
+ *   rope_base, pairing   as rope_apply_ex.
+ *   scale, dtype, stream, workspace, ws_bytes, lse   as attn_fwd_ws;
+ *             attn_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d_head, dtype) bytes
+ *             suffice for every pos.
+ * No written buffer (q, the caches, o, lse, workspace) may overlap another
+ * buffer (ERR_SHAPE).  Head sizes as attn_fwd; the rotation needs an even
+ * d_head.  Returns a rocattn_status.
+ */
+int attn_decode_step(void* q, const void* k_new, const void* v_new, void* k_cache,
+                     void* v_cache, void* o, int B, int Hq, int Hkv, int Tn, int Tmax, int pos,
+                     int d_head, float scale, double rope_base, int pairing, int dtype,
+                     void* stream, void* workspace, size_t ws_bytes, float* lse);
+
 /* attn_status_string -- static English text for a status code. */
 const char* attn_status_string(int status);
 

@@ -11,6 +11,8 @@ Functions (each cites its passage in ``attn_oracle.c``):
     attn(q, k, v, scale, causal=True, q_offset=0, return_lse=False)
     attn_rows(q, k, v, rows, scale, causal=True, q_offset=0)
     rope(x, pos0=0, base=10000.0, pairing="split")
+    decode_step(q, k_new, v_new, k_cache, v_cache, pos, scale, base=10000.0,
+                pairing="split")   (a composition of rope and attn)
 """
 from __future__ import annotations
 
@@ -125,6 +127,28 @@ class Oracle:
             raise ValueError(f"oracle_rope rejected its arguments (status {st})")
         return y
 
+    def decode_step(self, q, k_new, v_new, k_cache, v_cache, pos, scale, base=10000.0,
+                    pairing="split"):
+        """One cached generation step, as "The Transformer architecture" --
+        Hands-on states it: the Tn new query rows sit at positions pos + i and RoPE
+        is sliced from cache.pos, so q and the new keys are rotated at pos + t;
+        the new keys and values are written into the caches along the token axis
+        at pos ("Transformer Math and Implementation Deep Dive" -- Implementation
+        Bugs To Expect: the cache grows along the token axis); then causal
+        attention over cache tokens 0 .. pos + Tn - 1 with q_offset = pos.
+
+        Returns (o, q_rot, k_cache', v_cache') in float64 (the caches as copies
+        with the new rows written).  Only rope() and attn() do arithmetic."""
+        q_rot = self.rope(q, pos0=pos, base=base, pairing=pairing)
+        k_rot = self.rope(k_new, pos0=pos, base=base, pairing=pairing)
+        kc = _as_f64(k_cache).copy()
+        vc = _as_f64(v_cache).copy()
+        Tn = q_rot.shape[2]
+        kc[:, :, pos:pos + Tn] = k_rot
+        vc[:, :, pos:pos + Tn] = _as_f64(v_new)
+        o = self.attn(q_rot, kc[:, :, :pos + Tn], vc[:, :, :pos + Tn], scale, causal=True, q_offset=pos)
+        return o, q_rot, kc, vc
+
 
 _default: Oracle | None = None
 
@@ -154,6 +178,10 @@ def attn_rows(*args, **kwargs):
 
 def rope(*args, **kwargs):
     return default().rope(*args, **kwargs)
+
+
+def decode_step(*args, **kwargs):
+    return default().decode_step(*args, **kwargs)
 
 
 def threads_used() -> int:

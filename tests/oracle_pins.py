@@ -240,6 +240,32 @@ def pin_cached_rows_equal_prefill_rows(orc):
         assert np.array_equal(got[n], full[b, h, i])
 
 
+def pin_decode_steps_replay_the_prefill(orc):
+    """P2 Hands-on: with a cache, query positions start at cache.pos + i, keys
+    at 0, RoPE is sliced from cache.pos, and incremental decode matches the
+    one-shot forward (the page's kv-cache check).  Feeding a sequence to
+    decode_step one token at a time, then a chunk of several, from an empty
+    cache reproduces attention over the whole rotated sequence, and leaves
+    the rotated keys and the values in the caches in token order (P1
+    Implementation Bugs To Expect: the cache grows along the token axis)."""
+    r = _rng(14)
+    B, Hq, Hkv, T, d, Tmax = 2, 4, 2, 11, 8, 16
+    q = r.standard_normal((B, Hq, T, d)); k = r.standard_normal((B, Hkv, T, d))
+    v = r.standard_normal((B, Hkv, T, d))
+    qr, kr = orc.rope(q, 0, 500.0), orc.rope(k, 0, 500.0)
+    full = orc.attn(qr, kr, v, 0.4)
+    kc = np.full((B, Hkv, Tmax, d), np.nan); vc = np.full((B, Hkv, Tmax, d), np.nan)
+    steps = [(t, t + 1) for t in range(7)] + [(7, 11)]   # one token at a time, then a chunk
+    for c0, c1 in steps:
+        o, q_rot, kc, vc = orc.decode_step(q[:, :, c0:c1], k[:, :, c0:c1], v[:, :, c0:c1],
+                                           kc, vc, c0, 0.4, base=500.0)
+        assert np.max(np.abs(q_rot - qr[:, :, c0:c1])) < 1e-14
+        assert np.max(np.abs(o - full[:, :, c0:c1])) < 1e-13
+    assert np.max(np.abs(kc[:, :, :T] - kr)) < 1e-14
+    assert np.array_equal(vc[:, :, :T], v)
+    assert np.all(np.isnan(kc[:, :, T:])) and np.all(np.isnan(vc[:, :, T:]))
+
+
 # --------------------------------------------------------------------------
 # RoPE pins
 # --------------------------------------------------------------------------

@@ -159,3 +159,24 @@ def test_rope_apply_ex_rejects_unknown_pairing():
     with pytest.raises(ValueError, match="pairing"):
         import torch
         rocattn.rope_apply(torch.zeros(1, 1, 1, 4, device="meta"), pairing="interleaved")
+
+
+def step(q=A, kn=Bp, vn=C, kc=D, vc=0x70000000, o=0x78000000, B=1, Hq=4, Hkv=2, Tn=1,
+         Tmax=64, pos=10, d=64, pairing=0, dtype=BF16, ws=None, ws_bytes=0):
+    return rocattn.library().attn_decode_step(q, kn, vn, kc, vc, o, B, Hq, Hkv, Tn, Tmax, pos, d,
+                                              0.125, 10000.0, pairing, dtype, None, ws, ws_bytes,
+                                              None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(vc=None), -1), (dict(dtype=7), -3), (dict(d=96), -4),
+    (dict(Tn=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(pairing=3), -2),
+    (dict(pos=-1), -5), (dict(pos=60, Tn=5), -5),        # past the cache capacity
+    (dict(kc=A + 64), -2),                               # cache overlaps q
+    (dict(vc=D + 128), -2),                              # the two caches overlap
+    (dict(o=Bp), -2),                                    # o overlaps k_new
+    (dict(kn=Bp + 8), -7),
+    (dict(), -8),                                        # bf16, Tn == 1: workspace needed
+])
+def test_attn_decode_step_rejects(kw, status):
+    assert step(**kw) == status

@@ -546,3 +546,112 @@ def test_kv_broadcast_over_batch_bit_exact():
 
     want, got, _, _ = _dense_and_strided(q, k, v, 0.125, True, 0, views)
     assert torch.equal(got, want)
+
+
+# ---- the cached generation step (attn_decode_step): RoPE at cache.pos, cache
+#      append along the token axis, attention over the cache
+
+def _rand(shape, dtype, seed, sigma=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * sigma).to(dtype)
+
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,Tn,Tmax,pos,d,pairing", [
+    (torch.bfloat16, 4, 32, 8, 1, 4096, 3000, 128, "split"),     # decode, split-K kernels
+    (torch.bfloat16, 2, 12, 12, 1, 700, 0, 64, "adjacent"),       # first token of a sequence
+    (torch.bfloat16, 2, 8, 2, 100, 1000, 500, 64, "split"),       # chunked prefill on a cache
+    (torch.bfloat16, 1, 16, 4, 257, 600, 300, 128, "adjacent"),
+    (torch.float32, 2, 4, 2, 3, 64, 17, 64, "split"),
+])
+def test_decode_step_matches_oracle(dtype, B, Hq, Hkv, Tn, Tmax, pos, d, pairing):
+    say("decode step", dtype, B, Hq, Hkv, Tn, Tmax, pos, d, pairing)
+    q = _rand((B, Hq, Tn, d), dtype, 91)
+    kn = _rand((B, Hkv, Tn, d), dtype, 92)
+    vn = _rand((B, Hkv, Tn, d), dtype, 93)
+    kc = _rand((B, Hkv, Tmax, d), dtype, 94)
+    vc = _rand((B, Hkv, Tmax, d), dtype, 95)
+    scale = d ** -0.5
+    qd, knd, vnd, kcd, vcd = gpu(q, kn, vn, kc, vc)
+    o = ra.attn_decode_step(qd, knd, vnd, kcd, vcd, pos, scale=scale, base=10000.0,
+                            pairing=pairing)
+    torch.cuda.synchronize()
+    want_o, want_q, want_kc, want_vc = oracle.decode_step(q, kn, vn, kc, vc, pos, scale,
+                                                          base=10000.0, pairing=pairing)
+    # q rotated in place; the new cache rows rotated (k) or copied (v); the
+    # rest of the caches untouched
+    assert np.all(np.abs(f64(qd) - want_q) <= rope_tol(want_q, dtype))
+    got_kc, got_vc = kcd.cpu(), vcd.cpu()
+    new = slice(pos, pos + Tn)
+    assert np.all(np.abs(f64(got_kc[:, :, new]) - want_kc[:, :, new])
+                  <= rope_tol(want_kc[:, :, new], dtype))
+    assert torch.equal(got_vc[:, :, new], vn)
+    for got, old in ((got_kc, kc), (got_vc, vc)):
+        assert torch.equal(got[:, :, :pos], old[:, :, :pos])
+        assert torch.equal(got[:, :, pos + Tn:], old[:, :, pos + Tn:])
+    # the attention reads the GPU-rotated inputs: compare it to the oracle on them
+    want = oracle.attn(qd.cpu(), got_kc[:, :, :pos + Tn], got_vc[:, :, :pos + Tn], scale,
+                       causal=True, q_offset=pos)
+    err = float(np.max(np.abs(f64(o) - want)))
+    assert err <= TOL[dtype], err
+    # and the end-to-end step to the oracle's own composition
+    err2 = float(np.max(np.abs(f64(o) - want_o)))
+    assert err2 <= 2 * TOL[dtype], err2
+
+
+@pytest.mark.parametrize("Tn,pos", [(1, 2047), (64, 1000)])
+def test_decode_step_equals_unfused_calls_bit_exact(Tn, pos):
+    """One attn_decode_step gives the same bits as rope_apply on q and on the
+    new keys, copies into the caches, and attention over the cache prefix."""
+    say("decode step vs unfused", Tn, pos)
+    B, Hq, Hkv, Tmax, d = 2, 16, 4, 2048 + 64, 128
+    q = _rand((B, Hq, Tn, d), torch.bfloat16, 101).cuda()
+    kn = _rand((B, Hkv, Tn, d), torch.bfloat16, 102).cuda()
+    vn = _rand((B, Hkv, Tn, d), torch.bfloat16, 103).cuda()
+    kc = _rand((B, Hkv, Tmax, d), torch.bfloat16, 104).cuda()
+    vc = _rand((B, Hkv, Tmax, d), torch.bfloat16, 105).cuda()
+    q1, kc1, vc1 = q.clone(), kc.clone(), vc.clone()
+    o1 = ra.attn_decode_step(q1, kn, vn, kc1, vc1, pos, scale=0.0884)
+    q2, k2 = q.clone(), kn.clone()
+    ra.rope_apply(q2, None, pos0=pos)
+    ra.rope_apply(k2, None, pos0=pos)
+    kc2, vc2 = kc.clone(), vc.clone()
+    kc2[:, :, pos:pos + Tn] = k2
+    vc2[:, :, pos:pos + Tn] = vn
+    o2 = ra.attn_fwd(q2, kc2[:, :, :pos + Tn], vc2[:, :, :pos + Tn], scale=0.0884, q_offset=pos)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(kc1, kc2) and torch.equal(vc1, vc2)
+    assert torch.equal(o1, o2)
+
+
+def test_decode_steps_replay_the_prefill():
+    """The pages' KV-cache check ("The Transformer architecture" -- Hands-on):
+    a sequence fed one token at a time (then a chunk) through the cached step
+    gives the rows of the one-shot causal forward over the rotated sequence."""
+    say("decode replay")
+    B, Hq, Hkv, T, d, Tmax = 2, 8, 2, 300, 128, 512
+    q = _rand((B, Hq, T, d), torch.bfloat16, 111).cuda()
+    k = _rand((B, Hkv, T, d), torch.bfloat16, 112).cuda()
+    v = _rand((B, Hkv, T, d), torch.bfloat16, 113).cuda()
+    qf, kf = q.clone(), k.clone()
+    ra.rope_apply(qf, kf, pos0=0)
+    full = ra.attn_fwd(qf, kf, v, scale=0.0884)
+    kc = torch.zeros(B, Hkv, Tmax, d, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    nb = ra.attn_workspace_bytes(B, Hq, Hkv, 1, Tmax, d, torch.bfloat16)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    outs = []
+    for c0, c1 in [(t, t + 1) for t in range(200)] + [(200, 300)]:
+        qs = q[:, :, c0:c1].contiguous()
+        outs.append(ra.attn_decode_step(qs, k[:, :, c0:c1].contiguous(), v[:, :, c0:c1].contiguous(),
+                                        kc, vc, c0, scale=0.0884,
+                                        workspace=ws if c1 - c0 == 1 else None))
+    torch.cuda.synchronize()
+    got = torch.cat(outs, dim=2)
+    assert torch.equal(kc[:, :, :T], kf) and torch.equal(vc[:, :, :T], v)
+    # both GPU results against the oracle's one-shot forward on the rotated
+    # sequence (each is within the tolerance; they may differ by one bf16
+    # rounding step from each other)
+    want = oracle.attn(qf.cpu(), kf.cpu(), v.cpu(), 0.0884)
+    for res in (got, full):
+        err = float(np.max(np.abs(f64(res) - want)))
+        assert err <= TOL[torch.bfloat16], err

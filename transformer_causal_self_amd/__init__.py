@@ -14,7 +14,9 @@ or a call is made with CPU tensors, the call raises.
     attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype)
     rope_apply(q, k=None, pos0=0, base=10000.0, pairing="split"|"adjacent")
     status_string(code)
-    bind_attn_fwd_ws(...), bind_rope_apply(...)   -> Bound
+    attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o=None, scale=None,
+                     base=10000.0, pairing="split", workspace=None, lse=None)
+    bind_attn_fwd_ws(...), bind_rope_apply(...), bind_attn_decode_step(...) -> Bound
 
 A Bound is one of these calls with its arguments checked and marshalled
 once: calling it launches the same work again on the stream it was bound
@@ -32,7 +34,7 @@ LIBRARY = os.path.join(HERE, "librocattn.so")
 
 # the C ABI, as declared in include/rocattn.h
 SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_strided", "attn_workspace_bytes",
-           "rope_apply", "rope_apply_ex", "attn_status_string")
+           "rope_apply", "rope_apply_ex", "attn_decode_step", "attn_status_string")
 
 F32, BF16 = 0, 1
 OK = 0
@@ -75,6 +77,9 @@ def library() -> ctypes.CDLL:
         lib.rope_apply.argtypes = [vp, vp, i, i, i, i, i, i, ctypes.c_double, i, vp]
         lib.rope_apply_ex.restype = i
         lib.rope_apply_ex.argtypes = [vp, vp, i, i, i, i, i, i, ctypes.c_double, i, vp, i]
+        lib.attn_decode_step.restype = i
+        lib.attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
+                                         ctypes.c_double, i, i, vp, vp, sz, vp]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [i]
         _lib = lib
@@ -253,3 +258,65 @@ def bind_rope_apply(q, k=None, pos0=0, base=10000.0, stream=None, pairing="split
     """rope_apply's checks and marshalling now; the launch (in place, so each
     call rotates again) each time the returned Bound is called."""
     return _rope_call(q, k, pos0, base, stream, pairing)
+
+
+def _decode_step_call(q, k_new, v_new, k_cache, v_cache, pos, o, scale, base, pairing,
+                      workspace, lse, stream):
+    import torch
+    if pairing not in PAIRING:
+        raise ValueError(f"pairing must be one of {sorted(PAIRING)}")
+    for n, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                 ("v_cache", v_cache), ("o", o)):
+        _check_dev(n, t, q.dtype)
+    if q.dim() != 4 or k_new.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q, o: [B, Hq, Tn, d]; k_new, v_new: [B, Hkv, Tn, d]; "
+                         "k_cache, v_cache: [B, Hkv, Tmax, d]")
+    B, Hq, Tn, d = q.shape
+    Hkv, Tmax = k_cache.shape[1], k_cache.shape[2]
+    if (tuple(k_new.shape) != (B, Hkv, Tn, d) or tuple(v_new.shape) != (B, Hkv, Tn, d)
+            or tuple(k_cache.shape) != (B, Hkv, Tmax, d) or tuple(v_cache.shape) != (B, Hkv, Tmax, d)
+            or tuple(o.shape) != tuple(q.shape)):
+        raise ValueError("shape mismatch between q, k_new, v_new, the caches and o")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = 0
+    if workspace is not None:
+        _check_dev("workspace", workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, Hq, Tn):
+            raise ValueError("lse must be [B, Hq, Tn]")
+    args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(o), B, Hq,
+            Hkv, Tn, Tmax, int(pos), d, float(scale), float(base), PAIRING[pairing],
+            _dtype_code(q), _stream(q, stream), _ptr(workspace), ws_bytes, _ptr(lse))
+    return Bound("attn_decode_step", library().attn_decode_step, args,
+                 (q, k_new, v_new, k_cache, v_cache, o, workspace, lse))
+
+
+def attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o=None, scale=None, base=10000.0,
+                     pairing="split", workspace=None, lse=None, stream=None):
+    """One cached step: rotate q in place and k_new into k_cache at tokens
+    pos.., copy v_new into v_cache there, then attend over cache tokens
+    0 .. pos + Tn - 1 (causal, q_offset = pos); returns o.  A workspace of
+    attn_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d, dtype) bytes is needed when
+    that is non-zero (it is allocated here when not given)."""
+    import torch
+    if o is None:
+        o = torch.empty_like(q)
+    if workspace is None:
+        nb = attn_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
+                                  k_cache.shape[2], q.shape[3], q.dtype)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    _decode_step_call(q, k_new, v_new, k_cache, v_cache, pos, o, scale, base, pairing,
+                      workspace, lse, stream)()
+    return o
+
+
+def bind_attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o, scale=None,
+                          base=10000.0, pairing="split", workspace=None, lse=None,
+                          stream=None) -> Bound:
+    """attn_decode_step's checks and marshalling now; each call of the
+    returned Bound repeats the step (rotating q in place again)."""
+    return _decode_step_call(q, k_new, v_new, k_cache, v_cache, pos, o, scale, base, pairing,
+                             workspace, lse, stream)

@@ -304,6 +304,71 @@ ROCATTN_API int rope_apply(void* q, void* k, int B, int Hq, int Hkv, int T, int 
                          ROCATTN_ROPE_SPLIT_HALF);
 }
 
+ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, void* o, int B, int Hq, int Hkv, int Tn, int Tmax,
+                                 int pos, int d_head, float scale, double rope_base, int pairing,
+                                 int dtype, void* stream, void* workspace, size_t ws_bytes,
+                                 float* lse) {
+    if (dtype != ROCATTN_F32 && dtype != ROCATTN_BF16) return ROCATTN_ERR_DTYPE;
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !o) return ROCATTN_ERR_NULL;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tn <= 0 || Tmax <= 0 || d_head <= 0)
+        return ROCATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ROCATTN_ERR_SHAPE;
+    if (pairing != ROCATTN_ROPE_SPLIT_HALF && pairing != ROCATTN_ROPE_ADJACENT)
+        return ROCATTN_ERR_SHAPE;
+    if (dtype == ROCATTN_BF16) {
+        if (d_head != 64 && d_head != 128) return ROCATTN_ERR_HEADDIM;
+    } else {
+        if (d_head > 256 || d_head % 4 != 0) return ROCATTN_ERR_HEADDIM;
+        if (Hq > 65535 || B > 65535) return ROCATTN_ERR_SHAPE;
+    }
+    if (pos < 0 || (long long)pos + Tn > Tmax) return ROCATTN_ERR_OFFSET;
+    if (!isfinite(scale)) return ROCATTN_ERR_SCALE;
+    if (!isfinite(rope_base) || !(rope_base > 0.0)) return ROCATTN_ERR_SCALE;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(o))
+        return ROCATTN_ERR_ALIGN;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ROCATTN_ERR_ALIGN;
+    const long long nq = count4(B, Hq, Tn, d_head), nn = count4(B, Hkv, Tn, d_head);
+    const long long nc = count4(B, Hkv, Tmax, d_head);
+    if (nq < 0 || nn < 0 || nc < 0) return ROCATTN_ERR_SHAPE;
+    if (count4(B, Hq, (Tn + 127) / 128, 1) > INT_MAX) return ROCATTN_ERR_SHAPE;
+    const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
+    const size_t qb = (size_t)nq * elt, nb = (size_t)nn * elt, cb = (size_t)nc * elt;
+    // q and the caches are written; nothing written may overlap anything else
+    const void* bufs[6] = {q, k_new, v_new, k_cache, v_cache, o};
+    const size_t lens[6] = {qb, nb, nb, cb, cb, qb};
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j) {
+            const bool written = i == 0 || i >= 3 || j == 0 || j >= 3;
+            if (written && overlaps(bufs[i], lens[i], bufs[j], lens[j])) return ROCATTN_ERR_SHAPE;
+        }
+    if (lse) {
+        const size_t lb = (size_t)B * Hq * Tn * sizeof(float);
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(lse, lb, bufs[i], lens[i])) return ROCATTN_ERR_SHAPE;
+    }
+    const int Tk = pos + Tn;
+    const size_t wsb = workspace_for(B, Hq, Hkv, Tn, Tk, d_head, dtype);
+    if (wsb > 0) {
+        if (!workspace || ws_bytes < wsb) return ROCATTN_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return ROCATTN_ERR_ALIGN;
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(workspace, wsb, bufs[i], lens[i])) return ROCATTN_ERR_SHAPE;
+        if (lse && overlaps(workspace, wsb, lse, (size_t)B * Hq * Tn * sizeof(float)))
+            return ROCATTN_ERR_SHAPE;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (rocattn::launch_step_prep(q, k_new, v_new, k_cache, v_cache, B, Hq, Hkv, Tn, Tmax, d_head,
+                                  pos, rope_base, dtype, pairing, s) != hipSuccess)
+        return ROCATTN_ERR_HIP;
+    FwdParams p = make_params(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Tn, Tk, d_head, scale, 1,
+                              pos);
+    p.ks = {(long long)Hkv * Tmax * d_head, (long long)Tmax * d_head, d_head};
+    p.vs = p.ks;
+    return launch(p, dtype, s, workspace, ws_bytes);
+}
+
 ROCATTN_API const char* attn_status_string(int status) {
     switch (status) {
         case ROCATTN_OK: return "success";

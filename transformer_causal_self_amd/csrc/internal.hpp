@@ -57,4 +57,11 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_rope(void* x, long long n_seq, int T, int d, int pos0, double base,
                        int dtype, int pairing, hipStream_t stream);
 
+// Decode-step preparation in one launch: q [B][Hq][Tn][d] rotated in place,
+// the new keys kn [B][Hkv][Tn][d] rotated into kc [B][Hkv][Tmax][d] at
+// tokens pos .. pos + Tn - 1, the new values vn copied into vc there.
+hipError_t launch_step_prep(void* q, const void* kn, const void* vn, void* kc, void* vc, int B,
+                            int Hq, int Hkv, int Tn, int Tmax, int d, int pos, double base,
+                            int dtype, int pairing, hipStream_t stream);
+
 }  // namespace rocattn

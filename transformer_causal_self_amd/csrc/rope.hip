@@ -132,4 +132,130 @@ hipError_t launch_rope(void* x, long long n_seq, int T_len, int d, int pos0, dou
                 : launch_rope_t<bf16, 1>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, pairing, stream);
 }
 
+
+// ---------------------------------------------------------------------------
+// Decode-step preparation ("The Transformer architecture" -- Hands-on: the new
+// keys and values are written into the cache at cache.pos along the token
+// axis, and RoPE is sliced from cache.pos): in one launch, rotate the Tn new
+// query rows in place, rotate the new key rows into the key cache at
+// positions pos .. pos + Tn - 1, and copy the new value rows into the value
+// cache.  A thread owns kPairs channel pairs of one token; the block's
+// threads split into SPB pair slots x (256 / SPB) row lanes, so a one-token
+// step still fills every lane.  The virtual row list is [q rows | k rows |
+// v rows]; the cosine and sine of a slot are formed once (as in rope_kernel:
+// double precision, rounded once to float32) and reused for all its rows.
+namespace {
+
+struct PrepArgs {
+    void* q;             // [B][Hq][Tn][d], rotated in place
+    const void* kn;      // [B][Hkv][Tn][d]
+    const void* vn;      // [B][Hkv][Tn][d]
+    void* kc;            // [B][Hkv][Tmax][d]
+    void* vc;            // [B][Hkv][Tmax][d]
+    int Hq, Hkv, Tn, Tmax, d, pos;
+    long long nq, nk;    // q rows (B Hq), k rows (B Hkv); v rows = nk
+    int spb, rows_per_chunk;
+    double neg;          // -log2(base) / (d / 2)
+};
+
+template <typename T, int kPairs, bool ADJ>
+__global__ __launch_bounds__(kThreads) void step_prep_kernel(PrepArgs a) {
+    const int half = a.d >> 1;
+    const int groups = half / kPairs;
+    const int rpb = kThreads / a.spb;
+    const int lane_slot = threadIdx.x % a.spb, rl = threadIdx.x / a.spb;
+    const long long slot = (long long)blockIdx.x * a.spb + lane_slot;
+    if (slot >= (long long)a.Tn * groups) return;
+    const int t = (int)(slot / groups);
+    const int p0 = (int)(slot - (long long)t * groups) * kPairs;
+
+    float cs[kPairs], sn[kPairs];
+    const double pos = (double)a.pos + (double)t;
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) {
+        const double inv_freq = exp2((double)(p0 + u) * a.neg);
+        double s, c;
+        sincos(pos * inv_freq, &s, &c);
+        cs[u] = (float)c;
+        sn[u] = (float)s;
+    }
+    const int c0 = ADJ ? 2 * p0 : p0;             // first channel of the lane's slice
+    const int c1 = ADJ ? c0 + kPairs : p0 + half;  // second
+    const long long total = a.nq + 2 * a.nk;
+    const long long r0 = (long long)blockIdx.y * a.rows_per_chunk;
+    const long long r1 = min(total, r0 + a.rows_per_chunk);
+    for (long long r = r0 + rl; r < r1; r += rpb) {
+        const T* src;
+        T* dst;
+        bool rotate = true;
+        if (r < a.nq) {
+            dst = static_cast<T*>(a.q) + (r * a.Tn + t) * a.d;
+            src = dst;
+        } else {
+            const bool is_k = r < a.nq + a.nk;
+            const long long rk = r - a.nq - (is_k ? 0 : a.nk);   // b * Hkv + h
+            src = static_cast<const T*>(is_k ? a.kn : a.vn) + (rk * a.Tn + t) * a.d;
+            dst = static_cast<T*>(is_k ? a.kc : a.vc) + (rk * a.Tmax + a.pos + t) * a.d;
+            rotate = is_k;
+        }
+        float e[2 * kPairs], y[2 * kPairs];
+        load_f32<T, kPairs>(src + c0, e);
+        load_f32<T, kPairs>(src + c1, e + kPairs);
+        if (rotate) {
+#pragma unroll
+            for (int u = 0; u < kPairs; ++u) {
+                const int i1 = ADJ ? 2 * u : u, i2 = ADJ ? 2 * u + 1 : u + kPairs;
+                y[i1] = e[i1] * cs[u] - e[i2] * sn[u];
+                y[i2] = e[i1] * sn[u] + e[i2] * cs[u];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 2 * kPairs; ++u) y[u] = e[u];
+        }
+        store_f32<T, kPairs>(dst + c0, y);
+        store_f32<T, kPairs>(dst + c1, y + kPairs);
+    }
+}
+
+template <typename T, int kPairs>
+hipError_t launch_prep_t(PrepArgs a, int pairing, hipStream_t stream) {
+    const int groups = (a.d / 2) / kPairs;
+    const long long slots = (long long)a.Tn * groups;
+    a.spb = (int)(slots < kThreads ? slots : kThreads);
+    const long long gx = (slots + a.spb - 1) / a.spb;
+    const long long total = a.nq + 2 * a.nk;
+    const int rpb = kThreads / a.spb;
+    // enough blocks to fill the chip, each row lane with a few rows
+    long long gy = (2048 + gx - 1) / gx;
+    const long long max_gy = (total + rpb - 1) / rpb;
+    if (gy > max_gy) gy = max_gy;
+    if (gy < 1) gy = 1;
+    a.rows_per_chunk = (int)((total + gy - 1) / gy);
+    gy = (total + a.rows_per_chunk - 1) / a.rows_per_chunk;
+    dim3 grid((unsigned)gx, (unsigned)gy);
+    if (pairing)
+        hipLaunchKernelGGL((step_prep_kernel<T, kPairs, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((step_prep_kernel<T, kPairs, false>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_step_prep(void* q, const void* kn, const void* vn, void* kc, void* vc, int B,
+                            int Hq, int Hkv, int Tn, int Tmax, int d, int pos, double base,
+                            int dtype, int pairing, hipStream_t stream) {
+    PrepArgs a;
+    a.q = q; a.kn = kn; a.vn = vn; a.kc = kc; a.vc = vc;
+    a.Hq = Hq; a.Hkv = Hkv; a.Tn = Tn; a.Tmax = Tmax; a.d = d; a.pos = pos;
+    a.nq = (long long)B * Hq;
+    a.nk = (long long)B * Hkv;
+    a.neg = -log2(base) / (double)(d / 2);
+    a.spb = 1; a.rows_per_chunk = 1;
+    const bool wide = (d / 2) % 4 == 0;
+    if (dtype == 0)
+        return wide ? launch_prep_t<float, 4>(a, pairing, stream) : launch_prep_t<float, 1>(a, pairing, stream);
+    return wide ? launch_prep_t<bf16, 4>(a, pairing, stream) : launch_prep_t<bf16, 1>(a, pairing, stream);
+}
+
 }  // namespace rocattn
