@@ -11,6 +11,7 @@ Functions (each cites its passage in ``attn_oracle.c``):
     attn(q, k, v, scale, causal=True, q_offset=0, return_lse=False)
     attn_rows(q, k, v, rows, scale, causal=True, q_offset=0)
     rope(x, pos0=0, base=10000.0, pairing="split")
+    attn_bwd(q, k, v, dO, scale, causal=True, q_offset=0) -> (dq, dk, dv)
     decode_step(q, k_new, v_new, k_cache, v_cache, pos, scale, base=10000.0,
                 pairing="split")   (a composition of rope and attn)
 """
@@ -72,6 +73,9 @@ class Oracle:
         lib.oracle_attn_rows.argtypes = [_D, _D, _D, ctypes.POINTER(ctypes.c_long), _L,
                                          _D, _D, _L, _L, _L, _L, _L, _L,
                                          ctypes.c_double, ctypes.c_int, _L]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _L, _L, _L, _L, _L, _L,
+                                        ctypes.c_double, ctypes.c_int, _L]
         lib.oracle_rope.restype = ctypes.c_int
         lib.oracle_rope.argtypes = [_D, _L, _L, _L, _L, _L, ctypes.c_double, ctypes.c_int]
         self._lib = lib
@@ -116,6 +120,23 @@ class Oracle:
         if st != 0:
             raise ValueError(f"oracle_attn_rows rejected its arguments (status {st})")
         return (o, lse) if return_lse else o
+
+    def attn_bwd(self, q, k, v, dO, scale: float, causal: bool = True, q_offset: int = 0):
+        """(dq, dk, dv): gradients of sum(dO * attn(q, k, v)) (attn_oracle.c:
+        oracle_attn_bwd, the chain rule of the forward)."""
+        q, k, v, dO = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dO)
+        B, Hq, Tq, d = q.shape
+        _, Hkv, Tk, _ = k.shape
+        if k.shape != v.shape or dO.shape != q.shape or k.shape[0] != B or k.shape[3] != d:
+            raise ValueError("shape mismatch")
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        st = self._lib.oracle_attn_bwd(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(dO),
+                                       self._ptr(dq), self._ptr(dk), self._ptr(dv),
+                                       B, Hq, Hkv, Tq, Tk, d, float(scale), int(bool(causal)),
+                                       int(q_offset))
+        if st != 0:
+            raise ValueError(f"oracle_attn_bwd rejected its arguments (status {st})")
+        return dq, dk, dv
 
     def rope(self, x, pos0: int = 0, base: float = 10000.0, pairing: str = "split"):
         """Rotated copy of x[B,H,T,d] (token t at position pos0 + t)."""
@@ -178,6 +199,10 @@ def attn_rows(*args, **kwargs):
 
 def rope(*args, **kwargs):
     return default().rope(*args, **kwargs)
+
+
+def attn_bwd(*args, **kwargs):
+    return default().attn_bwd(*args, **kwargs)
 
 
 def decode_step(*args, **kwargs):

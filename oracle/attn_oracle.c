@@ -135,6 +135,94 @@ int oracle_attn(const double* q, const double* k, const double* v, double* o,
     return failed ? -10 : 0;
 }
 
+/* Gradients of the attention forward (oracle_attn) for an upstream
+ * gradient dO = dL/dO: dq = dL/dq, dk = dL/dk, dv = dL/dv, same layouts as
+ * q, k, v.  The pages train this operator ([P1] What To Implement: tiny
+ * training loop) through the softmax, a differentiable allocation ([P2]
+ * Softmax is a differentiable allocation); they print no gradient formulas,
+ * so these are the chain rule of the forward definition, row by row:
+ *     o_i = sum_j alpha_ij v_j                 ->  dv_j += alpha_ij dO_i,
+ *                                                   g_ij  = dO_i . v_j
+ *     alpha_i = softmax(s_i)                   ->  ds_ij = sum_k g_ik dalpha_ik/ds_ij
+ *         with dalpha_ik/ds_ij = alpha_ik (delta_jk - alpha_ij)
+ *                                              ->  ds_ij = alpha_ij (g_ij - sum_k alpha_ik g_ik)
+ *     s_ij = scale q_i . k_j (visible j only)  ->  dq_i += scale ds_ij k_j,
+ *                                                   dk_j += scale ds_ij q_i.
+ * A K/V head accumulates over every query head of its group and every row.
+ * Masked keys have alpha = 0 and receive nothing.  Work is split over
+ * (batch, K/V head) so each thread owns the dk / dv rows it adds into.
+ * Same status codes as oracle_attn. */
+int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dO,
+                    double* dq, double* dk, double* dv, long B, long Hq, long Hkv,
+                    long Tq, long Tk, long d, double scale, int causal, long q_offset) {
+    int st = check_shape(B, Hq, Hkv, Tq, Tk, d, scale, causal, q_offset);
+    if (st) return st;
+    const long R = Hq / Hkv;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* alpha = (double*)malloc(sizeof(double) * (size_t)Tk);
+        double* g = (double*)malloc(sizeof(double) * (size_t)Tk);
+        double* oi = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!alpha || !g || !oi) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long bk = 0; bk < B * Hkv; ++bk) {
+                const long b = bk / Hkv, hk = bk % Hkv;
+                const double* kh = k + bk * Tk * d;
+                const double* vh = v + bk * Tk * d;
+                double* dkh = dk + bk * Tk * d;
+                double* dvh = dv + bk * Tk * d;
+                for (long x = 0; x < Tk * d; ++x) { dkh[x] = 0.0; dvh[x] = 0.0; }
+                for (long hq = hk * R; hq < (hk + 1) * R; ++hq) {
+                    for (long i = 0; i < Tq; ++i) {
+                        const long r = (b * Hq + hq) * Tq + i;
+                        const double* qi = q + r * d;
+                        const double* gi = dO + r * d;
+                        double* dqi = dq + r * d;
+                        const long lim = last_visible_key(i, Tk, causal, q_offset);
+                        /* alpha_ij: the forward's softmax weights (attn_row
+                         * leaves exp(s_j - m) in its scratch and o_i / l in
+                         * oi; divide the weights by l = sum of them) */
+                        attn_row(qi, kh, vh, oi, NULL, alpha, Tk, d, scale, lim);
+                        double l = 0.0;
+                        for (long j = 0; j <= lim; ++j) l += alpha[j];
+                        for (long j = 0; j <= lim; ++j) alpha[j] /= l;
+                        /* dv_j += alpha_ij dO_i;  g_ij = dO_i . v_j */
+                        for (long j = 0; j <= lim; ++j) {
+                            const double* vj = vh + j * d;
+                            double dot = 0.0;
+                            for (long c = 0; c < d; ++c) {
+                                dvh[j * d + c] += alpha[j] * gi[c];
+                                dot += gi[c] * vj[c];
+                            }
+                            g[j] = dot;
+                        }
+                        /* ds_ij = alpha_ij (g_ij - sum_k alpha_ik g_ik) */
+                        double ag = 0.0;
+                        for (long j = 0; j <= lim; ++j) ag += alpha[j] * g[j];
+                        for (long c = 0; c < d; ++c) dqi[c] = 0.0;
+                        for (long j = 0; j <= lim; ++j) {
+                            const double ds = alpha[j] * (g[j] - ag);
+                            const double* kj = kh + j * d;
+                            for (long c = 0; c < d; ++c) {
+                                dqi[c] += scale * ds * kj[c];
+                                dkh[j * d + c] += scale * ds * qi[c];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(alpha);
+        free(g);
+        free(oi);
+    }
+    return failed ? -10 : 0;
+}
+
 /* The same rows as oracle_attn, but only the n rows listed in `rows`
  * (triples b, hq, i), written densely to o_rows[n][d] (and lse_rows[n] if
  * not NULL).  Used to check selected rows of workloads too large for the

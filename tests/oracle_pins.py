@@ -267,6 +267,75 @@ def pin_decode_steps_replay_the_prefill(orc):
 
 
 # --------------------------------------------------------------------------
+# gradient pins (the backward is the chain rule of the forward; nothing on
+# the pages prints it, so it is tied to differences of the forward itself,
+# to a library's automatic differentiation, and to two exact invariants)
+# --------------------------------------------------------------------------
+
+def _loss(orc, q, k, v, dO, scale, causal, q_offset):
+    return float(np.sum(dO * orc.attn(q, k, v, scale, causal=causal, q_offset=q_offset)))
+
+
+def pin_bwd_central_differences(orc):
+    """dL/dx for L = sum(dO * attn(q, k, v)) equals the central difference
+    (L(x + h) - L(x - h)) / 2h of the oracle's own forward, element by
+    element, for a causal GQA chunk with q_offset and a non-causal case."""
+    r = _rng(31)
+    for causal, qo, Tq, Tk in ((True, 2, 3, 5), (False, 0, 4, 3)):
+        B, Hq, Hkv, d = 1, 4, 2, 3
+        q = r.standard_normal((B, Hq, Tq, d)); k = r.standard_normal((B, Hkv, Tk, d))
+        v = r.standard_normal((B, Hkv, Tk, d)); dO = r.standard_normal((B, Hq, Tq, d))
+        grads = orc.attn_bwd(q, k, v, dO, 0.7, causal=causal, q_offset=qo)
+        h = 1e-5
+        for x, gx in zip((q, k, v), grads):
+            for idx in np.ndindex(x.shape):
+                x0 = x[idx]
+                x[idx] = x0 + h
+                lp = _loss(orc, q, k, v, dO, 0.7, causal, qo)
+                x[idx] = x0 - h
+                lm = _loss(orc, q, k, v, dO, 0.7, causal, qo)
+                x[idx] = x0
+                assert abs((lp - lm) / (2 * h) - gx[idx]) < 1e-7, (idx, (lp - lm) / (2 * h), gx[idx])
+
+
+def pin_bwd_torch_autograd(orc):
+    """Automatic differentiation (torch, float64) of the explicit formula
+    softmax(scale QK^T + M) V with K/V heads repeat_interleave'd."""
+    import torch
+    r = _rng(32)
+    B, Hq, Hkv, Tq, Tk, d, qo = 2, 6, 2, 7, 12, 5, 5
+    arrs = [r.standard_normal(s) for s in ((B, Hq, Tq, d), (B, Hkv, Tk, d), (B, Hkv, Tk, d),
+                                           (B, Hq, Tq, d))]
+    q, k, v, dO = (torch.tensor(a, requires_grad=i < 3) for i, a in enumerate(arrs))
+    rep = Hq // Hkv
+    s = 0.45 * q @ k.repeat_interleave(rep, 1).transpose(-1, -2)
+    i = torch.arange(Tq)[:, None]
+    j = torch.arange(Tk)[None, :]
+    s = s.masked_fill(j > qo + i, float("-inf"))
+    o = torch.softmax(s, -1) @ v.repeat_interleave(rep, 1)
+    (o * dO).sum().backward()
+    got = orc.attn_bwd(*arrs, 0.45, causal=True, q_offset=qo)
+    for g, t in zip(got, (q, k, v)):
+        assert np.max(np.abs(g - t.grad.numpy())) < 1e-12
+
+
+def pin_bwd_invariants(orc):
+    """Adding one vector to every key shifts each score row by a constant,
+    which the softmax ignores: the dk of a K/V head sum to zero.  Every
+    weight row sums to one: the dv of a K/V head sum to the dO rows of its
+    query heads."""
+    r = _rng(33)
+    B, Hq, Hkv, Tq, Tk, d = 2, 4, 2, 9, 9, 6
+    q = r.standard_normal((B, Hq, Tq, d)); k = r.standard_normal((B, Hkv, Tk, d))
+    v = r.standard_normal((B, Hkv, Tk, d)); dO = r.standard_normal((B, Hq, Tq, d))
+    dq, dk, dv = orc.attn_bwd(q, k, v, dO, 0.5)
+    assert np.max(np.abs(dk.sum(axis=2))) < 1e-12
+    want = dO.reshape(B, Hkv, Hq // Hkv, Tq, d).sum(axis=(2, 3))
+    assert np.max(np.abs(dv.sum(axis=2) - want)) < 1e-12
+    assert np.max(np.abs(dq)) > 1e-3 and np.max(np.abs(dk)) > 1e-3
+
+
+# --------------------------------------------------------------------------
 # RoPE pins
 # --------------------------------------------------------------------------
 

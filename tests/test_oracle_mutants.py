@@ -28,6 +28,12 @@ MUTANTS = {
     "value_row_index_wrong": [("oi[c] += srow[j] * vj[c];", "oi[c] += srow[j] * vh[c];")],
     "key_channels_reversed": [("dot += qi[c] * kj[c];", "dot += qi[c] * kj[d - 1 - c];")],
     "lse_without_max": [("*lse_i = m + log(l);", "*lse_i = log(l);")],
+    "bwd_dv_uses_unnormalised_weights": [("for (long j = 0; j <= lim; ++j) alpha[j] /= l;", "")],
+    "bwd_softmax_jacobian_term_dropped": [("const double ds = alpha[j] * (g[j] - ag);",
+                                           "const double ds = alpha[j] * g[j];")],
+    "bwd_dk_missing_scale": [("dkh[j * d + c] += scale * ds * qi[c];", "dkh[j * d + c] += ds * qi[c];")],
+    "bwd_dq_uses_query_not_key": [("dqi[c] += scale * ds * kj[c];", "dqi[c] += scale * ds * qi[c];")],
+    "bwd_dv_uses_values": [("dvh[j * d + c] += alpha[j] * gi[c];", "dvh[j * d + c] += alpha[j] * vj[c];")],
     "rope_sign_flipped": [("xr[a] = x1 * cs - x2 * sn;", "xr[a] = x1 * cs + x2 * sn;")],
     "rope_frequency_halved_exponent": [("pow(base, -2.0 * (double)p / (double)d)",
                                         "pow(base, -1.0 * (double)p / (double)d)")],
