@@ -244,6 +244,40 @@ int attn_decode_step(void* q, const void* k_new, const void* v_new, void* k_cach
                      int d_head, float scale, double rope_base, int pairing, int dtype,
                      void* stream, void* workspace, size_t ws_bytes, float* lse);
 
+/*
+ * attn_bwd -- gradients of attn_fwd: for an upstream gradient dO = dL/dO,
+ * dq = dL/dq, dk = dL/dk, dv = dL/dv.  The pages train this operator
+ * ("Transformer Math and Implementation Deep Dive" -- What To Implement:
+ * tiny training loop) through the softmax, a differentiable allocation
+ * ("The Transformer architecture" -- Softmax is a differentiable
+ * allocation); the gradients are the chain rule of equation (1):
+ *     P = exp(scale Q K^T + M - lse),  dV = P^T dO,  dP = dO V^T,
+ *     D_i = sum_c dO_ic O_ic,  dS = P (dP - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q,
+ * with a K/V head's dK and dV summed over the query heads of its group.
+ *
+ *   q, k, v, o   the forward's inputs and output (dense layouts as attn_fwd).
+ *   dO           [B][Hq][Tq][d_head], the upstream gradient.
+ *   lse          float32 [B][Hq][Tq], the forward's log-sum-exp rows (from
+ *                attn_fwd_ws with a non-NULL lse on the same inputs).
+ *   dq           [B][Hq][Tq][d_head], dk and dv [B][Hkv][Tk][d_head]; fully
+ *                overwritten (keys no query sees get 0).
+ *   workspace    attn_bwd_workspace_bytes(...) bytes of device memory.
+ *   other arguments as attn_fwd.
+ * Supported: bf16, d_head in {64, 128} (float32 returns ERR_DTYPE).
+ * Outputs and workspace must not overlap each other or the inputs
+ * (ERR_SHAPE).  Deterministic: a fixed summation order, no atomics.
+ * Returns a rocattn_status.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Tq,
+             int Tk, int d_head, float scale, int causal, int q_offset, int dtype, void* stream,
+             void* workspace, size_t ws_bytes);
+
+/* attn_bwd_workspace_bytes -- bytes of workspace attn_bwd needs (0 for a
+ * shape or dtype it rejects). */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d_head, int dtype);
+
 /* attn_status_string -- static English text for a status code. */
 const char* attn_status_string(int status);
 

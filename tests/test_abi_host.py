@@ -180,3 +180,35 @@ def step(q=A, kn=Bp, vn=C, kc=D, vc=0x70000000, o=0x78000000, B=1, Hq=4, Hkv=2, 
 ])
 def test_attn_decode_step_rejects(kw, status):
     assert step(**kw) == status
+
+
+def bwd(q=A, k=Bp, v=C, o=D, dO=0x70000000, lse=0x78000000, dq=0x7C000000, dk=0x7E000000,
+        dv=0x7F000000, B=1, Hq=4, Hkv=2, Tq=16, Tk=16, d=64, scale=0.125, causal=1, q_offset=0,
+        dtype=BF16, ws=0x7F800000, ws_bytes=1 << 20):
+    return rocattn.library().attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d,
+                                      scale, causal, q_offset, dtype, None, ws, ws_bytes)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), -1), (dict(lse=None), -1), (dict(dv=None), -1),
+    (dict(dtype=F32), -3), (dict(dtype=9), -3),          # the gradient kernels are bf16
+    (dict(Tq=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(d=96), -4), (dict(d=32), -4),
+    (dict(q_offset=-1), -5), (dict(scale=float("nan")), -6),
+    (dict(lse=0x78000004), -7), (dict(dk=0x7E000002), -7), (dict(ws=0x7F800008), -7),
+    (dict(ws=None), -8), (dict(ws_bytes=4 * 4 * 16 - 1), -8),
+    (dict(dq=A + 64), -2),                               # dq overlaps q
+    (dict(dk=0x7F000000 - 64), -2),                      # dk overlaps dv
+    (dict(dv=0x70000000 + 256), -2),                     # dv overlaps dO
+    (dict(ws=0x78000000), -2),                           # workspace overlaps lse
+])
+def test_attn_bwd_rejects(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_workspace_bytes():
+    lib = rocattn.library()
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 16, 16, 64, BF16) == 4 * 4 * 16
+    assert lib.attn_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 128, BF16) == 4 * 2 * 32 * 4096
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 16, 16, 64, F32) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 16, 16, 96, BF16) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 6, 4, 16, 16, 64, BF16) == 0

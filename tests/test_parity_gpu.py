@@ -655,3 +655,91 @@ def test_decode_steps_replay_the_prefill():
     for res in (got, full):
         err = float(np.max(np.abs(f64(res) - want)))
         assert err <= TOL[torch.bfloat16], err
+
+
+# ---- gradients (attn_bwd): the chain rule of the forward, against the
+#      oracle's fp64 gradients on the same bf16 inputs and the GPU forward's
+#      own o and lse (the oracle recomputes its forward in fp64)
+#
+# Tolerance: the kernels round P and dS to bf16 (relative 2^-9) before the
+# matrix products and the results to bf16, so the error of a gradient entry
+# scales with the size of its terms; the bound is the forward's 1.5e-2 taken
+# relative to the tensor's largest entry (at least 1).
+
+def _bwd_inputs(B, Hq, Hkv, Tq, Tk, d, seed):
+    q, k, v = wl.random_qkv(B, Hq, Hkv, Tq, Tk, d, torch.bfloat16, seed=seed)
+    dO = _rand((B, Hq, Tq, d), torch.bfloat16, seed + 7)
+    return q, k, v, dO
+
+
+def _gpu_bwd(q, k, v, dO, scale, causal, qo):
+    qd, kd, vd, gd = gpu(q, k, v, dO)
+    o, lse = run_attn(q, k, v, scale, causal, qo, lse=True)
+    od, lsed = gpu(o, lse)
+    dq, dk, dv = ra.attn_bwd(qd, kd, vd, od, gd, lsed, scale=scale, causal=causal, q_offset=qo)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _grad_err(got, want):
+    g = f64(got)
+    assert np.all(np.isfinite(g))
+    return float(np.max(np.abs(g - want))) / max(1.0, float(np.max(np.abs(want))))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tk,d,causal,qo", [
+    (1, 4, 2, 300, 300, 64, True, 0),        # GQA, ragged tail of keys and rows
+    (1, 4, 2, 300, 300, 128, True, 0),
+    (2, 2, 2, 129, 200, 64, False, 0),       # no mask, Tq != Tk
+    (1, 2, 2, 129, 200, 128, False, 0),
+    (1, 8, 2, 70, 1030, 128, True, 960),     # a chunk at the end of a long context
+    (1, 4, 4, 100, 600, 64, True, 500),
+    (1, 2, 1, 1, 77, 64, True, 76),          # one query row
+    (1, 3, 3, 33, 31, 128, False, 0),        # fewer keys than one tile
+    (1, 4, 1, 513, 513, 64, True, 0),        # four query heads per K/V head
+])
+def test_bwd_matches_oracle(B, Hq, Hkv, Tq, Tk, d, causal, qo):
+    say("bwd", B, Hq, Hkv, Tq, Tk, d, causal, qo)
+    q, k, v, dO = _bwd_inputs(B, Hq, Hkv, Tq, Tk, d, 200 + Tq)
+    scale = d ** -0.5
+    got = _gpu_bwd(q, k, v, dO, scale, causal, qo)
+    want = oracle.attn_bwd(q, k, v, dO, scale, causal=causal, q_offset=qo)
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        err = _grad_err(g, w)
+        assert err <= TOL[torch.bfloat16], f"{name}: relative max err {err:.3e}"
+    if causal and Tk > qo + Tq:
+        # keys past the last visible one get exactly zero
+        for g in got[1:]:
+            assert not torch.any(g[:, :, qo + Tq:].float() != 0)
+
+
+def test_bwd_deterministic():
+    say("bwd determinism")
+    q, k, v, dO = _bwd_inputs(1, 8, 2, 700, 700, 128, 31)
+    a = _gpu_bwd(q, k, v, dO, 0.0884, True, 0)
+    b = _gpu_bwd(q, k, v, dO, 0.0884, True, 0)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_workload2_full():
+    """The GPT-2-small-shaped case at full size: dq of the last 64 rows of
+    every head against the oracle (a row's dq needs only that row), and the
+    column sums the softmax fixes for dk and dv (sum over keys of dk is 0;
+    sum over keys of dv equals the sum over rows of dO)."""
+    w = wl.WORKLOADS[2]
+    say("bwd", w.name)
+    q, k, v = wl.inputs(w)
+    dO = _rand(q.shape, torch.bfloat16, 2002)
+    dq, dk, dv = _gpu_bwd(q, k, v, dO, w.scale, True, 0)
+    T = w.Tq
+    tail = slice(T - 64, T)
+    want_dq, _, _ = oracle.attn_bwd(q[:, :, tail], k, v, dO[:, :, tail], w.scale, causal=True,
+                                    q_offset=T - 64)
+    assert _grad_err(dq[:, :, tail], want_dq) <= TOL[torch.bfloat16]
+    dk64, dv64, dO64 = f64(dk), f64(dv), f64(dO)
+    # bf16 rounding of each entry bounds the error of the sums
+    bound_k = 2.0 ** -8 * np.abs(dk64).sum(axis=2) + 1e-3
+    assert np.all(np.abs(dk64.sum(axis=2)) <= bound_k)
+    bound_v = 2.0 ** -8 * (np.abs(dv64).sum(axis=2) + np.abs(dO64).sum(axis=2)) + 1e-3
+    assert np.all(np.abs(dv64.sum(axis=2) - dO64.sum(axis=2)) <= bound_v)

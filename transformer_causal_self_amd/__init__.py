@@ -16,7 +16,9 @@ or a call is made with CPU tensors, the call raises.
     status_string(code)
     attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o=None, scale=None,
                      base=10000.0, pairing="split", workspace=None, lse=None)
-    bind_attn_fwd_ws(...), bind_rope_apply(...), bind_attn_decode_step(...) -> Bound
+    attn_bwd(q, k, v, o, dO, lse, scale=None, causal=True, q_offset=0) -> (dq, dk, dv)
+    bind_attn_fwd_ws(...), bind_rope_apply(...), bind_attn_decode_step(...),
+    bind_attn_bwd(...) -> Bound
 
 A Bound is one of these calls with its arguments checked and marshalled
 once: calling it launches the same work again on the stream it was bound
@@ -34,7 +36,8 @@ LIBRARY = os.path.join(HERE, "librocattn.so")
 
 # the C ABI, as declared in include/rocattn.h
 SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_strided", "attn_workspace_bytes",
-           "rope_apply", "rope_apply_ex", "attn_decode_step", "attn_status_string")
+           "rope_apply", "rope_apply_ex", "attn_decode_step", "attn_bwd",
+           "attn_bwd_workspace_bytes", "attn_status_string")
 
 F32, BF16 = 0, 1
 OK = 0
@@ -80,6 +83,11 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_step.restype = i
         lib.attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
                                          ctypes.c_double, i, i, vp, vp, sz, vp]
+        lib.attn_bwd.restype = i
+        lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
+                                 i, vp, vp, sz]
+        lib.attn_bwd_workspace_bytes.restype = sz
+        lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [i]
         _lib = lib
@@ -320,3 +328,60 @@ def bind_attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o, scale=None,
     returned Bound repeats the step (rotating q in place again)."""
     return _decode_step_call(q, k_new, v_new, k_cache, v_cache, pos, o, scale, base, pairing,
                              workspace, lse, stream)
+
+
+def _bwd_call(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal, q_offset, stream):
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq), ("dk", dk),
+                 ("dv", dv)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, o, dO, dq: [B, Hq, Tq, d]; k, v, dk, dv: [B, Hkv, Tk, d]")
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if (tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d
+            or any(tuple(t.shape) != tuple(q.shape) for t in (o, dO, dq))
+            or any(tuple(t.shape) != tuple(k.shape) for t in (dk, dv))
+            or tuple(lse.shape) != (B, Hq, Tq)):
+        raise ValueError("shape mismatch between the gradient operands")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = 0
+    if workspace is not None:
+        _check_dev("workspace", workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, Hq, Hkv, Tq, Tk, d, float(scale), int(bool(causal)), int(q_offset), _dtype_code(q),
+            _stream(q, stream), _ptr(workspace), ws_bytes)
+    return Bound("attn_bwd", library().attn_bwd, args,
+                 (q, k, v, o, dO, lse, dq, dk, dv, workspace))
+
+
+def attn_bwd_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype) -> int:
+    if not isinstance(dtype, int):
+        import torch
+        dtype = F32 if dtype == torch.float32 else BF16
+    return int(library().attn_bwd_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype))
+
+
+def attn_bwd(q, k, v, o, dO, lse, scale=None, causal=True, q_offset=0, dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of attn_fwd for the upstream gradient dO, from
+    the forward's output o and its log-sum-exp rows lse (float32 [B, Hq, Tq])."""
+    import torch
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        nb = attn_bwd_workspace_bytes(q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2],
+                                      q.shape[3], q.dtype)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    _bwd_call(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal, q_offset, stream)()
+    return dq, dk, dv
+
+
+def bind_attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale=None, causal=True,
+                  q_offset=0, stream=None) -> Bound:
+    """attn_bwd's checks and marshalling now; the launches at each call."""
+    return _bwd_call(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal, q_offset, stream)

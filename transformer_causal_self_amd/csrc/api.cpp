@@ -369,6 +369,65 @@ ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, 
     return launch(p, dtype, s, workspace, ws_bytes);
 }
 
+ROCATTN_API size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d_head,
+                                            int dtype) {
+    if (dtype != ROCATTN_BF16) return 0;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || Hq % Hkv != 0) return 0;
+    if (d_head != 64 && d_head != 128) return 0;
+    return rocattn::bwd_workspace_bytes(B, Hq, Tq);
+}
+
+ROCATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int Hq, int Hkv, int Tq, int Tk, int d_head, float scale, int causal,
+                         int q_offset, int dtype, void* stream, void* workspace,
+                         size_t ws_bytes) {
+    if (dtype != ROCATTN_F32 && dtype != ROCATTN_BF16) return ROCATTN_ERR_DTYPE;
+    if (dtype != ROCATTN_BF16) return ROCATTN_ERR_DTYPE;   // the gradient kernels are bf16
+    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ROCATTN_ERR_NULL;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || d_head <= 0) return ROCATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ROCATTN_ERR_SHAPE;
+    if (d_head != 64 && d_head != 128) return ROCATTN_ERR_HEADDIM;
+    if (causal && q_offset < 0) return ROCATTN_ERR_OFFSET;
+    if (causal && (long long)q_offset + Tq > INT_MAX) return ROCATTN_ERR_OFFSET;
+    if (!isfinite(scale)) return ROCATTN_ERR_SCALE;
+    const void* in[6] = {q, k, v, o, dO, lse};
+    void* out[3] = {dq, dk, dv};
+    for (const void* x : in)
+        if (!aligned16(x)) return ROCATTN_ERR_ALIGN;
+    for (const void* x : out)
+        if (!aligned16(x)) return ROCATTN_ERR_ALIGN;
+    const long long nq = count4(B, Hq, Tq, d_head), nkv = count4(B, Hkv, Tk, d_head);
+    if (nq < 0 || nkv < 0) return ROCATTN_ERR_SHAPE;
+    if (count4(B, Hq, (Tq + 127) / 128, 1) > INT_MAX || count4(B, Hkv, (Tk + 127) / 128, 1) > INT_MAX)
+        return ROCATTN_ERR_SHAPE;
+    const size_t wsb = rocattn::bwd_workspace_bytes(B, Hq, Tq);
+    if (!workspace || ws_bytes < wsb) return ROCATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ROCATTN_ERR_ALIGN;
+    const size_t qb = (size_t)nq * 2, kvb = (size_t)nkv * 2, lb = (size_t)B * Hq * Tq * sizeof(float);
+    const size_t inb[6] = {qb, kvb, kvb, qb, qb, lb};
+    const size_t outb[3] = {qb, kvb, kvb};
+    // outputs and workspace overlap nothing else
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(out[i], outb[i], in[j], inb[j])) return ROCATTN_ERR_SHAPE;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(out[i], outb[i], out[j], outb[j])) return ROCATTN_ERR_SHAPE;
+        if (overlaps(out[i], outb[i], workspace, wsb)) return ROCATTN_ERR_SHAPE;
+    }
+    for (int j = 0; j < 6; ++j)
+        if (overlaps(workspace, wsb, in[j], inb[j])) return ROCATTN_ERR_SHAPE;
+    rocattn::BwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.workspace = workspace;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Tq = Tq; p.Tk = Tk; p.d = d_head;
+    p.scale = scale;
+    p.causal = causal ? 1 : 0;
+    p.q_offset = causal ? q_offset : 0;
+    return rocattn::launch_bwd_bf16(p, static_cast<hipStream_t>(stream)) == hipSuccess ? ROCATTN_OK
+                                                                                        : ROCATTN_ERR_HIP;
+}
+
 ROCATTN_API const char* attn_status_string(int status) {
     switch (status) {
         case ROCATTN_OK: return "success";

@@ -1,0 +1,432 @@
+// attn_bwd_bf16.hip -- gradients of the fused causal attention, bf16 in/out,
+// float32 accumulation, on the gfx950 matrix cores, head sizes 64 and 128.
+//
+// What it computes: for an upstream gradient dO of o = softmax(scale S + M) V,
+// S = Q K^T, per (batch, query head):
+//     P   = exp(scale S - lse)           (the forward's weights, rebuilt from
+//                                          its log-sum-exp rows)
+//     dV  = P^T dO,   dP = dO V^T,   D_i = sum_c dO_ic O_ic,
+//     dS  = P (dP - D),   dQ = scale dS K,   dK = scale dS^T Q,
+// the chain rule of the forward through the softmax ("The Transformer
+// architecture" -- Softmax is a differentiable allocation; the operator is
+// trained in "Transformer Math and Implementation Deep Dive" -- What To
+// Implement: tiny training loop).  A K/V head sums dK and dV over the
+// query heads of its group ("The Transformer architecture" -- GQA), in a
+// fixed order, so results are deterministic.  D_i equals sum_j P_ij dP_ij.
+//
+// Three kernels, each a plain adaptation of the forward's tile scheme:
+//  * bwd_rowdot_kernel: D = rowsum(dO * O) into the workspace.
+//  * bwd_dq_kernel: one workgroup = 4 waves x 32 query rows; it walks the
+//    32-key tiles of its rows like the forward (S^T = K Q^T with keys on the
+//    MFMA rows, one query per lane), forms dP^T = V dO^T the same way, then
+//    dQ^T += K^T dS^T with K^T read by the LDS transpose read.  Per tile the
+//    ring holds K and V with the row-read swizzle and K again with the
+//    transpose-read swizzle.
+//  * bwd_dkv_kernel: one workgroup = 4 waves x 32 keys; it walks the 32-row
+//    query tiles of every query head of the group (S = Q K^T with queries on
+//    the MFMA rows, one key per lane), and accumulates dV^T += dO^T P and
+//    dK^T += Q^T dS with dO^T and Q^T from transpose reads.  The rows' lse
+//    and D values travel with the query tile through LDS.
+// Rows past Tq and keys past Tk contribute nothing; keys no query can see
+// get dK = dV = 0.
+#include <math.h>
+
+#include "internal.hpp"
+#include "mfma_tiles.hpp"
+
+namespace rocattn {
+namespace {
+
+struct BwdArgs {
+    const bf16* q;
+    const bf16* k;
+    const bf16* v;
+    const bf16* o;
+    const bf16* dO;
+    const float* lse;   // natural-log row log-sum-exp of the forward [B][Hq][Tq]
+    float* Drow;        // workspace: rowsum(dO * O) [B][Hq][Tq]
+    bf16* dq;
+    bf16* dk;
+    bf16* dv;
+    int B, Hq, Hkv, Tq, Tk, R;
+    float c;            // scale * log2(e)
+    float scale;
+    int causal, q_offset;
+};
+
+template <int D>
+struct BCfg {
+    static constexpr int BN = 32;               // keys (dq) or query rows (dkv) per tile
+    static constexpr int NW = 4;                // waves per workgroup, 32 rows or keys each
+    static constexpr int BM = NW * 32;          // rows (dq) or keys (dkv) per workgroup
+    static constexpr int NQ = D / 16;           // 16-wide d slices of a product over d
+    static constexpr int NDB = D / 32;          // 32-row blocks of d in the accumulators
+    static constexpr int NKC = 2;               // 16-wide slices of a 32-long tile
+    static constexpr int NCH = D / 8;           // 16-byte chunks per row
+    static constexpr int TB = BN * D * 2;       // bytes of one tile
+    static constexpr int CPL = NW * 64;         // lanes that copy
+    static constexpr int NINS = BN * NCH / CPL; // 16-byte copies per lane per tile
+    static constexpr int RSTR = CPL / NCH;      // tile rows filled by one copy instruction
+};
+
+// offset (before + 4h) of element e of a 32x32 accumulator block along its rows
+__device__ inline int row_of(int e) { return 8 * (e >> 2) + (e & 3); }
+
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdArgs a) {
+    constexpr int LPR = D / 8;    // lanes per row, 8 elements each
+    const long long rows = (long long)a.B * a.Hq * a.Tq;
+    const long long r = ((long long)blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int part = threadIdx.x % LPR;
+    float s = 0.f;
+    if (r < rows) {
+        const bf16x8 g = *reinterpret_cast<const bf16x8*>(a.dO + r * D + 8 * part);
+        const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + r * D + 8 * part);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf((float)g[e], (float)o[e], s);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (r < rows && part == 0) a.Drow[r] = s;
+}
+
+// Per-lane tile addressing shared by the two gradient kernels.
+template <int D>
+struct TileLanes {
+    typedef BCfg<D> C;
+    int cp_r0;
+    unsigned cp_kcol, cp_vcol, cp_lds;
+    unsigned koff, voff;   // row-read and transpose-read offsets in a tile
+    __device__ TileLanes(int wave, int lane) {
+        const int cl = wave * 64 + lane;
+        cp_r0 = cl / C::NCH;
+        const int cp_p = cl % C::NCH;
+        cp_kcol = 16u * (unsigned)(cp_p ^ swz_k<D>(cp_r0));
+        cp_vcol = 16u * (unsigned)(cp_p ^ swz_v<D>(cp_r0));
+        cp_lds = (unsigned)(wave * 64 * 16);
+        const int h = lane >> 5, li = lane & 31;
+        koff = 2u * (unsigned)(li * D + 8 * (h ^ swz_k<D>(li)));
+        const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
+        voff = 2u * (unsigned)((4 * (tg >> 1) + tr) * D + 16 * (tg & 1) + 4 * tq + 8 * swz_v<D>(tr));
+    }
+    // copy rows [j0, j0 + BN) of a [T][D] matrix (rows past T - 1 repeat row
+    // T - 1) into the tile at `slot`, chunk positions swizzled by `col`
+    __device__ void copy(const bf16* m, int T, int j0, unsigned slot, unsigned col) const {
+#pragma unroll
+        for (int i = 0; i < C::NINS; ++i) {
+            const int row = min(cp_r0 + i * C::RSTR, T - 1 - j0);
+            copy16(m + (long long)j0 * D, (unsigned)row * (unsigned)(D * 2) + col,
+                   slot + (unsigned)(i * C::CPL * 16) + cp_lds);
+        }
+    }
+    // row operand: row li of the tile, d slice m (16 wide), half h
+    __device__ bf16x8 rowfrag(unsigned tile, int m) const {
+        return *(lds_bf16x8*)(uintptr_t)((tile + koff) ^ (32u * m));
+    }
+    // transposed operand: d-block cb (32 wide) over tile rows slice kc
+    // (16 rows, in the row order of an accumulator block's elements)
+    __device__ bf16x8 trfrag(unsigned tile, int cb, int kc) const {
+        const unsigned addr = (tile + voff + (unsigned)(16 * kc * D * 2)) ^ (64u * cb);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 16u * D));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+};
+
+// lane's 8 consecutive d values (16m + 8h ..) of row `row` of a [T][D] matrix
+template <int D>
+__device__ inline void load_row_frags(const bf16* m, int row, bool ok, int h, bf16x8 (&f)[D / 16]) {
+    const uint4* src = reinterpret_cast<const uint4*>(m + (long long)(ok ? row : 0) * D + 8 * h);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+        uint4 u = src[2 * i];
+        if (!ok) u = make_uint4(0, 0, 0, 0);
+        f[i] = __builtin_bit_cast(bf16x8, u);
+    }
+}
+
+// store 32 d-blocks' worth of a transposed accumulator (rows = d, lane = row
+// of the output) times `scale` as bf16 into row `dst`
+template <int D>
+__device__ inline void store_rowT(bf16* dst, const f32x16 (&acc)[D / 32], float scale, int h) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            bf16x4 val;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) val[e] = (bf16)(acc[cb][4 * g4 + e] * scale);
+            *reinterpret_cast<bf16x4*>(dst + 32 * cb + 8 * g4 + 4 * h) = val;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: walk the key tiles of a block of 128 query rows.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdArgs a) {
+    typedef BCfg<D> C;
+    constexpr int BN = C::BN, TB = C::TB, NQ = C::NQ, NDB = C::NDB, NKC = C::NKC;
+    constexpr int SLOT = 3 * TB;   // ring slot: K (row reads) | V (row reads) | K (transpose reads)
+    __shared__ __attribute__((aligned(1024))) char lds[2 * SLOT];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, li = lane & 31;
+    const int n_qt = (a.Tq + C::BM - 1) / C::BM;
+    const int BH = a.B * a.Hq;
+    const int qt = n_qt - 1 - (int)(blockIdx.x / BH);   // longest first
+    const int bh = (int)(blockIdx.x % BH);
+    const int b = bh / a.Hq, hq = bh - b * a.Hq, hk = hq / a.R;
+    const int i0w = qt * C::BM + 32 * wave, iq = i0w + li;
+    const bool row_ok = iq < a.Tq;
+    const long long rowid = (long long)bh * a.Tq + iq;
+
+    bf16x8 qf[NQ], gf[NQ];
+    load_row_frags<D>(a.q + (long long)bh * a.Tq * D, iq, row_ok, h, qf);
+    load_row_frags<D>(a.dO + (long long)bh * a.Tq * D, iq, row_ok, h, gf);
+    const float Lr = row_ok ? a.lse[rowid] * kLog2e : 0.f;
+    const float Dv = row_ok ? a.Drow[rowid] : 0.f;
+
+    const int kv_end = a.causal ? min(a.Tk, a.q_offset + qt * C::BM + C::BM) : a.Tk;
+    const int n = (kv_end + BN - 1) / BN;
+    const int row_lim = a.causal ? min(a.Tk - 1, a.q_offset + iq) : a.Tk - 1;
+    const int wave_last = a.causal ? min(a.Tk - 1, a.q_offset + i0w + 31) : a.Tk - 1;
+    const int wave_full = a.causal ? min(a.Tk, a.q_offset + i0w + 1) : a.Tk;
+    const int last = i0w >= a.Tq ? -1 : wave_last / BN;
+
+    const TileLanes<D> tl(wave, lane);
+    const unsigned base = lds_addr(lds);
+    const bf16* kh = a.k + (long long)(b * a.Hkv + hk) * a.Tk * D;
+    const bf16* vh = a.v + (long long)(b * a.Hkv + hk) * a.Tk * D;
+    auto copy_step = [&](int t, int P) {
+        const int j0 = min(t, n - 1) * BN;
+        const unsigned s = base + (unsigned)(P * SLOT);
+        tl.copy(kh, a.Tk, j0, s, tl.cp_kcol);
+        tl.copy(vh, a.Tk, j0, s + TB, tl.cp_kcol);
+        tl.copy(kh, a.Tk, j0, s + 2 * TB, tl.cp_vcol);
+    };
+
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int cb = 0; cb < NDB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+    copy_step(0, 0);
+    wait_vm<0>();
+    __syncthreads();
+    auto step = [&](int t, auto slot) {
+        constexpr int P = decltype(slot)::value;
+        copy_step(t + 1, 1 - P);
+        if (t <= last) {
+            const unsigned s = base + (unsigned)(P * SLOT);
+            f32x16 st = {}, dp = {};
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(s, m), qf[m], st, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(s + TB, m), gf[m], dp, 0, 0, 0);
+            }
+            const bool mask = (t + 1) * BN > wave_full;
+            const int lim = row_lim - (t * BN + 4 * h);
+            bf16x8 dsb[NKC];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const bool vis = !mask || row_of(e) <= lim;
+                const float p = vis ? __builtin_amdgcn_exp2f(fmaf(st[e], a.c, -Lr)) : 0.f;
+                dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - Dv));
+            }
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int cb = 0; cb < NDB; ++cb)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.trfrag(s + 2 * TB, cb, kc), dsb[kc],
+                                                                      acc[cb], 0, 0, 0);
+        }
+        wait_vm<0>();   // tile t + 1 has landed
+        __syncthreads();
+    };
+    for (int t = 0; t < n; t += 2) {
+        step(t, IC<0>{});
+        if (t + 1 < n) step(t + 1, IC<1>{});
+    }
+    wait_vm<0>();
+    if (row_ok) store_rowT<D>(a.dq + rowid * D, acc, a.scale, h);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: walk the query tiles of every query head of the group for a block
+// of 128 keys.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
+void bwd_dkv_kernel(BwdArgs a) {
+    typedef BCfg<D> C;
+    constexpr int BN = C::BN, TB = C::TB, NQ = C::NQ, NDB = C::NDB, NKC = C::NKC;
+    // ring slot: Q (row reads) | dO (row reads) | Q (transpose reads) |
+    // dO (transpose reads) | lse and D of the 32 rows (padded to 1 KiB)
+    constexpr int SLOT = 4 * TB + 1024;
+    __shared__ __attribute__((aligned(1024))) char lds[2 * SLOT];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, li = lane & 31;
+    const int G = a.B * a.Hkv;
+    const int kb = (int)(blockIdx.x / G);   // ascending: early keys are seen by the most rows
+    const int g = (int)(blockIdx.x % G);
+    const int b = g / a.Hkv, hk = g - b * a.Hkv;
+    const int j0 = kb * C::BM, jw = j0 + 32 * wave, key = jw + li;
+    const bool key_ok = key < a.Tk;
+
+    bf16x8 kf[NQ], vf[NQ];
+    load_row_frags<D>(a.k + (long long)g * a.Tk * D, key, key_ok, h, kf);
+    load_row_frags<D>(a.v + (long long)g * a.Tk * D, key, key_ok, h, vf);
+
+    // query tiles that can see a key of this block
+    const int n_rt = (a.Tq + BN - 1) / BN;
+    const int rt0 = a.causal ? min(n_rt, max(0, j0 - a.q_offset) / BN) : 0;
+    const int per_head = n_rt - rt0;
+    const int nsteps = a.R * per_head;
+
+    const TileLanes<D> tl(wave, lane);
+    const unsigned base = lds_addr(lds);
+    auto head_of = [&](int s) { return hk * a.R + s / per_head; };
+    auto rows_of = [&](int s) { return (rt0 + s % per_head) * BN; };
+    auto copy_step = [&](int s, int P) {
+        const int sc = min(s, nsteps - 1);
+        const long long bh = (long long)b * a.Hq + head_of(sc);
+        const int r0 = rows_of(sc);
+        const unsigned sl = base + (unsigned)(P * SLOT);
+        const bf16* qm = a.q + bh * a.Tq * D;
+        const bf16* gm = a.dO + bh * a.Tq * D;
+        tl.copy(qm, a.Tq, r0, sl, tl.cp_kcol);
+        tl.copy(gm, a.Tq, r0, sl + TB, tl.cp_kcol);
+        tl.copy(qm, a.Tq, r0, sl + 2 * TB, tl.cp_vcol);
+        tl.copy(gm, a.Tq, r0, sl + 3 * TB, tl.cp_vcol);
+    };
+    // lse (as log2) and D of the 32 rows of step s into slot P, by wave 0
+    auto rowstats_step = [&](int s, int P) {
+        if (wave == 0 && lane < 2 * BN && s < nsteps) {
+            const long long bh = (long long)b * a.Hq + head_of(s);
+            const int r = rows_of(s) + (lane & 31);
+            const bool ok = r < a.Tq;
+            const float x = !ok ? 0.f : (lane < BN ? a.lse[bh * a.Tq + r] * kLog2e : a.Drow[bh * a.Tq + r]);
+            reinterpret_cast<float*>(lds + P * SLOT + 4 * TB)[lane] = x;
+        }
+    };
+
+    f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+    for (int cb = 0; cb < NDB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dk[cb][r] = 0.f; dv[cb][r] = 0.f; }
+
+    if (nsteps > 0) {
+        copy_step(0, 0);
+        rowstats_step(0, 0);
+        wait_vm<0>();
+        __syncthreads();
+    }
+    auto step = [&](int s, auto slot) {
+        constexpr int P = decltype(slot)::value;
+        copy_step(s + 1, 1 - P);
+        const int r0 = rows_of(s);
+        // some row of the tile sees a key of this wave
+        const bool any = !a.causal || jw <= a.q_offset + min(r0 + BN, a.Tq) - 1;
+        if (any && jw < a.Tk) {
+            const unsigned sl = base + (unsigned)(P * SLOT);
+            f32x16 st = {}, dp = {};
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(sl, m), kf[m], st, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(sl + TB, m), vf[m], dp, 0, 0, 0);
+            }
+            const float* stats = reinterpret_cast<const float*>(lds + P * SLOT + 4 * TB);
+            // every pair of the 32 x 32 block visible: no mask work
+            const bool full = key_ok && jw + 31 < a.Tk && r0 + BN <= a.Tq &&
+                              (!a.causal || jw + 31 <= a.q_offset + r0);
+            bf16x8 pb[NKC], dsb[NKC];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 8 * i + 4 * h;   // rows rr .. rr + 3 of the tile
+                const float4 L4 = *reinterpret_cast<const float4*>(stats + rr);
+                const float4 D4 = *reinterpret_cast<const float4*>(stats + BN + rr);
+                const float Ls[4] = {L4.x, L4.y, L4.z, L4.w}, Ds[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int e = 4 * i + j, row = r0 + rr + j;
+                    const bool vis = full || (key_ok && row < a.Tq && (!a.causal || key <= a.q_offset + row));
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(st[e], a.c, -Ls[j])) : 0.f;
+                    pb[e >> 3][e & 7] = (bf16)p;
+                    dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - Ds[j]));
+                }
+            }
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int cb = 0; cb < NDB; ++cb) {
+                    dv[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.trfrag(sl + 3 * TB, cb, kc), pb[kc],
+                                                                     dv[cb], 0, 0, 0);
+                    dk[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.trfrag(sl + 2 * TB, cb, kc), dsb[kc],
+                                                                     dk[cb], 0, 0, 0);
+                }
+        }
+        rowstats_step(s + 1, 1 - P);
+        wait_vm<0>();   // step s + 1 has landed
+        __syncthreads();
+    };
+    for (int s = 0; s < nsteps; s += 2) {
+        step(s, IC<0>{});
+        if (s + 1 < nsteps) step(s + 1, IC<1>{});
+    }
+    wait_vm<0>();
+    if (key_ok) {
+        store_rowT<D>(a.dk + ((long long)g * a.Tk + key) * D, dk, a.scale, h);
+        store_rowT<D>(a.dv + ((long long)g * a.Tk + key) * D, dv, 1.f, h);
+    }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+    typedef BCfg<D> C;
+    const long long rows = (long long)a.B * a.Hq * a.Tq;
+    const long long nthreads = rows * (D / 8);
+    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long n_qt = (a.Tq + C::BM - 1) / C::BM;
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(n_qt * a.B * a.Hq)), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long n_kb = (a.Tk + C::BM - 1) / C::BM;
+    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)(n_kb * a.B * a.Hkv)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int Hq, int Tq) { return sizeof(float) * (size_t)B * Hq * Tq; }
+
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+    BwdArgs a;
+    a.q = static_cast<const bf16*>(p.q);
+    a.k = static_cast<const bf16*>(p.k);
+    a.v = static_cast<const bf16*>(p.v);
+    a.o = static_cast<const bf16*>(p.o);
+    a.dO = static_cast<const bf16*>(p.dO);
+    a.lse = p.lse;
+    a.Drow = static_cast<float*>(p.workspace);
+    a.dq = static_cast<bf16*>(p.dq);
+    a.dk = static_cast<bf16*>(p.dk);
+    a.dv = static_cast<bf16*>(p.dv);
+    a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Tq = p.Tq; a.Tk = p.Tk;
+    a.R = p.Hq / p.Hkv;
+    a.c = p.scale * kLog2e;
+    a.scale = p.scale;
+    a.causal = p.causal;
+    a.q_offset = p.causal ? p.q_offset : 0;
+    return p.d == 64 ? launch_bwd_d<64>(a, stream) : launch_bwd_d<128>(a, stream);
+}
+
+}  // namespace rocattn

@@ -57,6 +57,29 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_rope(void* x, long long n_seq, int T, int d, int pos0, double base,
                        int dtype, int pairing, hipStream_t stream);
 
+// Everything a backward launch needs (dense [B][H][T][d] tensors), validated
+// by the host API.
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dO;
+    const float* lse;   // natural-log row log-sum-exp of the forward
+    void* dq;
+    void* dk;
+    void* dv;
+    void* workspace;    // bwd_workspace_bytes(B, Hq, Tq) bytes
+    int B, Hq, Hkv, Tq, Tk, d;
+    float scale;
+    int causal;
+    int q_offset;
+};
+
+// Gradients dq, dk, dv of the bf16 attention, d in {64, 128}.
+size_t bwd_workspace_bytes(int B, int Hq, int Tq);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+
 // Decode-step preparation in one launch: q [B][Hq][Tn][d] rotated in place,
 // the new keys kn [B][Hkv][Tn][d] rotated into kc [B][Hkv][Tmax][d] at
 // tokens pos .. pos + Tn - 1, the new values vn copied into vc there.
