@@ -265,6 +265,8 @@ int attn_decode_step(void* q, const void* k_new, const void* v_new, void* k_cach
  *   workspace    attn_bwd_workspace_bytes(...) bytes of device memory.
  *   other arguments as attn_fwd.
  * Supported: bf16, d_head in {64, 128} (float32 returns ERR_DTYPE).
+ * The workspace holds per-row statistics (256 bytes per 32 query rows of a
+ * head); its contents need no initialisation and are scratch afterwards.
  * Outputs and workspace must not overlap each other or the inputs
  * (ERR_SHAPE).  Deterministic: a fixed summation order, no atomics.
  * Returns a rocattn_status.

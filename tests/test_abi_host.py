@@ -195,7 +195,7 @@ def bwd(q=A, k=Bp, v=C, o=D, dO=0x70000000, lse=0x78000000, dq=0x7C000000, dk=0x
     (dict(Tq=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(d=96), -4), (dict(d=32), -4),
     (dict(q_offset=-1), -5), (dict(scale=float("nan")), -6),
     (dict(lse=0x78000004), -7), (dict(dk=0x7E000002), -7), (dict(ws=0x7F800008), -7),
-    (dict(ws=None), -8), (dict(ws_bytes=4 * 4 * 16 - 1), -8),
+    (dict(ws=None), -8), (dict(ws_bytes=4 * 64 * 4 - 1), -8),
     (dict(dq=A + 64), -2),                               # dq overlaps q
     (dict(dk=0x7F000000 - 64), -2),                      # dk overlaps dv
     (dict(dv=0x70000000 + 256), -2),                     # dv overlaps dO
@@ -207,8 +207,10 @@ def test_attn_bwd_rejects(kw, status):
 
 def test_bwd_workspace_bytes():
     lib = rocattn.library()
-    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 16, 16, 64, BF16) == 4 * 4 * 16
-    assert lib.attn_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 128, BF16) == 4 * 2 * 32 * 4096
+    # 64 floats (lse and D of 32 rows) per 32-row tile of each (batch, query head)
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 16, 16, 64, BF16) == 4 * 64 * 4
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 33, 16, 64, BF16) == 4 * 64 * 4 * 2
+    assert lib.attn_bwd_workspace_bytes(2, 32, 8, 4096, 4096, 128, BF16) == 4 * 2 * 32 * 4096 * 2
     assert lib.attn_bwd_workspace_bytes(1, 4, 2, 16, 16, 64, F32) == 0
     assert lib.attn_bwd_workspace_bytes(1, 4, 2, 16, 16, 96, BF16) == 0
     assert lib.attn_bwd_workspace_bytes(1, 6, 4, 16, 16, 64, BF16) == 0

@@ -15,7 +15,10 @@
 // fixed order, so results are deterministic.  D_i equals sum_j P_ij dP_ij.
 //
 // Three kernels, each a plain adaptation of the forward's tile scheme:
-//  * bwd_rowdot_kernel: D = rowsum(dO * O) into the workspace.
+//  * bwd_rowdot_kernel: per 32-row tile of a head, the rows' lse (as a
+//    base-2 exponent) and D = rowsum(dO * O) into the workspace, 64 floats
+//    per tile (32 lse, then 32 D; rows past Tq get 0), so a tile's row
+//    statistics are one contiguous 256-byte block.
 //  * bwd_dq_kernel: one workgroup = 4 waves x 32 query rows; it walks the
 //    32-key tiles of its rows like the forward (S^T = K Q^T with keys on the
 //    MFMA rows, one query per lane), forms dP^T = V dO^T the same way, then
@@ -44,11 +47,12 @@ struct BwdArgs {
     const bf16* o;
     const bf16* dO;
     const float* lse;   // natural-log row log-sum-exp of the forward [B][Hq][Tq]
-    float* Drow;        // workspace: rowsum(dO * O) [B][Hq][Tq]
+    float* stats;       // workspace [B * Hq][n_rt][64]: lse * log2(e), then D, of a row tile
     bf16* dq;
     bf16* dk;
     bf16* dv;
     int B, Hq, Hkv, Tq, Tk, R;
+    int n_rt;           // 32-row tiles per head
     float c;            // scale * log2(e)
     float scale;
     int causal, q_offset;
@@ -76,19 +80,28 @@ __device__ inline int row_of(int e) { return 8 * (e >> 2) + (e & 3); }
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdArgs a) {
     constexpr int LPR = D / 8;    // lanes per row, 8 elements each
-    const long long rows = (long long)a.B * a.Hq * a.Tq;
+    const int rows_pad = a.n_rt * 32;
+    const long long rows = (long long)a.B * a.Hq * rows_pad;
     const long long r = ((long long)blockIdx.x * 256 + threadIdx.x) / LPR;
     const int part = threadIdx.x % LPR;
+    const long long bh = r / rows_pad;
+    const int i = (int)(r - bh * rows_pad);
+    const bool ok = r < rows && i < a.Tq;
     float s = 0.f;
-    if (r < rows) {
-        const bf16x8 g = *reinterpret_cast<const bf16x8*>(a.dO + r * D + 8 * part);
-        const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + r * D + 8 * part);
+    if (ok) {
+        const long long row = bh * a.Tq + i;
+        const bf16x8 g = *reinterpret_cast<const bf16x8*>(a.dO + row * D + 8 * part);
+        const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + row * D + 8 * part);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = fmaf((float)g[e], (float)o[e], s);
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (r < rows && part == 0) a.Drow[r] = s;
+    if (r < rows && part == 0) {
+        float* t = a.stats + (bh * a.n_rt + (i >> 5)) * 64;
+        t[i & 31] = ok ? a.lse[bh * a.Tq + i] * kLog2e : 0.f;
+        t[32 + (i & 31)] = s;
+    }
 }
 
 // Per-lane tile addressing shared by the two gradient kernels.
@@ -186,8 +199,9 @@ void bwd_dq_kernel(BwdArgs a) {
     bf16x8 qf[NQ], gf[NQ];
     load_row_frags<D>(a.q + (long long)bh * a.Tq * D, iq, row_ok, h, qf);
     load_row_frags<D>(a.dO + (long long)bh * a.Tq * D, iq, row_ok, h, gf);
-    const float Lr = row_ok ? a.lse[rowid] * kLog2e : 0.f;
-    const float Dv = row_ok ? a.Drow[rowid] : 0.f;
+    const float* tstats = a.stats + ((long long)bh * a.n_rt + (i0w >> 5)) * 64;
+    const float Lr = row_ok ? tstats[li] : 0.f;
+    const float Dv = row_ok ? tstats[32 + li] : 0.f;
 
     const int kv_end = a.causal ? min(a.Tk, a.q_offset + qt * C::BM + C::BM) : a.Tk;
     const int n = (kv_end + BN - 1) / BN;
@@ -282,20 +296,28 @@ void bwd_dkv_kernel(BwdArgs a) {
     load_row_frags<D>(a.k + (long long)g * a.Tk * D, key, key_ok, h, kf);
     load_row_frags<D>(a.v + (long long)g * a.Tk * D, key, key_ok, h, vf);
 
-    // query tiles that can see a key of this block
+    // query tiles that can see a key of this block; step s covers head
+    // hk * R + s / per_head and row tile n_rt - 1 - s % per_head (the tiles
+    // of a head from the last down, so the key blocks of a group, on one XCD
+    // when B * Hkv is a multiple of 8, walk the same tiles at the same time)
     const int n_rt = (a.Tq + BN - 1) / BN;
     const int rt0 = a.causal ? min(n_rt, max(0, j0 - a.q_offset) / BN) : 0;
     const int per_head = n_rt - rt0;
     const int nsteps = a.R * per_head;
+    struct Pos { int head, tile; };   // head within the group, row tile
+    auto advance = [&](Pos p) {
+        if (--p.tile < rt0) { p.tile = n_rt - 1; ++p.head; }
+        return p;
+    };
 
     const TileLanes<D> tl(wave, lane);
     const unsigned base = lds_addr(lds);
-    auto head_of = [&](int s) { return hk * a.R + s / per_head; };
-    auto rows_of = [&](int s) { return (rt0 + s % per_head) * BN; };
-    auto copy_step = [&](int s, int P) {
-        const int sc = min(s, nsteps - 1);
-        const long long bh = (long long)b * a.Hq + head_of(sc);
-        const int r0 = rows_of(sc);
+    const long long bh0 = (long long)b * a.Hq + (long long)hk * a.R;
+    // tiles of step position p into slot P (the last position repeats past the end)
+    auto copy_step = [&](Pos p, int P) {
+        if (p.head >= a.R) { p.head = a.R - 1; p.tile = rt0; }
+        const long long bh = bh0 + p.head;
+        const int r0 = p.tile * BN;
         const unsigned sl = base + (unsigned)(P * SLOT);
         const bf16* qm = a.q + bh * a.Tq * D;
         const bf16* gm = a.dO + bh * a.Tq * D;
@@ -304,15 +326,13 @@ void bwd_dkv_kernel(BwdArgs a) {
         tl.copy(qm, a.Tq, r0, sl + 2 * TB, tl.cp_vcol);
         tl.copy(gm, a.Tq, r0, sl + 3 * TB, tl.cp_vcol);
     };
-    // lse (as log2) and D of the 32 rows of step s into slot P, by wave 0
-    auto rowstats_step = [&](int s, int P) {
-        if (wave == 0 && lane < 2 * BN && s < nsteps) {
-            const long long bh = (long long)b * a.Hq + head_of(s);
-            const int r = rows_of(s) + (lane & 31);
-            const bool ok = r < a.Tq;
-            const float x = !ok ? 0.f : (lane < BN ? a.lse[bh * a.Tq + r] * kLog2e : a.Drow[bh * a.Tq + r]);
-            reinterpret_cast<float*>(lds + P * SLOT + 4 * TB)[lane] = x;
-        }
+    // the row statistics of a step's tile into the slot, by wave 0 (one
+    // dword per lane, asynchronous like the tiles)
+    auto stats_step = [&](Pos p, int P) {
+        if (p.head >= a.R) { p.head = a.R - 1; p.tile = rt0; }
+        if (wave == 0)
+            copy4(a.stats + ((bh0 + p.head) * a.n_rt + p.tile) * 64, 4u * (unsigned)lane,
+                  base + (unsigned)(P * SLOT + 4 * TB));
     };
 
     f32x16 dk[NDB], dv[NDB];
@@ -321,63 +341,88 @@ void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dk[cb][r] = 0.f; dv[cb][r] = 0.f; }
 
+    Pos cur = {0, n_rt - 1};
     if (nsteps > 0) {
-        copy_step(0, 0);
-        rowstats_step(0, 0);
+        copy_step(cur, 0);
+        stats_step(cur, 0);
         wait_vm<0>();
         __syncthreads();
     }
-    auto step = [&](int s, auto slot) {
+    auto step = [&](auto slot) {
         constexpr int P = decltype(slot)::value;
-        copy_step(s + 1, 1 - P);
-        const int r0 = rows_of(s);
+        const Pos nxt = advance(cur);
+        copy_step(nxt, 1 - P);
+        stats_step(nxt, 1 - P);
+        const int r0 = cur.tile * BN;
         // some row of the tile sees a key of this wave
         const bool any = !a.causal || jw <= a.q_offset + min(r0 + BN, a.Tq) - 1;
         if (any && jw < a.Tk) {
             const unsigned sl = base + (unsigned)(P * SLOT);
+            bf16x8 qa[NQ], ga[NQ];
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                qa[m] = tl.rowfrag(sl, m);
+                ga[m] = tl.rowfrag(sl + TB, m);
+            }
             f32x16 st = {}, dp = {};
 #pragma unroll
             for (int m = 0; m < NQ; ++m) {
-                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(sl, m), kf[m], st, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(sl + TB, m), vf[m], dp, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[m], kf[m], st, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[m], vf[m], dp, 0, 0, 0);
             }
+            // dO^T and Q^T for the second products (independent of the softmax)
+            bf16x8 ta[NKC][NDB], tq[NKC][NDB];
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int cb = 0; cb < NDB; ++cb) {
+                    ta[kc][cb] = tl.trfrag(sl + 3 * TB, cb, kc);
+                    tq[kc][cb] = tl.trfrag(sl + 2 * TB, cb, kc);
+                }
             const float* stats = reinterpret_cast<const float*>(lds + P * SLOT + 4 * TB);
-            // every pair of the 32 x 32 block visible: no mask work
-            const bool full = key_ok && jw + 31 < a.Tk && r0 + BN <= a.Tq &&
-                              (!a.causal || jw + 31 <= a.q_offset + r0);
+            float Ls[16], Ds[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {   // rows 8i + 4h .. + 3 of the tile
+                const float4 L4 = *reinterpret_cast<const float4*>(stats + 8 * i + 4 * h);
+                const float4 D4 = *reinterpret_cast<const float4*>(stats + BN + 8 * i + 4 * h);
+                Ls[4 * i] = L4.x; Ls[4 * i + 1] = L4.y; Ls[4 * i + 2] = L4.z; Ls[4 * i + 3] = L4.w;
+                Ds[4 * i] = D4.x; Ds[4 * i + 1] = D4.y; Ds[4 * i + 2] = D4.z; Ds[4 * i + 3] = D4.w;
+            }
+            float p[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st[e], a.c, -Ls[e]));
+            // every pair of the 32 x 32 block visible: no mask work (uniform)
+            const bool full = jw + 31 < a.Tk && r0 + BN <= a.Tq && (!a.causal || jw + 31 <= a.q_offset + r0);
+            if (!full) {
+                const int lim = a.causal ? key - a.q_offset - 1 : -1;   // rows <= lim precede the key
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = r0 + row_of(e) + 4 * h;
+                    const bool vis = key_ok && row < a.Tq && row > lim;
+                    p[e] = vis ? p[e] : 0.f;
+                }
+            }
             bf16x8 pb[NKC], dsb[NKC];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 8 * i + 4 * h;   // rows rr .. rr + 3 of the tile
-                const float4 L4 = *reinterpret_cast<const float4*>(stats + rr);
-                const float4 D4 = *reinterpret_cast<const float4*>(stats + BN + rr);
-                const float Ls[4] = {L4.x, L4.y, L4.z, L4.w}, Ds[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int e = 4 * i + j, row = r0 + rr + j;
-                    const bool vis = full || (key_ok && row < a.Tq && (!a.causal || key <= a.q_offset + row));
-                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(st[e], a.c, -Ls[j])) : 0.f;
-                    pb[e >> 3][e & 7] = (bf16)p;
-                    dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - Ds[j]));
-                }
+            for (int e = 0; e < 16; ++e) {
+                pb[e >> 3][e & 7] = (bf16)p[e];
+                dsb[e >> 3][e & 7] = (bf16)(p[e] * (dp[e] - Ds[e]));
             }
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int cb = 0; cb < NDB; ++cb) {
-                    dv[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.trfrag(sl + 3 * TB, cb, kc), pb[kc],
-                                                                     dv[cb], 0, 0, 0);
-                    dk[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.trfrag(sl + 2 * TB, cb, kc), dsb[kc],
-                                                                     dk[cb], 0, 0, 0);
+                    dv[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[kc][cb], pb[kc], dv[cb], 0, 0, 0);
+                    dk[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[kc][cb], dsb[kc], dk[cb], 0, 0, 0);
                 }
         }
-        rowstats_step(s + 1, 1 - P);
-        wait_vm<0>();   // step s + 1 has landed
+        cur = nxt;
+        wait_vm<0>();   // the next step's tiles have landed
         __syncthreads();
     };
     for (int s = 0; s < nsteps; s += 2) {
-        step(s, IC<0>{});
-        if (s + 1 < nsteps) step(s + 1, IC<1>{});
+        step(IC<0>{});
+        if (s + 1 < nsteps) step(IC<1>{});
     }
     wait_vm<0>();
     if (key_ok) {
@@ -389,7 +434,7 @@ void bwd_dkv_kernel(BwdArgs a) {
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     typedef BCfg<D> C;
-    const long long rows = (long long)a.B * a.Hq * a.Tq;
+    const long long rows = (long long)a.B * a.Hq * a.n_rt * 32;
     const long long nthreads = rows * (D / 8);
     hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
                        stream, a);
@@ -406,7 +451,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int Hq, int Tq) { return sizeof(float) * (size_t)B * Hq * Tq; }
+size_t bwd_workspace_bytes(int B, int Hq, int Tq) {
+    return sizeof(float) * 64 * (size_t)B * Hq * (size_t)((Tq + 31) / 32);
+}
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     BwdArgs a;
@@ -416,12 +463,13 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     a.o = static_cast<const bf16*>(p.o);
     a.dO = static_cast<const bf16*>(p.dO);
     a.lse = p.lse;
-    a.Drow = static_cast<float*>(p.workspace);
+    a.stats = static_cast<float*>(p.workspace);
     a.dq = static_cast<bf16*>(p.dq);
     a.dk = static_cast<bf16*>(p.dk);
     a.dv = static_cast<bf16*>(p.dv);
     a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.Tq = p.Tq; a.Tk = p.Tk;
     a.R = p.Hq / p.Hkv;
+    a.n_rt = (p.Tq + 31) / 32;
     a.c = p.scale * kLog2e;
     a.scale = p.scale;
     a.causal = p.causal;

@@ -53,6 +53,17 @@ __device__ inline void copy16(const void* sbase, unsigned voff, unsigned lds) {
                  :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base) : "memory");
 }
 
+// The same for 4 bytes per lane: the wave's 64 dwords land contiguously at
+// `lds` (lane i at lds + 4 i).
+__device__ inline void copy4(const void* sbase, unsigned voff, unsigned lds) {
+    const unsigned long long b = (unsigned long long)sbase;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+    const void* base = (const void*)(((unsigned long long)hi << 32) | lo);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(base) : "memory");
+}
+
 // Wait until at most N (0) of this wave's vector-memory operations are in flight.
 template <int N>
 __device__ inline void wait_vm() {
