@@ -31,7 +31,8 @@ and k.
 Also printed in the same line (unless --no-also): the other workloads'
 per-kernel rates, each timed the same way, so every part of the path has a
 live number; and a CPU baseline: the fp64 oracle timed on the host cores
-on a bounded sample of the headline workload.
+on a bounded sample of the headline workload.  The attention gradients
+(attn_bwd) are timed on the shapes of workloads 2 and 3 ("backward").
 
 --calib-copy runs only a plain device copy of a known size (used to scale
 the HBM byte counters of a profiler run).
@@ -323,6 +324,42 @@ def measure_cached_steps(torch, ra, wl, dev):
     return out
 
 
+BACKWARD_WORKLOADS = (2, 3)
+
+
+def measure_backward(torch, ra, wl, dev):
+    """attn_bwd (the three gradient kernels: row statistics, dQ, dK/dV) on
+    the workloads' shapes, with the upstream gradient a seeded N(0, 1) draw
+    and o, lse from the forward on the same inputs.  FLOPs: the five matrix
+    products of the gradients (S recomputed, dP, dV, dK, dQ) over the visible
+    pairs, 10 * B * Hq * d * N_vis."""
+    out = {}
+    for key in BACKWARD_WORKLOADS:
+        w = wl.WORKLOADS[key]
+        q, k, v = (x.to(dev) for x in wl.inputs(w))
+        g = torch.Generator(device="cpu").manual_seed(w.seed + 500)
+        dO = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(w.B, w.Hq, w.Tq, dtype=torch.float32, device=dev)
+        ra.attn_fwd_ws(q, k, v, o, None, lse, scale=w.scale, causal=w.causal, q_offset=w.q_offset)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        nb = ra.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, q.dtype)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        bwd = ra.bind_attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, ws, scale=w.scale, causal=w.causal,
+                               q_offset=w.q_offset)
+        timer = Timer(torch)
+        t_est = timer(bwd, 3, 1) * 1e-3
+        ms = timer(bwd, max(10, int(0.05 / t_est)), max(5, int(0.03 / t_est)))
+        flops = 10.0 * w.B * w.Hq * w.d * n_visible(w.Tq, w.Tk, w.causal, w.q_offset)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[w.name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                       "pct_of_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 1)}
+        print(f"# backward {w.name}: {ms * 1e3:.1f} us = {tf:.1f} TFLOP/s", file=sys.stderr)
+        del q, k, v, dO, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, seconds):
     """The fp64 oracle on the host cores, on a bounded sample of workload w:
     whole passes over the workload when one pass fits the time budget, else
@@ -489,6 +526,7 @@ def main():
                   f"{r['attn_tflops']:.1f} TFLOP/s, {r['attn_gbs']:.0f} GB/s", file=sys.stderr)
         line["also"] = also
         line["cached_steps"] = measure_cached_steps(torch, ra, wl, dev)
+        line["backward"] = measure_backward(torch, ra, wl, dev)
 
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -236,27 +236,49 @@ void bwd_dq_kernel(BwdArgs a) {
         copy_step(t + 1, 1 - P);
         if (t <= last) {
             const unsigned s = base + (unsigned)(P * SLOT);
+            // d 64: all fragments read ahead of the products; d 128 reads
+            // them at the products (reading ahead there spills and measured
+            // slower)
+            constexpr bool PRE = D == 64;
+            bf16x8 ka[NQ], va[NQ], kt[NKC][NDB];
+            if constexpr (PRE) {
+#pragma unroll
+                for (int m = 0; m < NQ; ++m) {
+                    ka[m] = tl.rowfrag(s, m);
+                    va[m] = tl.rowfrag(s + TB, m);
+                }
+            }
             f32x16 st = {}, dp = {};
 #pragma unroll
             for (int m = 0; m < NQ; ++m) {
-                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(s, m), qf[m], st, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(s + TB, m), gf[m], dp, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(PRE ? ka[m] : tl.rowfrag(s, m), qf[m], st, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(PRE ? va[m] : tl.rowfrag(s + TB, m), gf[m], dp, 0, 0,
+                                                             0);
             }
-            const bool mask = (t + 1) * BN > wave_full;
-            const int lim = row_lim - (t * BN + 4 * h);
+            // K^T for the second product (independent of the softmax)
+            if constexpr (PRE) {
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                    for (int cb = 0; cb < NDB; ++cb) kt[kc][cb] = tl.trfrag(s + 2 * TB, cb, kc);
+            }
+            float p[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st[e], a.c, -Lr));
+            if ((t + 1) * BN > wave_full) {   // a tile on the diagonal or past Tk (uniform)
+                const int lim = row_lim - (t * BN + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) p[e] = row_of(e) <= lim ? p[e] : 0.f;
+            }
             bf16x8 dsb[NKC];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const bool vis = !mask || row_of(e) <= lim;
-                const float p = vis ? __builtin_amdgcn_exp2f(fmaf(st[e], a.c, -Lr)) : 0.f;
-                dsb[e >> 3][e & 7] = (bf16)(p * (dp[e] - Dv));
-            }
+            for (int e = 0; e < 16; ++e) dsb[e >> 3][e & 7] = (bf16)(p[e] * (dp[e] - Dv));
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int cb = 0; cb < NDB; ++cb)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.trfrag(s + 2 * TB, cb, kc), dsb[kc],
-                                                                      acc[cb], 0, 0, 0);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(PRE ? kt[kc][cb] : tl.trfrag(s + 2 * TB, cb, kc),
+                                                                      dsb[kc], acc[cb], 0, 0, 0);
         }
         wait_vm<0>();   // tile t + 1 has landed
         __syncthreads();
