@@ -6,8 +6,13 @@
 
 A step is one pass of the hot path over one batch of the workload's seeded
 synthetic inputs, resident in HBM before timing starts:
-    RoPE on q and k (workloads with RoPE), then the fused causal attention
-    forward (prefill), or the split-K decode step (decode workload).
+    prefill with RoPE (workloads 3, 4): one attn_fwd_rope call -- the RoPE
+    pass rotates k in place and writes the angle table, then the fused causal
+    attention rotates each query row as it loads it;
+    prefill without RoPE (workloads 1, 2): the fused causal attention;
+    decode (workload 5): RoPE on the new query row, then the split-K decode.
+For the RoPE prefills the same step as two calls (rope_apply on q and k,
+then attention) is timed beside it ("ms_per_step_rope_then_attn").
 The headline workload (default 2: bf16 B8 H12 T1024 d64, causal MHA) is timed
 for K steps between HIP events on the stream the kernels run on, after W
 warm-up steps; the JSON line reports causal-adjusted TFLOP/s.  The K steps
@@ -211,20 +216,33 @@ def setup(w, torch, ra, wl, dev):
     else:
         rope = rope_b = None
 
-    def step():
+    def step_sep():
         if rope is not None:
             rope()
         attn()
 
     if rope_b is not None:
-        def step_b():
+        def step_sep_b():
             rope_b()
             attn_b()
     else:
-        step_b = attn_b
+        step_sep_b = attn_b
+
+    step, step_b, sep_b = step_sep, step_sep_b, None
+    if w.rope and not decode:   # RoPE fused into the attention call
+        tab = torch.empty(ra.attn_fwd_rope_workspace_bytes(w.Tk, w.d), dtype=torch.uint8,
+                          device=dev)
+
+        def step():
+            ra.attn_fwd_rope(qd, kd, vd, od, scale=w.scale, causal=w.causal, q_offset=w.q_offset,
+                             base=w.rope_base, workspace=tab)
+
+        step_b = ra.bind_attn_fwd_rope(qd, kd, vd, od, tab, scale=w.scale, causal=w.causal,
+                                       q_offset=w.q_offset, base=w.rope_base)
+        sep_b = step_sep_b
 
     return dict(step=step, attn=attn, rope=rope, step_b=step_b, attn_b=attn_b, rope_b=rope_b,
-                decode=decode, q=qd, k=kd, v=vd, o=od)
+                sep_b=sep_b, decode=decode, q=qd, k=kd, v=vd, o=od)
 
 
 def measure(w, args, torch, ra, wl, dev, steps=None, warmup=None):
@@ -240,6 +258,8 @@ def measure(w, args, torch, ra, wl, dev, steps=None, warmup=None):
     ms_attn = timer(s["attn_b"], steps, warmup)
     out = dict(workload=w.name, ms_per_step=ms_step, attn_ms=ms_attn,
                timing="back-to-back launches, arguments marshalled once")
+    if s["sep_b"] is not None:
+        out["ms_per_step_rope_then_attn"] = timer(s["sep_b"], steps, warmup)
     if not args.no_graph:  # the same steps as HIP graph replays, for comparison
         graph_ok = check_graph_replay(torch, s["step"], [s["o"], s["q"], s["k"]],
                                       [s["q"], s["k"], s["v"]])
@@ -509,6 +529,7 @@ def main():
         "roofline": roof,
         "timing": head["timing"],
         "ms_per_step_graph": head.get("ms_per_step_graph"),
+        "ms_per_step_rope_then_attn": head.get("ms_per_step_rope_then_attn"),
         "graph_replay_matches_eager": head.get("graph_replay_matches_eager"),
     }
 

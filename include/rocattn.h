@@ -245,6 +245,41 @@ int attn_decode_step(void* q, const void* k_new, const void* v_new, void* k_cach
                      void* stream, void* workspace, size_t ws_bytes, float* lse);
 
 /*
+ * attn_fwd_rope -- RoPE and attention of one prefill in two launches: k is
+ * rotated in place at positions 0 .. Tk - 1 (the key rows a cache keeps,
+ * "The Transformer architecture" -- Hands-on), and the attention of
+ * attn_fwd_ws runs with each query row rotated as it is loaded, at position
+ * q_offset + i, so q stays unrotated in memory and the rotation costs no
+ * pass over q ("Transformer" (ai-notes) -- RoPE; "The Transformer
+ * architecture" -- Now: RoPE: rotate q and k, not v, before the scores).
+ * The result equals rope_apply_ex on q (at pos0 = q_offset) and k (at 0)
+ * followed by attn_fwd_ws, bit for bit.
+ *
+ *   q          [B][Hq][Tq][d_head], read only (not rotated in memory).
+ *   k          [B][Hkv][Tk][d_head], rotated in place (read, then written).
+ *   v, o, lse, scale, causal, stream   as attn_fwd_ws.
+ *   q_offset   position of query row 0 (and, with causal, the mask offset):
+ *              0 <= q_offset and q_offset + Tq <= Tk, else ERR_OFFSET.
+ *   rope_base, pairing   as rope_apply_ex.
+ *   workspace  attn_fwd_rope_workspace_bytes(Tk, d_head) bytes of device
+ *              memory, 16-byte aligned: the float32 (cos, sin) table
+ *              [Tk][d_head / 2] the key pass writes and the query load reads;
+ *              scratch afterwards.
+ * Supported: bf16 (float32 returns ERR_DTYPE), d_head in {64, 128}; every Tq
+ * runs on the prefill kernel (a one-token step is attn_decode_step's job).
+ * k may not overlap q, v, o or lse; the workspace overlaps nothing (ERR_SHAPE).
+ * Returns a rocattn_status.
+ */
+int attn_fwd_rope(const void* q, void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                  int Tq, int Tk, int d_head, float scale, int causal, int q_offset,
+                  double rope_base, int pairing, int dtype, void* stream, void* workspace,
+                  size_t ws_bytes, float* lse);
+
+/* attn_fwd_rope_workspace_bytes -- bytes of the angle table attn_fwd_rope
+ * needs: Tk * (d_head / 2) * 8 (0 for an unsupported head size). */
+size_t attn_fwd_rope_workspace_bytes(int Tk, int d_head);
+
+/*
  * attn_bwd -- gradients of attn_fwd: for an upstream gradient dO = dL/dO,
  * dq = dL/dq, dk = dL/dk, dv = dL/dv.  The pages train this operator
  * ("Transformer Math and Implementation Deep Dive" -- What To Implement:

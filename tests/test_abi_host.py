@@ -214,3 +214,32 @@ def test_bwd_workspace_bytes():
     assert lib.attn_bwd_workspace_bytes(1, 4, 2, 16, 16, 64, F32) == 0
     assert lib.attn_bwd_workspace_bytes(1, 4, 2, 16, 16, 96, BF16) == 0
     assert lib.attn_bwd_workspace_bytes(1, 6, 4, 16, 16, 64, BF16) == 0
+
+
+def fwd_rope(q=A, k=Bp, v=C, o=D, B=1, Hq=4, Hkv=2, Tq=16, Tk=16, d=64, causal=1, q_offset=0,
+             base=10000.0, pairing=0, dtype=BF16, ws=0x70000000, ws_bytes=1 << 20, lse=None):
+    return rocattn.library().attn_fwd_rope(q, k, v, o, B, Hq, Hkv, Tq, Tk, d, 0.125, causal,
+                                           q_offset, base, pairing, dtype, None, ws, ws_bytes, lse)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(dtype=F32), -3), (dict(dtype=4), -3), (dict(d=96), -4),
+    (dict(Hq=6, Hkv=4), -2), (dict(pairing=2), -2),
+    (dict(base=0.0), -6), (dict(base=float("inf")), -6),
+    (dict(q_offset=1), -5), (dict(Tq=17), -5),                 # a query position past the keys
+    (dict(causal=0, q_offset=-1), -5),
+    (dict(ws=None), -8), (dict(ws_bytes=16 * 32 * 8 - 1), -8), (dict(ws=0x70000008), -7),
+    (dict(k=A + 64), -2),                                      # k (written) overlaps q
+    (dict(ws=C + 256), -2),                                    # table overlaps v
+    (dict(o=Bp + 128), -2),                                    # o overlaps k
+])
+def test_attn_fwd_rope_rejects(kw, status):
+    assert fwd_rope(**kw) == status
+
+
+def test_attn_fwd_rope_workspace_bytes():
+    lib = rocattn.library()
+    assert lib.attn_fwd_rope_workspace_bytes(16, 64) == 16 * 32 * 8
+    assert lib.attn_fwd_rope_workspace_bytes(4096, 128) == 4096 * 64 * 8
+    assert lib.attn_fwd_rope_workspace_bytes(16, 96) == 0
+    assert lib.attn_fwd_rope_workspace_bytes(0, 64) == 0

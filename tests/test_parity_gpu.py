@@ -743,3 +743,72 @@ def test_bwd_workload2_full():
     assert np.all(np.abs(dk64.sum(axis=2)) <= bound_k)
     bound_v = 2.0 ** -8 * (np.abs(dv64).sum(axis=2) + np.abs(dO64).sum(axis=2)) + 1e-3
     assert np.all(np.abs(dv64.sum(axis=2) - dO64.sum(axis=2)) <= bound_v)
+
+
+# ---- RoPE fused into the attention: attn_fwd_rope rotates k in place and
+#      each query row as the kernel loads it
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tk,d,causal,qo,pairing", [
+    (2, 8, 2, 300, 300, 64, True, 0, "split"),
+    (1, 8, 2, 300, 300, 128, True, 0, "adjacent"),
+    (1, 16, 4, 129, 1000, 128, True, 871, "split"),       # a chunk at the end of a context
+    (2, 4, 4, 200, 200, 64, True, 0, "adjacent"),
+    (1, 4, 2, 70, 333, 64, False, 50, "split"),           # no mask: positions still q_offset + i
+])
+def test_attn_fwd_rope_equals_rope_then_attention_bit_exact(B, Hq, Hkv, Tq, Tk, d, causal, qo,
+                                                            pairing):
+    """One attn_fwd_rope call gives the same bits as rope_apply_ex on q (at
+    pos0 = q_offset) and on k (at 0) followed by attn_fwd_ws, leaves q as it
+    was and k rotated exactly as rope_apply_ex rotates it; and it agrees with
+    the oracle's RoPE followed by its attention."""
+    say("attn_fwd_rope", B, Hq, Hkv, Tq, Tk, d, causal, qo, pairing)
+    q, k, v = wl.random_qkv(B, Hq, Hkv, Tq, Tk, d, torch.bfloat16, seed=300 + Tq)
+    scale = d ** -0.5
+    qd, kd, vd = gpu(q, k, v)
+    lse1 = torch.empty(B, Hq, Tq, dtype=torch.float32, device=DEV)
+    o1 = ra.attn_fwd_rope(qd, kd, vd, scale=scale, causal=causal, q_offset=qo, pairing=pairing,
+                          lse=lse1)
+    q2, k2 = gpu(q, k)
+    ra.rope_apply(q2, None, pos0=qo, pairing=pairing)
+    ra.rope_apply(k2, None, pos0=0, pairing=pairing)
+    o2 = torch.empty_like(q2)
+    lse2 = torch.empty_like(lse1)
+    ra.attn_fwd_ws(q2, k2, vd, o2, None, lse2, scale=scale, causal=causal, q_offset=qo)
+    torch.cuda.synchronize()
+    assert torch.equal(qd.cpu(), q)
+    assert torch.equal(kd, k2)
+    assert torch.equal(o1, o2)
+    assert torch.equal(lse1, lse2)
+    want = oracle.attn(oracle.rope(q, pos0=qo, pairing=pairing), oracle.rope(k, pos0=0, pairing=pairing),
+                       v, scale, causal=causal, q_offset=qo)
+    err = float(np.max(np.abs(f64(o1) - want)))
+    assert err <= TOL[torch.bfloat16], err
+
+
+def test_attn_fwd_rope_one_row_matches_oracle():
+    """Tq = 1 runs on the prefill kernel with the query-load rotation."""
+    say("attn_fwd_rope Tq=1")
+    B, Hq, Hkv, Tk, d = 4, 32, 8, 777, 128
+    q, k, v = wl.random_qkv(B, Hq, Hkv, 1, Tk, d, torch.bfloat16, seed=77)
+    qd, kd, vd = gpu(q, k, v)
+    o = ra.attn_fwd_rope(qd, kd, vd, scale=0.0884, q_offset=Tk - 1)
+    torch.cuda.synchronize()
+    want = oracle.attn(oracle.rope(q, pos0=Tk - 1), oracle.rope(k, pos0=0), v, 0.0884,
+                       q_offset=Tk - 1)
+    err = float(np.max(np.abs(f64(o) - want)))
+    assert err <= TOL[torch.bfloat16], err
+
+
+def test_attn_fwd_rope_workload3_full():
+    """The GQA + RoPE prefill of workload 3 through the fused entry, against
+    the oracle on the whole output."""
+    w = wl.WORKLOADS[3]
+    say("attn_fwd_rope", w.name)
+    q, k, v = wl.inputs(w)
+    qd, kd, vd = gpu(q, k, v)
+    o = ra.attn_fwd_rope(qd, kd, vd, scale=w.scale, causal=True, q_offset=0, base=w.rope_base)
+    torch.cuda.synchronize()
+    want = oracle.attn(oracle.rope(q, pos0=0, base=w.rope_base), oracle.rope(k, pos0=0, base=w.rope_base),
+                       v, w.scale)
+    err = float(np.max(np.abs(f64(o) - want)))
+    assert err <= TOL[torch.bfloat16], err

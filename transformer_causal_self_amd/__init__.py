@@ -16,9 +16,10 @@ or a call is made with CPU tensors, the call raises.
     status_string(code)
     attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o=None, scale=None,
                      base=10000.0, pairing="split", workspace=None, lse=None)
+    attn_fwd_rope(q, k, v, o=None, ..., base=10000.0, pairing="split") -> o
     attn_bwd(q, k, v, o, dO, lse, scale=None, causal=True, q_offset=0) -> (dq, dk, dv)
     bind_attn_fwd_ws(...), bind_rope_apply(...), bind_attn_decode_step(...),
-    bind_attn_bwd(...) -> Bound
+    bind_attn_fwd_rope(...), bind_attn_bwd(...) -> Bound
 
 A Bound is one of these calls with its arguments checked and marshalled
 once: calling it launches the same work again on the stream it was bound
@@ -36,7 +37,8 @@ LIBRARY = os.path.join(HERE, "librocattn.so")
 
 # the C ABI, as declared in include/rocattn.h
 SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_strided", "attn_workspace_bytes",
-           "rope_apply", "rope_apply_ex", "attn_decode_step", "attn_bwd",
+           "rope_apply", "rope_apply_ex", "attn_decode_step", "attn_fwd_rope",
+           "attn_fwd_rope_workspace_bytes", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_status_string")
 
 F32, BF16 = 0, 1
@@ -83,6 +85,11 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_step.restype = i
         lib.attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
                                          ctypes.c_double, i, i, vp, vp, sz, vp]
+        lib.attn_fwd_rope.restype = i
+        lib.attn_fwd_rope.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, ctypes.c_double, i,
+                                      i, vp, vp, sz, vp]
+        lib.attn_fwd_rope_workspace_bytes.restype = sz
+        lib.attn_fwd_rope_workspace_bytes.argtypes = [i, i]
         lib.attn_bwd.restype = i
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
                                  i, vp, vp, sz]
@@ -328,6 +335,52 @@ def bind_attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o, scale=None,
     returned Bound repeats the step (rotating q in place again)."""
     return _decode_step_call(q, k_new, v_new, k_cache, v_cache, pos, o, scale, base, pairing,
                              workspace, lse, stream)
+
+
+def attn_fwd_rope_workspace_bytes(Tk, d_head) -> int:
+    return int(library().attn_fwd_rope_workspace_bytes(Tk, d_head))
+
+
+def _fwd_rope_call(q, k, v, o, workspace, lse, scale, causal, q_offset, base, pairing, stream):
+    import torch
+    if pairing not in PAIRING:
+        raise ValueError(f"pairing must be one of {sorted(PAIRING)}")
+    B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt = _fwd_args(q, k, v, o, scale, causal, q_offset)
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be dense [B, H, T, d] (contiguous)")
+    _check_dev("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, Hq, Tq):
+            raise ValueError("lse must be [B, Hq, Tq]")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, float(base),
+            PAIRING[pairing], dt, _stream(q, stream), _ptr(workspace), ws_bytes, _ptr(lse))
+    return Bound("attn_fwd_rope", library().attn_fwd_rope, args, (q, k, v, o, workspace, lse))
+
+
+def attn_fwd_rope(q, k, v, o=None, scale=None, causal=True, q_offset=0, base=10000.0,
+                  pairing="split", workspace=None, lse=None, stream=None):
+    """Rotate k in place at positions 0.., then attention with each query row
+    rotated at load (position q_offset + i; q itself is left unrotated);
+    returns o.  The angle-table workspace is allocated here when not given."""
+    import torch
+    if o is None:
+        o = torch.empty_like(q)
+    if workspace is None:
+        nb = attn_fwd_rope_workspace_bytes(k.shape[2], q.shape[3])
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    _fwd_rope_call(q, k, v, o, workspace, lse, scale, causal, q_offset, base, pairing, stream)()
+    return o
+
+
+def bind_attn_fwd_rope(q, k, v, o, workspace, lse=None, scale=None, causal=True, q_offset=0,
+                       base=10000.0, pairing="split", stream=None) -> Bound:
+    """attn_fwd_rope's checks and marshalling now; each call of the returned
+    Bound repeats it (rotating k in place again)."""
+    return _fwd_rope_call(q, k, v, o, workspace, lse, scale, causal, q_offset, base, pairing,
+                          stream)
 
 
 def _bwd_call(q, k, v, o, dO, lse, dq, dk, dv, workspace, scale, causal, q_offset, stream):

@@ -369,6 +369,51 @@ ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, 
     return launch(p, dtype, s, workspace, ws_bytes);
 }
 
+ROCATTN_API size_t attn_fwd_rope_workspace_bytes(int Tk, int d_head) {
+    if (Tk <= 0 || (d_head != 64 && d_head != 128)) return 0;
+    return (size_t)Tk * (size_t)(d_head / 2) * 2 * sizeof(float);
+}
+
+ROCATTN_API int attn_fwd_rope(const void* q, void* k, const void* v, void* o, int B, int Hq,
+                              int Hkv, int Tq, int Tk, int d_head, float scale, int causal,
+                              int q_offset, double rope_base, int pairing, int dtype, void* stream,
+                              void* workspace, size_t ws_bytes, float* lse) {
+    if (dtype != ROCATTN_F32 && dtype != ROCATTN_BF16) return ROCATTN_ERR_DTYPE;
+    if (dtype != ROCATTN_BF16) return ROCATTN_ERR_DTYPE;   // the query-load rotation is bf16
+    const int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d_head, scale, causal, q_offset,
+                             dtype, lse);
+    if (st != ROCATTN_OK) return st;
+    if (pairing != ROCATTN_ROPE_SPLIT_HALF && pairing != ROCATTN_ROPE_ADJACENT) return ROCATTN_ERR_SHAPE;
+    if (!(rope_base > 0.0) || !isfinite(rope_base)) return ROCATTN_ERR_SCALE;
+    // query row i sits at position q_offset + i, key row j at j: every
+    // query position must have a key row (the table covers [0, Tk))
+    if (q_offset < 0 || (long long)q_offset + Tq > Tk) return ROCATTN_ERR_OFFSET;
+    const size_t tb = attn_fwd_rope_workspace_bytes(Tk, d_head);
+    if (!workspace || ws_bytes < tb) return ROCATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ROCATTN_ERR_ALIGN;
+    const size_t qb = (size_t)count4(B, Hq, Tq, d_head) * 2, kvb = (size_t)count4(B, Hkv, Tk, d_head) * 2;
+    const size_t lb = lse ? (size_t)B * Hq * Tq * sizeof(float) : 0;
+    // k is rotated in place: it shares no byte with q or v (o and lse were
+    // checked against it); the table shares none with any operand
+    if (overlaps(k, kvb, q, qb) || overlaps(k, kvb, v, kvb)) return ROCATTN_ERR_SHAPE;
+    if (overlaps(workspace, tb, q, qb) || overlaps(workspace, tb, k, kvb) ||
+        overlaps(workspace, tb, v, kvb) || overlaps(workspace, tb, o, qb) ||
+        (lse && overlaps(workspace, tb, lse, lb)))
+        return ROCATTN_ERR_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* tab = static_cast<float*>(workspace);
+    hipError_t e = rocattn::launch_rope_table(tab, Tk, d_head, 0, rope_base, s);
+    if (e == hipSuccess)
+        e = rocattn::launch_rope(k, (long long)B * Hkv, Tk, d_head, 0, rope_base, dtype, pairing, s, tab);
+    if (e != hipSuccess) return ROCATTN_ERR_HIP;
+    FwdParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d_head, scale, causal, q_offset);
+    p.rope_tab = tab;
+    p.rope_adj = pairing;
+    p.rope_pos0 = q_offset;
+    // the prefill kernel for every Tq (the split-K decode kernels do not rotate)
+    return rocattn::launch_prefill_bf16(p, s) == hipSuccess ? ROCATTN_OK : ROCATTN_ERR_HIP;
+}
+
 ROCATTN_API size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d_head,
                                             int dtype) {
     if (dtype != ROCATTN_BF16) return 0;

@@ -57,6 +57,7 @@
 
 #include "internal.hpp"
 #include "mfma_tiles.hpp"
+#include "rope_math.hpp"
 
 namespace rocattn {
 namespace {
@@ -103,7 +104,56 @@ struct Args {
     // element strides between batches and heads, and (32-bit) between tokens
     long long qsb, qsh, ksb, ksh, vsb, vsh, osb, osh;
     int qst, kst, vst, ost;
+    // RoPE of q at load: (cos, sin) table [position][D/2] or null; query row
+    // i at position rope_pos0 + i; rope_adj picks the channel pairing
+    const float2* rope;
+    int rope_adj, rope_pos0;
 };
+
+// RoPE of a lane's query fragments (channels 16m + 8h .. +7 of one row)
+// from the row's (cos, sin) table entries: the turn in float32, rounded once
+// to bf16 -- the same arithmetic as the RoPE pass.  Split-half pair
+// p = (p, p + D/2) joins fragment m with fragment m + D/32 (entries
+// 16m + 8h .. +7); adjacent pair p = (2p, 2p + 1) lies inside fragment m
+// (entries 8m + 4h .. +3).  Entries are loaded per fragment and used at
+// once (loading all of them ahead spills at d = 128 and measured no faster).
+template <int D>
+__device__ inline void rope_q_frags(bf16x8 (&f)[D / 16], const float2* tab, int adj, int h) {
+    constexpr int NQ = D / 16;
+    float y1, y2;
+    if (!adj) {
+#pragma unroll
+        for (int m = 0; m < NQ / 2; ++m) {
+            float4 t[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] = reinterpret_cast<const float4*>(tab + 16 * m + 8 * h)[i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float4 x = t[j / 2];
+                const float c = (j & 1) ? x.z : x.x, sn = (j & 1) ? x.w : x.y;
+                rope_turn((float)f[m][j], (float)f[m + NQ / 2][j], c, sn, y1, y2);
+                f[m][j] = (bf16)y1;
+                f[m + NQ / 2][j] = (bf16)y2;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            float4 t[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) t[i] = reinterpret_cast<const float4*>(tab + 8 * m + 4 * h)[i];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                rope_turn((float)f[m][4 * i], (float)f[m][4 * i + 1], t[i].x, t[i].y, y1, y2);
+                f[m][4 * i] = (bf16)y1;
+                f[m][4 * i + 1] = (bf16)y2;
+                rope_turn((float)f[m][4 * i + 2], (float)f[m][4 * i + 3], t[i].z, t[i].w, y1, y2);
+                f[m][4 * i + 2] = (bf16)y1;
+                f[m][4 * i + 3] = (bf16)y2;
+            }
+        }
+    }
+}
 
 template <int D>
 struct Scores {
@@ -112,7 +162,8 @@ struct Scores {
 
 // DENSE: q, k, v and o are dense [B][H][T][D], so every token stride is the
 // compile-time D (the strided instantiation reads the strides from Args).
-template <int D, bool DENSE>
+// ROPE: the query rows are turned by RoPE at load (a.rope holds the table).
+template <int D, bool DENSE, bool ROPE>
 __global__ __launch_bounds__(Cfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(Cfg<D>::WPE, Cfg<D>::WPE)))
 void prefill_kernel(Args a) {
     typedef Cfg<D> C;
@@ -162,7 +213,8 @@ void prefill_kernel(Args a) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) iq[rb] = i0w + 32 * rb + li;
 
-    // ---- Q fragments (B operand): lane holds q[iq[rb]][16m + 8h .. +7]
+    // ---- Q fragments (B operand): lane holds q[iq[rb]][16m + 8h .. +7],
+    //      turned by RoPE at position rope_pos0 + iq[rb] when a table is given
     bf16x8 qf[RB][NQ];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -173,6 +225,13 @@ void prefill_kernel(Args a) {
         for (int m = 0; m < NQ; ++m) {
             uint4 u = src[2 * m];
             if (iq[rb] >= a.Tq) u = make_uint4(0, 0, 0, 0);
+            qf[rb][m] = __builtin_bit_cast(bf16x8, u);
+        }
+        if constexpr (ROPE)
+            rope_q_frags<D>(qf[rb], a.rope + (size_t)(a.rope_pos0 + row) * (D / 2), a.rope_adj, h);
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+            uint4 u = __builtin_bit_cast(uint4, qf[rb][m]);
             u.x ^= a.neg; u.y ^= a.neg; u.z ^= a.neg; u.w ^= a.neg;
             qf[rb][m] = __builtin_bit_cast(bf16x8, u);
         }
@@ -459,11 +518,18 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     a.ksb = p.ks.b; a.ksh = p.ks.h; a.kst = (int)p.ks.t;
     a.vsb = p.vs.b; a.vsh = p.vs.h; a.vst = (int)p.vs.t;
     a.osb = p.os.b; a.osh = p.os.h; a.ost = (int)p.os.t;
+    a.rope = reinterpret_cast<const float2*>(p.rope_tab);
+    a.rope_adj = p.rope_adj;
+    a.rope_pos0 = p.rope_pos0;
     const long long nwg = (long long)a.n_qt * a.G * a.R;
-    if (dense)
-        hipLaunchKernelGGL((prefill_kernel<D, true>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL((prefill_kernel<D, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
+    if (p.rope_tab) {   // dense layouts only (the fused-RoPE entry takes dense tensors)
+        if (!dense) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((prefill_kernel<D, true, true>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
+    } else if (dense) {
+        hipLaunchKernelGGL((prefill_kernel<D, true, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((prefill_kernel<D, false, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -36,6 +36,11 @@ struct FwdParams {
     int causal;
     int q_offset;
     Strides qs, ks, vs, os;
+    // RoPE of the query rows at load (bf16 prefill only): float32 (cos, sin)
+    // pairs [position][d/2]; query row i sits at position rope_pos0 + i
+    const float* rope_tab = nullptr;
+    int rope_adj = 0;      // 0: split-half pairs (p, p + d/2); 1: adjacent (2p, 2p + 1)
+    int rope_pos0 = 0;
 };
 
 // Prefill (any Tq) bf16 MFMA kernel, d in {64, 128}: four-wave workgroups of
@@ -54,8 +59,15 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 // RoPE in place; dtype 0 = f32, 1 = bf16; pairing 0 = split-half, 1 =
 // adjacent.  x holds n_seq sequences of T rows of d elements ([n_seq][T][d])
 // with token t at position pos0 + t.
+// tab (optional): float32 (cos, sin) [position][d/2] covering positions
+// pos0 .. pos0 + T - 1, read instead of forming the angles per lane.
 hipError_t launch_rope(void* x, long long n_seq, int T, int d, int pos0, double base,
-                       int dtype, int pairing, hipStream_t stream);
+                       int dtype, int pairing, hipStream_t stream, const float* tab = nullptr);
+
+// The table launch_rope and the prefill kernel's query load read: the
+// float32 (cos, sin) of every pair at positions pos0 .. pos0 + T - 1, formed
+// in double precision exactly as the RoPE pass forms them.
+hipError_t launch_rope_table(float* tab, int T, int d, int pos0, double base, hipStream_t stream);
 
 // Everything a backward launch needs (dense [B][H][T][d] tensors), validated
 // by the host API.

@@ -8,16 +8,20 @@
 // theta_p = pos * base^(-2p/d) ("Transformer" (ai-notes) -- RoPE) through
 // [[cos, -sin], [sin, cos]].
 //
-// The angle table is not stored in HBM: each lane forms, in double
-// precision, the cosine and sine of the few pairs it owns at one position,
-// rounds them once to float32, and then rotates that (position, pairs) slot
-// in every head and batch entry of its share.  The work is HBM-bound
+// Angles: each lane forms, in double precision, the cosine and sine of the
+// few pairs it owns at one position, rounds them once to float32, and then
+// rotates that (position, pairs) slot in every head and batch entry of its
+// share -- or, when a table [position][d/2] of those float32 (cos, sin)
+// values is given (rope_table_kernel writes it with the same arithmetic),
+// reads them from it.  The double-precision cosine and sine cost a few
+// hundred instructions each, so without a table a lane keeps many rows.  The work is HBM-bound
 // (one read and one write of q and k); each lane moves 2 x 8 bytes (bf16) or
 // 2 x 16 bytes (f32) per head row, with neighbouring lanes on neighbouring
 // pairs so every head row is read and written by full, coalesced segments.
 #include <math.h>
 
 #include "internal.hpp"
+#include "rope_math.hpp"
 
 namespace rocattn {
 namespace {
@@ -50,7 +54,8 @@ __device__ inline void store_f32(T* dst, const float* f) {
 template <typename T, int kPairs, bool ADJ>  // kPairs channel pairs per lane
 __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long long n_seq,
                                                         int rows_per_chunk, int T_len, int d,
-                                                        int pos0, double neg_log2_base_over_half) {
+                                                        int pos0, double neg_log2_base_over_half,
+                                                        const float2* __restrict__ tab) {
     const int half = d >> 1;
     const int groups = half / kPairs;  // lanes per token
     const long long slot = (long long)blockIdx.x * kThreads + threadIdx.x;
@@ -59,15 +64,24 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long 
     const int p0 = (int)(slot - (long long)t * groups) * kPairs;
 
     float cs[kPairs], sn[kPairs];
-    const double pos = (double)pos0 + (double)t;
+    if (tab) {
+        const float2* row = tab + (size_t)(pos0 + t) * half + p0;
 #pragma unroll
-    for (int u = 0; u < kPairs; ++u) {
-        // base^(-2p/d) = 2^(-(p / (d/2)) * log2(base))
-        const double inv_freq = exp2((double)(p0 + u) * neg_log2_base_over_half);
-        double s, c;
-        sincos(pos * inv_freq, &s, &c);
-        cs[u] = (float)c;
-        sn[u] = (float)s;
+        for (int u = 0; u < kPairs; ++u) {
+            cs[u] = row[u].x;
+            sn[u] = row[u].y;
+        }
+    } else {
+        const double pos = (double)pos0 + (double)t;
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u) {
+            // base^(-2p/d) = 2^(-(p / (d/2)) * log2(base))
+            const double inv_freq = exp2((double)(p0 + u) * neg_log2_base_over_half);
+            double s, c;
+            sincos(pos * inv_freq, &s, &c);
+            cs[u] = (float)c;
+            sn[u] = (float)s;
+        }
     }
 
     const long long r0 = (long long)blockIdx.y * rows_per_chunk;
@@ -86,23 +100,41 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long 
 #pragma unroll
         for (int u = 0; u < kPairs; ++u) {
             const int i1 = ADJ ? 2 * u : u, i2 = ADJ ? 2 * u + 1 : u + kPairs;
-            y[i1] = e[i1] * cs[u] - e[i2] * sn[u];
-            y[i2] = e[i1] * sn[u] + e[i2] * cs[u];
+            rope_turn(e[i1], e[i2], cs[u], sn[u], y[i1], y[i2]);
         }
         store_f32<T, kPairs>(lo, y);
         store_f32<T, kPairs>(hi, y + kPairs);
     }
 }
 
+// The float32 (cos, sin) of pair p at position pos0 + t, for t < T_len and
+// every pair, into tab[pos0 + t][p]: the arithmetic of rope_kernel's own
+// angles, once per (position, pair).
+__global__ __launch_bounds__(kThreads) void rope_table_kernel(float2* __restrict__ tab, int T_len,
+                                                              int half, int pos0,
+                                                              double neg_log2_base_over_half) {
+    const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (long long)T_len * half) return;
+    const int t = (int)(i / half), p = (int)(i - (long long)t * half);
+    const double pos = (double)pos0 + (double)t;
+    const double inv_freq = exp2((double)p * neg_log2_base_over_half);
+    double s, c;
+    sincos(pos * inv_freq, &s, &c);
+    tab[(size_t)(pos0 + t) * half + p] = make_float2((float)c, (float)s);
+}
+
 template <typename T, int kPairs>
 hipError_t launch_rope_t(T* x, long long n_seq, int T_len, int d, int pos0, double base,
-                         int pairing, hipStream_t stream) {
+                         int pairing, hipStream_t stream, const float* tab) {
     const int half = d / 2;
     const int groups = half / kPairs;
     const long long slots = (long long)T_len * groups;
     const long long gx = (slots + kThreads - 1) / kThreads;
-    // split the head rows so the launch has enough workgroups to fill the chip
+    // split the head rows so the launch has enough workgroups to fill the
+    // chip; without a table each chunk forms its own cosines and sines, so
+    // the chunks are capped at 2^17 / slots (at most 2^17 lanes' worth)
     long long gy = (2048 + gx - 1) / gx;
+    if (!tab && gy > (1LL << 17) / slots) gy = (1LL << 17) / slots;
     if (gy > n_seq) gy = n_seq;
     if (gy < 1) gy = 1;
     const int rows_per_chunk = (int)((n_seq + gy - 1) / gy);
@@ -111,25 +143,34 @@ hipError_t launch_rope_t(T* x, long long n_seq, int T_len, int d, int pos0, doub
     dim3 grid((unsigned)gx, (unsigned)gy);
     if (pairing)
         hipLaunchKernelGGL((rope_kernel<T, kPairs, true>), grid, dim3(kThreads), 0, stream,
-                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg);
+                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg, reinterpret_cast<const float2*>(tab));
     else
         hipLaunchKernelGGL((rope_kernel<T, kPairs, false>), grid, dim3(kThreads), 0, stream,
-                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg);
+                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg, reinterpret_cast<const float2*>(tab));
     return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_rope_table(float* tab, int T_len, int d, int pos0, double base,
+                             hipStream_t stream) {
+    const int half = d / 2;
+    const long long n = (long long)T_len * half;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, reinterpret_cast<float2*>(tab), T_len, half, pos0, -log2(base) / (double)half);
+    return hipGetLastError();
+}
+
 hipError_t launch_rope(void* x, long long n_seq, int T_len, int d, int pos0, double base,
-                       int dtype, int pairing, hipStream_t stream) {
+                       int dtype, int pairing, hipStream_t stream, const float* tab) {
     // four pairs per lane (8-byte bf16 / 16-byte f32 accesses) when the half
     // head size allows it, else one pair per lane
     const bool wide = (d / 2) % 4 == 0;
     if (dtype == 0)
-        return wide ? launch_rope_t<float, 4>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, pairing, stream)
-                    : launch_rope_t<float, 1>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, pairing, stream);
-    return wide ? launch_rope_t<bf16, 4>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, pairing, stream)
-                : launch_rope_t<bf16, 1>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, pairing, stream);
+        return wide ? launch_rope_t<float, 4>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, pairing, stream, tab)
+                    : launch_rope_t<float, 1>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, pairing, stream, tab);
+    return wide ? launch_rope_t<bf16, 4>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, pairing, stream, tab)
+                : launch_rope_t<bf16, 1>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, pairing, stream, tab);
 }
 
 
@@ -205,8 +246,7 @@ __global__ __launch_bounds__(kThreads) void step_prep_kernel(PrepArgs a) {
 #pragma unroll
             for (int u = 0; u < kPairs; ++u) {
                 const int i1 = ADJ ? 2 * u : u, i2 = ADJ ? 2 * u + 1 : u + kPairs;
-                y[i1] = e[i1] * cs[u] - e[i2] * sn[u];
-                y[i2] = e[i1] * sn[u] + e[i2] * cs[u];
+                rope_turn(e[i1], e[i2], cs[u], sn[u], y[i1], y[i2]);
             }
         } else {
 #pragma unroll
