@@ -11,6 +11,7 @@ Functions (each cites its passage in ``attn_oracle.c``):
     attn(q, k, v, scale, causal=True, q_offset=0, return_lse=False)
     attn_rows(q, k, v, rows, scale, causal=True, q_offset=0)
     rope(x, pos0=0, base=10000.0, pairing="split")
+    rope_table(T, d, pos0=0, base=10000.0) -> float32 [T, d/2, 2] (cos, sin)
     attn_bwd(q, k, v, dO, scale, causal=True, q_offset=0) -> (dq, dk, dv)
     decode_step(q, k_new, v_new, k_cache, v_cache, pos, scale, base=10000.0,
                 pairing="split")   (a composition of rope and attn)
@@ -76,6 +77,8 @@ class Oracle:
         lib.oracle_attn_bwd.restype = ctypes.c_int
         lib.oracle_attn_bwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, _L, _L, _L, _L, _L, _L,
                                         ctypes.c_double, ctypes.c_int, _L]
+        lib.oracle_rope_table.restype = ctypes.c_int
+        lib.oracle_rope_table.argtypes = [ctypes.POINTER(ctypes.c_float), _L, _L, _L, ctypes.c_double]
         lib.oracle_rope.restype = ctypes.c_int
         lib.oracle_rope.argtypes = [_D, _L, _L, _L, _L, _L, ctypes.c_double, ctypes.c_int]
         self._lib = lib
@@ -148,6 +151,15 @@ class Oracle:
             raise ValueError(f"oracle_rope rejected its arguments (status {st})")
         return y
 
+    def rope_table(self, T: int, d: int, pos0: int = 0, base: float = 10000.0):
+        """float32 [T, d/2, 2]: (cos, sin) of pair p at position pos0 + t."""
+        out = np.zeros((T, d // 2, 2), dtype=np.float32)
+        st = self._lib.oracle_rope_table(out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), T, d,
+                                         int(pos0), float(base))
+        if st != 0:
+            raise ValueError(f"oracle_rope_table rejected its arguments (status {st})")
+        return out
+
     def decode_step(self, q, k_new, v_new, k_cache, v_cache, pos, scale, base=10000.0,
                     pairing="split"):
         """One cached generation step, as "The Transformer architecture" --
@@ -199,6 +211,10 @@ def attn_rows(*args, **kwargs):
 
 def rope(*args, **kwargs):
     return default().rope(*args, **kwargs)
+
+
+def rope_table(*args, **kwargs):
+    return default().rope_table(*args, **kwargs)
 
 
 def attn_bwd(*args, **kwargs):

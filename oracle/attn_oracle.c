@@ -32,9 +32,9 @@
 #include <stdlib.h>
 
 /* Query head hq reads key/value head hq / (Hq / Hkv): contiguous groups of
- * n_rep = Hq / Hkv query heads share one K/V head [P1 Attention Shapes: "the
- * implementation repeats or maps KV heads across query head groups"; P2 GQA:
- * "each group of n_rep query heads share one set of K/V heads"]. */
+ * n_rep = Hq / Hkv query heads share one K/V head [P1 Attention Shapes: the
+ * K/V heads are repeated or mapped over groups of query heads; P2 GQA: a
+ * group of n_rep consecutive query heads reads a single K/V head]. */
 static long kv_head_of(long hq, long Hq, long Hkv) { return hq / (Hq / Hkv); }
 
 /* Last key a query row may read.  Causal: key j is visible to query row i
@@ -265,7 +265,7 @@ int oracle_attn_rows(const double* q, const double* k, const double* v,
 /* Rotary position embedding, in place on x[B][H][T][d].
  *
  * Token t sits at absolute position pos = pos0 + t (pos0 = cache.pos for a
- * cached step [P2 Hands-on: "RoPE is sliced from cache.pos too"]).  Channel
+ * cached step [P2 Hands-on: the RoPE angles are taken from cache.pos onward]).  Channel
  * pair p (p = 0 .. d/2 - 1) turns by the angle
  *     theta_p(pos) = pos * base^(-2p/d)
  * [P4 RoPE: theta_i(pos) = pos * 10000^(-2i/d_head)], through the 2x2
@@ -299,6 +299,28 @@ int oracle_rope(double* x, long B, long H, long T, long d, long pos0,
             double x1 = xr[a], x2 = xr[b2];
             xr[a] = x1 * cs - x2 * sn;
             xr[b2] = x1 * sn + x2 * cs;
+        }
+    }
+    return 0;
+}
+
+/* RoPE angle table: for positions pos0 .. pos0 + T - 1 and pairs
+ * p = 0 .. d/2 - 1, the cosine and sine of theta_p(pos) = pos * base^(-2p/d)
+ * [P4 RoPE], taken in double precision exactly as oracle_rope takes them and
+ * then rounded once to float32 (the precision the rotation tables are stored
+ * in).  out: float [T][d/2][2], (cos, sin).  Returns -4 for an odd d, -2 for
+ * other bad sizes, -6 for a bad base. */
+int oracle_rope_table(float* out, long T, long d, long pos0, double base) {
+    if (T <= 0 || d <= 0 || pos0 < 0) return -2;
+    if (d % 2 != 0) return -4;
+    if (!(base > 0.0) || !isfinite(base)) return -6;
+    const long half = d / 2;
+    for (long t = 0; t < T; ++t) {
+        const double position = (double)(pos0 + t);
+        for (long p = 0; p < half; ++p) {
+            const double theta = position * pow(base, -(2.0 * (double)p) / (double)d);
+            out[(t * half + p) * 2 + 0] = (float)cos(theta);
+            out[(t * half + p) * 2 + 1] = (float)sin(theta);
         }
     }
     return 0;

@@ -439,6 +439,38 @@ def pin_rope_then_attention_relative(orc):
     assert np.max(np.abs(o1 - o2)) < 1e-10
 
 
+def pin_rope_table(orc):
+    """The float32 angle table: position 0 turns nothing (cos 1, sin 0 for
+    every pair); pair 0 turns by the position itself (base^0 = 1), so
+    position 1 holds (cos 1, sin 1) and position 2 the double-angle values;
+    every entry lies on the unit circle to float32 rounding; a table that
+    starts at pos0 is the slice of one that starts at 0 (RoPE sliced from
+    cache.pos, "The Transformer architecture" -- Hands-on); and turning
+    vectors with the table's entries gives what the oracle's RoPE (its own
+    double-precision angles) gives, to the table's float32 rounding."""
+    d = 64
+    tab = orc.rope_table(300, d, 0, 10000.0)
+    assert np.all(tab[0, :, 0] == 1.0) and np.all(tab[0, :, 1] == 0.0)
+    # cos 1 = 0.5403023058681398, sin 1 = 0.8414709848078965;
+    # cos 2 = 2 cos^2 1 - 1, sin 2 = 2 sin 1 cos 1
+    c1, s1 = 0.5403023058681398, 0.8414709848078965
+    assert tab[1, 0, 0] == np.float32(c1) and tab[1, 0, 1] == np.float32(s1)
+    assert abs(float(tab[2, 0, 0]) - (2 * c1 * c1 - 1)) < 1e-7
+    assert abs(float(tab[2, 0, 1]) - 2 * s1 * c1) < 1e-7
+    norm = tab[..., 0].astype(np.float64) ** 2 + tab[..., 1].astype(np.float64) ** 2
+    assert np.max(np.abs(norm - 1.0)) < 3e-7
+    assert np.array_equal(orc.rope_table(100, d, 200, 10000.0), tab[200:300])
+    # rotation with the table against the oracle's RoPE
+    x = np.random.default_rng(5).standard_normal((1, 1, 300, d))
+    want = orc.rope(x, pos0=0)
+    c = tab[..., 0].astype(np.float64)[None, None]
+    sn = tab[..., 1].astype(np.float64)[None, None]
+    x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    got = np.concatenate([x1 * c - x2 * sn, x1 * sn + x2 * c], axis=-1)
+    assert np.max(np.abs(got - want)) < 1e-6
+    assert np.max(np.abs(got - want)) > 0.0   # the table is float32, the oracle's angles are not
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]
 
 

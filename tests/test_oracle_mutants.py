@@ -42,6 +42,14 @@ MUTANTS = {
     "rope_ignores_pos0": [("double pos = (double)(pos0 + t);", "double pos = (double)t;")],
     "rope_sin_cos_swapped": [("double cs = cos(theta), sn = sin(theta);",
                               "double cs = sin(theta), sn = cos(theta);")],
+    "rope_table_cos_sin_swapped": [("out[(t * half + p) * 2 + 0] = (float)cos(theta);",
+                                    "out[(t * half + p) * 2 + 0] = (float)sin(theta);"),
+                                   ("out[(t * half + p) * 2 + 1] = (float)sin(theta);",
+                                    "out[(t * half + p) * 2 + 1] = (float)cos(theta);")],
+    "rope_table_frequency_index_shifted": [("pow(base, -(2.0 * (double)p) / (double)d)",
+                                            "pow(base, -(2.0 * (double)(p + 1)) / (double)d)")],
+    "rope_table_ignores_pos0": [("const double position = (double)(pos0 + t);",
+                                 "const double position = (double)t;")],
     "rope_split_half_uses_adjacent_pairs": [
         ("long a = pairing == 0 ? p : 2 * p;", "long a = 2 * p;"),
         ("long b2 = pairing == 0 ? p + half : 2 * p + 1;", "long b2 = 2 * p + 1;")],

@@ -812,3 +812,23 @@ def test_attn_fwd_rope_workload3_full():
                        v, w.scale)
     err = float(np.max(np.abs(f64(o) - want)))
     assert err <= TOL[torch.bfloat16], err
+
+
+@pytest.mark.parametrize("Tk,d,base", [(4096, 128, 10000.0), (1024, 64, 10000.0), (16384, 128, 500000.0)])
+def test_rope_angle_table_matches_oracle(Tk, d, base):
+    """The float32 (cos, sin) table attn_fwd_rope leaves in its workspace:
+    every entry within one float32 ulp of the oracle's (double-precision
+    angle, cosine and sine, rounded once), almost all of them equal."""
+    say("rope table", Tk, d, base)
+    q, k, v = wl.random_qkv(1, 1, 1, 1, Tk, d, torch.bfloat16, seed=9)
+    qd, kd, vd = gpu(q, k, v)
+    nb = ra.attn_fwd_rope_workspace_bytes(Tk, d)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    ra.attn_fwd_rope(qd, kd, vd, q_offset=Tk - 1, base=base, workspace=ws)
+    torch.cuda.synchronize()
+    got = ws.cpu().view(torch.float32).numpy().reshape(Tk, d // 2, 2)
+    want = oracle.rope_table(Tk, d, 0, base)
+    ulp = np.spacing(np.abs(want).astype(np.float32))
+    diff = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    assert np.all(diff <= ulp), float(np.max(diff / ulp))
+    assert np.mean(got == want) > 0.999

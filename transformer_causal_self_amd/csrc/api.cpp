@@ -402,9 +402,8 @@ ROCATTN_API int attn_fwd_rope(const void* q, void* k, const void* v, void* o, in
         return ROCATTN_ERR_SHAPE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     float* tab = static_cast<float*>(workspace);
-    hipError_t e = rocattn::launch_rope_table(tab, Tk, d_head, 0, rope_base, s);
-    if (e == hipSuccess)
-        e = rocattn::launch_rope(k, (long long)B * Hkv, Tk, d_head, 0, rope_base, dtype, pairing, s, tab);
+    hipError_t e = rocattn::launch_rope(k, (long long)B * Hkv, Tk, d_head, 0, rope_base, dtype,
+                                        pairing, s, tab);
     if (e != hipSuccess) return ROCATTN_ERR_HIP;
     FwdParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d_head, scale, causal, q_offset);
     p.rope_tab = tab;

@@ -59,15 +59,10 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 // RoPE in place; dtype 0 = f32, 1 = bf16; pairing 0 = split-half, 1 =
 // adjacent.  x holds n_seq sequences of T rows of d elements ([n_seq][T][d])
 // with token t at position pos0 + t.
-// tab (optional): float32 (cos, sin) [position][d/2] covering positions
-// pos0 .. pos0 + T - 1, read instead of forming the angles per lane.
+// tab (optional): also store the float32 (cos, sin) of every pair at
+// positions pos0 .. pos0 + T - 1 into tab[position][d/2].
 hipError_t launch_rope(void* x, long long n_seq, int T, int d, int pos0, double base,
-                       int dtype, int pairing, hipStream_t stream, const float* tab = nullptr);
-
-// The table launch_rope and the prefill kernel's query load read: the
-// float32 (cos, sin) of every pair at positions pos0 .. pos0 + T - 1, formed
-// in double precision exactly as the RoPE pass forms them.
-hipError_t launch_rope_table(float* tab, int T, int d, int pos0, double base, hipStream_t stream);
+                       int dtype, int pairing, hipStream_t stream, float* tab = nullptr);
 
 // Everything a backward launch needs (dense [B][H][T][d] tensors), validated
 // by the host API.

@@ -11,10 +11,9 @@
 // Angles: each lane forms, in double precision, the cosine and sine of the
 // few pairs it owns at one position, rounds them once to float32, and then
 // rotates that (position, pairs) slot in every head and batch entry of its
-// share -- or, when a table [position][d/2] of those float32 (cos, sin)
-// values is given (rope_table_kernel writes it with the same arithmetic),
-// reads them from it.  The double-precision cosine and sine cost a few
-// hundred instructions each, so without a table a lane keeps many rows.  The work is HBM-bound
+// share.  On request the lanes of the first row chunk also store those
+// float32 (cos, sin) values in a table [position][d/2], which the attention
+// kernel's query load reads.  The work is HBM-bound
 // (one read and one write of q and k); each lane moves 2 x 8 bytes (bf16) or
 // 2 x 16 bytes (f32) per head row, with neighbouring lanes on neighbouring
 // pairs so every head row is read and written by full, coalesced segments.
@@ -55,7 +54,7 @@ template <typename T, int kPairs, bool ADJ>  // kPairs channel pairs per lane
 __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long long n_seq,
                                                         int rows_per_chunk, int T_len, int d,
                                                         int pos0, double neg_log2_base_over_half,
-                                                        const float2* __restrict__ tab) {
+                                                        float2* __restrict__ tab) {
     const int half = d >> 1;
     const int groups = half / kPairs;  // lanes per token
     const long long slot = (long long)blockIdx.x * kThreads + threadIdx.x;
@@ -64,24 +63,20 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long 
     const int p0 = (int)(slot - (long long)t * groups) * kPairs;
 
     float cs[kPairs], sn[kPairs];
-    if (tab) {
-        const float2* row = tab + (size_t)(pos0 + t) * half + p0;
+    const double pos = (double)pos0 + (double)t;
 #pragma unroll
-        for (int u = 0; u < kPairs; ++u) {
-            cs[u] = row[u].x;
-            sn[u] = row[u].y;
-        }
-    } else {
-        const double pos = (double)pos0 + (double)t;
+    for (int u = 0; u < kPairs; ++u) {
+        // base^(-2p/d) = 2^(-(p / (d/2)) * log2(base))
+        const double inv_freq = exp2((double)(p0 + u) * neg_log2_base_over_half);
+        double s, c;
+        rope_sincos(pos * inv_freq, s, c);
+        cs[u] = (float)c;
+        sn[u] = (float)s;
+    }
+    if (tab && blockIdx.y == 0) {
+        float2* row = tab + (size_t)(pos0 + t) * half + p0;
 #pragma unroll
-        for (int u = 0; u < kPairs; ++u) {
-            // base^(-2p/d) = 2^(-(p / (d/2)) * log2(base))
-            const double inv_freq = exp2((double)(p0 + u) * neg_log2_base_over_half);
-            double s, c;
-            sincos(pos * inv_freq, &s, &c);
-            cs[u] = (float)c;
-            sn[u] = (float)s;
-        }
+        for (int u = 0; u < kPairs; ++u) row[u] = make_float2(cs[u], sn[u]);
     }
 
     const long long r0 = (long long)blockIdx.y * rows_per_chunk;
@@ -107,34 +102,18 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long 
     }
 }
 
-// The float32 (cos, sin) of pair p at position pos0 + t, for t < T_len and
-// every pair, into tab[pos0 + t][p]: the arithmetic of rope_kernel's own
-// angles, once per (position, pair).
-__global__ __launch_bounds__(kThreads) void rope_table_kernel(float2* __restrict__ tab, int T_len,
-                                                              int half, int pos0,
-                                                              double neg_log2_base_over_half) {
-    const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= (long long)T_len * half) return;
-    const int t = (int)(i / half), p = (int)(i - (long long)t * half);
-    const double pos = (double)pos0 + (double)t;
-    const double inv_freq = exp2((double)p * neg_log2_base_over_half);
-    double s, c;
-    sincos(pos * inv_freq, &s, &c);
-    tab[(size_t)(pos0 + t) * half + p] = make_float2((float)c, (float)s);
-}
-
 template <typename T, int kPairs>
 hipError_t launch_rope_t(T* x, long long n_seq, int T_len, int d, int pos0, double base,
-                         int pairing, hipStream_t stream, const float* tab) {
+                         int pairing, hipStream_t stream, float* tab) {
     const int half = d / 2;
     const int groups = half / kPairs;
     const long long slots = (long long)T_len * groups;
     const long long gx = (slots + kThreads - 1) / kThreads;
     // split the head rows so the launch has enough workgroups to fill the
-    // chip; without a table each chunk forms its own cosines and sines, so
-    // the chunks are capped at 2^17 / slots (at most 2^17 lanes' worth)
+    // chip; each chunk forms its own cosines and sines, so the chunks are
+    // capped at 2^17 / slots (at most 2^17 lanes' worth of angles)
     long long gy = (2048 + gx - 1) / gx;
-    if (!tab && gy > (1LL << 17) / slots) gy = (1LL << 17) / slots;
+    if (gy > (1LL << 17) / slots) gy = (1LL << 17) / slots;
     if (gy > n_seq) gy = n_seq;
     if (gy < 1) gy = 1;
     const int rows_per_chunk = (int)((n_seq + gy - 1) / gy);
@@ -143,26 +122,17 @@ hipError_t launch_rope_t(T* x, long long n_seq, int T_len, int d, int pos0, doub
     dim3 grid((unsigned)gx, (unsigned)gy);
     if (pairing)
         hipLaunchKernelGGL((rope_kernel<T, kPairs, true>), grid, dim3(kThreads), 0, stream,
-                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg, reinterpret_cast<const float2*>(tab));
+                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg, reinterpret_cast<float2*>(tab));
     else
         hipLaunchKernelGGL((rope_kernel<T, kPairs, false>), grid, dim3(kThreads), 0, stream,
-                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg, reinterpret_cast<const float2*>(tab));
+                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg, reinterpret_cast<float2*>(tab));
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_rope_table(float* tab, int T_len, int d, int pos0, double base,
-                             hipStream_t stream) {
-    const int half = d / 2;
-    const long long n = (long long)T_len * half;
-    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       stream, reinterpret_cast<float2*>(tab), T_len, half, pos0, -log2(base) / (double)half);
-    return hipGetLastError();
-}
-
 hipError_t launch_rope(void* x, long long n_seq, int T_len, int d, int pos0, double base,
-                       int dtype, int pairing, hipStream_t stream, const float* tab) {
+                       int dtype, int pairing, hipStream_t stream, float* tab) {
     // four pairs per lane (8-byte bf16 / 16-byte f32 accesses) when the half
     // head size allows it, else one pair per lane
     const bool wide = (d / 2) % 4 == 0;
@@ -216,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void step_prep_kernel(PrepArgs a) {
     for (int u = 0; u < kPairs; ++u) {
         const double inv_freq = exp2((double)(p0 + u) * a.neg);
         double s, c;
-        sincos(pos * inv_freq, &s, &c);
+        rope_sincos(pos * inv_freq, s, c);
         cs[u] = (float)c;
         sn[u] = (float)s;
     }
