@@ -70,6 +70,9 @@ class Oracle:
         lib.oracle_attn.restype = ctypes.c_int
         lib.oracle_attn.argtypes = [_D, _D, _D, _D, _D, _L, _L, _L, _L, _L, _L,
                                     ctypes.c_double, ctypes.c_int, _L]
+        lib.oracle_attn_dv.restype = ctypes.c_int
+        lib.oracle_attn_dv.argtypes = [_D, _D, _D, _D, _D, _L, _L, _L, _L, _L, _L, _L,
+                                       ctypes.c_double, ctypes.c_int, _L]
         lib.oracle_attn_rows.restype = ctypes.c_int
         lib.oracle_attn_rows.argtypes = [_D, _D, _D, ctypes.POINTER(ctypes.c_long), _L,
                                          _D, _D, _L, _L, _L, _L, _L, _L,
@@ -89,18 +92,20 @@ class Oracle:
 
     def attn(self, q, k, v, scale: float, causal: bool = True, q_offset: int = 0,
              return_lse: bool = False):
-        """o[B,Hq,Tq,d] (and lse[B,Hq,Tq]) for q[B,Hq,Tq,d], k/v[B,Hkv,Tk,d]."""
+        """o[B,Hq,Tq,dv] (and lse[B,Hq,Tq]) for q[B,Hq,Tq,dk], k[B,Hkv,Tk,dk],
+        v[B,Hkv,Tk,dv] (dv may differ from dk)."""
         q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
-        B, Hq, Tq, d = q.shape
+        B, Hq, Tq, dk = q.shape
         _, Hkv, Tk, _ = k.shape
-        if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        dv = v.shape[3]
+        if k.shape[:3] != v.shape[:3] or k.shape[0] != B or k.shape[3] != dk:
             raise ValueError("shape mismatch")
-        o = np.empty_like(q)
+        o = np.empty((B, Hq, Tq, dv), dtype=np.float64)
         lse = np.empty((B, Hq, Tq), dtype=np.float64) if return_lse else None
-        st = self._lib.oracle_attn(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(o),
-                                   self._ptr(lse) if lse is not None else None,
-                                   B, Hq, Hkv, Tq, Tk, d, float(scale), int(bool(causal)),
-                                   int(q_offset))
+        st = self._lib.oracle_attn_dv(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(o),
+                                      self._ptr(lse) if lse is not None else None,
+                                      B, Hq, Hkv, Tq, Tk, dk, dv, float(scale), int(bool(causal)),
+                                      int(q_offset))
         if st != 0:
             raise ValueError(f"oracle_attn rejected its arguments (status {st})")
         return (o, lse) if return_lse else o

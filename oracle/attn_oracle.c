@@ -59,15 +59,17 @@ static long last_visible_key(long i, long Tk, int causal, long q_offset) {
  * Negative Infinity?], so the masked keys are simply left out of both sums.
  * Subtracting the row maximum m from every score before exp leaves alpha
  * unchanged in exact arithmetic (the factor exp(-m) cancels) and keeps
- * exp() finite.  `srow` is caller scratch of at least Tk doubles. */
+ * exp() finite.  q and k rows have dk channels, v and o rows dv [P2 Scaled
+ * dot-product attention: queries and keys share d_k, values have their own
+ * d_v].  `srow` is caller scratch of at least Tk doubles. */
 static void attn_row(const double* qi, const double* kh, const double* vh,
                      double* oi, double* lse_i, double* srow,
-                     long Tk, long d, double scale, long lim) {
+                     long Tk, long dk, long dv, double scale, long lim) {
     /* scores s_j = scale * sum_c q[c] k[j][c] */
     for (long j = 0; j <= lim; ++j) {
-        const double* kj = kh + j * d;
+        const double* kj = kh + j * dk;
         double dot = 0.0;
-        for (long c = 0; c < d; ++c) dot += qi[c] * kj[c];
+        for (long c = 0; c < dk; ++c) dot += qi[c] * kj[c];
         srow[j] = scale * dot;
     }
     (void)Tk;
@@ -82,12 +84,12 @@ static void attn_row(const double* qi, const double* kh, const double* vh,
         l += srow[j];
     }
     /* o[c] = sum_j w_j v[j][c] / l */
-    for (long c = 0; c < d; ++c) oi[c] = 0.0;
+    for (long c = 0; c < dv; ++c) oi[c] = 0.0;
     for (long j = 0; j <= lim; ++j) {
-        const double* vj = vh + j * d;
-        for (long c = 0; c < d; ++c) oi[c] += srow[j] * vj[c];
+        const double* vj = vh + j * dv;
+        for (long c = 0; c < dv; ++c) oi[c] += srow[j] * vj[c];
     }
-    for (long c = 0; c < d; ++c) oi[c] /= l;
+    for (long c = 0; c < dv; ++c) oi[c] /= l;
     /* log of the softmax denominator of the unshifted scores */
     if (lse_i) *lse_i = m + log(l);
 }
@@ -103,12 +105,14 @@ static int check_shape(long B, long Hq, long Hkv, long Tq, long Tk, long d,
     return 0;
 }
 
-/* Full attention forward.  lse may be NULL. */
-int oracle_attn(const double* q, const double* k, const double* v, double* o,
-                double* lse, long B, long Hq, long Hkv, long Tq, long Tk,
-                long d, double scale, int causal, long q_offset) {
-    int st = check_shape(B, Hq, Hkv, Tq, Tk, d, scale, causal, q_offset);
+/* Full attention forward with dk channels in q and k and dv in v and o
+ * (q, k: [..][dk]; v, o: [..][dv]).  lse may be NULL. */
+int oracle_attn_dv(const double* q, const double* k, const double* v, double* o,
+                   double* lse, long B, long Hq, long Hkv, long Tq, long Tk,
+                   long dk, long dv, double scale, int causal, long q_offset) {
+    int st = check_shape(B, Hq, Hkv, Tq, Tk, dk, scale, causal, q_offset);
     if (st) return st;
+    if (dv <= 0) return -2;
     const long nrows = B * Hq * Tq;
     int failed = 0;
 #pragma omp parallel
@@ -122,17 +126,24 @@ int oracle_attn(const double* q, const double* k, const double* v, double* o,
             for (long r = 0; r < nrows; ++r) {
                 long i = r % Tq, bh = r / Tq, hq = bh % Hq, b = bh / Hq;
                 long hk = kv_head_of(hq, Hq, Hkv);
-                const double* qi = q + r * d;
-                const double* kh = k + (b * Hkv + hk) * Tk * d;
-                const double* vh = v + (b * Hkv + hk) * Tk * d;
+                const double* qi = q + r * dk;
+                const double* kh = k + (b * Hkv + hk) * Tk * dk;
+                const double* vh = v + (b * Hkv + hk) * Tk * dv;
                 long lim = last_visible_key(i, Tk, causal, q_offset);
-                attn_row(qi, kh, vh, o + r * d, lse ? lse + r : NULL, srow,
-                         Tk, d, scale, lim);
+                attn_row(qi, kh, vh, o + r * dv, lse ? lse + r : NULL, srow,
+                         Tk, dk, dv, scale, lim);
             }
             free(srow);
         }
     }
     return failed ? -10 : 0;
+}
+
+/* The forward with one head size d for q, k, v and o. */
+int oracle_attn(const double* q, const double* k, const double* v, double* o,
+                double* lse, long B, long Hq, long Hkv, long Tq, long Tk,
+                long d, double scale, int causal, long q_offset) {
+    return oracle_attn_dv(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, d, scale, causal, q_offset);
 }
 
 /* Gradients of the attention forward (oracle_attn) for an upstream
@@ -186,7 +197,7 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
                         /* alpha_ij: the forward's softmax weights (attn_row
                          * leaves exp(s_j - m) in its scratch and o_i / l in
                          * oi; divide the weights by l = sum of them) */
-                        attn_row(qi, kh, vh, oi, NULL, alpha, Tk, d, scale, lim);
+                        attn_row(qi, kh, vh, oi, NULL, alpha, Tk, d, d, scale, lim);
                         double l = 0.0;
                         for (long j = 0; j <= lim; ++j) l += alpha[j];
                         for (long j = 0; j <= lim; ++j) alpha[j] /= l;
@@ -254,7 +265,7 @@ int oracle_attn_rows(const double* q, const double* k, const double* v,
                 const double* vh = v + (b * Hkv + hk) * Tk * d;
                 long lim = last_visible_key(i, Tk, causal, q_offset);
                 attn_row(qi, kh, vh, o_rows + r * d,
-                         lse_rows ? lse_rows + r : NULL, srow, Tk, d, scale, lim);
+                         lse_rows ? lse_rows + r : NULL, srow, Tk, d, d, scale, lim);
             }
             free(srow);
         }

@@ -185,6 +185,40 @@ def pin_torch_sdpa_library(orc):
         assert np.max(np.abs(o - ref.numpy())) < 1e-12, (B, Hq, Hkv, Tq, Tk, d)
 
 
+def pin_value_width_differs_from_key_width(orc):
+    """Values may have their own width d_v ("The Transformer architecture" --
+    Scaled dot-product attention: queries and keys share d_k, values d_v).
+    Against torch's float64 SDPA, which takes value rows of another width;
+    T = 1 returns v_0 whatever d_v; and the output channels of V are
+    independent: attention with V = [V1 | V2] is [attn(V1) | attn(V2)]."""
+    import torch
+    import torch.nn.functional as F
+    r = _rng(17)
+    for B, Hq, Hkv, Tq, Tk, dk, dv, causal, qo in [(2, 4, 2, 6, 9, 8, 12, True, 3),
+                                                   (1, 2, 2, 5, 5, 16, 4, False, 0),
+                                                   (1, 8, 2, 1, 13, 6, 10, True, 12)]:
+        q = r.standard_normal((B, Hq, Tq, dk)); k = r.standard_normal((B, Hkv, Tk, dk))
+        v = r.standard_normal((B, Hkv, Tk, dv))
+        sc = 1.0 / math.sqrt(dk)
+        o = orc.attn(q, k, v, sc, causal=causal, q_offset=qo)
+        assert o.shape == (B, Hq, Tq, dv)
+        rep = Hq // Hkv
+        tk = torch.from_numpy(k).repeat_interleave(rep, dim=1)
+        tv = torch.from_numpy(v).repeat_interleave(rep, dim=1)
+        i = torch.arange(Tq)[:, None]; j = torch.arange(Tk)[None, :]
+        mask = (j <= qo + i) if causal else torch.ones(Tq, Tk, dtype=torch.bool)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), tk, tv, attn_mask=mask, scale=sc)
+        assert np.max(np.abs(o - ref.numpy())) < 1e-12
+        split = dv // 2
+        o1 = orc.attn(q, k, np.ascontiguousarray(v[..., :split]), sc, causal=causal, q_offset=qo)
+        o2 = orc.attn(q, k, np.ascontiguousarray(v[..., split:]), sc, causal=causal, q_offset=qo)
+        assert np.max(np.abs(np.concatenate([o1, o2], axis=-1) - o)) < 1e-14
+    q = r.standard_normal((1, 2, 1, 8)); k = r.standard_normal((1, 1, 1, 8))
+    v = r.standard_normal((1, 1, 1, 24))
+    o = orc.attn(q, k, v, 0.3)
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0]) and np.array_equal(o[0, 1, 0], v[0, 0, 0])
+
+
 def pin_lse_matches_logsumexp(orc):
     """log of the softmax denominator equals torch.logsumexp of the masked,
     scaled scores (library routine)."""

@@ -23,10 +23,11 @@ MUTANTS = {
         "        srow[j] = scale * dot;\n    }\n"
         "    for (long j = lim + 1; j < Tk; ++j) srow[j] = 0.0;\n    lim = Tk - 1;\n")],
     "gqa_heads_tiled": [("return hq / (Hq / Hkv);", "return hq % Hkv;")],
-    "softmax_not_normalised": [("for (long c = 0; c < d; ++c) oi[c] /= l;",
-                                "for (long c = 0; c < d; ++c) oi[c] /= 1.0;")],
+    "softmax_not_normalised": [("for (long c = 0; c < dv; ++c) oi[c] /= l;",
+                                "for (long c = 0; c < dv; ++c) oi[c] /= 1.0;")],
     "value_row_index_wrong": [("oi[c] += srow[j] * vj[c];", "oi[c] += srow[j] * vh[c];")],
-    "key_channels_reversed": [("dot += qi[c] * kj[c];", "dot += qi[c] * kj[d - 1 - c];")],
+    "value_rows_strided_by_key_width": [("const double* vj = vh + j * dv;", "const double* vj = vh + j * dk;")],
+    "key_channels_reversed": [("dot += qi[c] * kj[c];", "dot += qi[c] * kj[dk - 1 - c];")],
     "lse_without_max": [("*lse_i = m + log(l);", "*lse_i = log(l);")],
     "bwd_dv_uses_unnormalised_weights": [("for (long j = 0; j <= lim; ++j) alpha[j] /= l;", "")],
     "bwd_softmax_jacobian_term_dropped": [("const double ds = alpha[j] * (g[j] - ag);",
