@@ -37,7 +37,9 @@ Also printed in the same line (unless --no-also): the other workloads'
 per-kernel rates, each timed the same way, so every part of the path has a
 live number; and a CPU baseline: the fp64 oracle timed on the host cores
 on a bounded sample of the headline workload.  The attention gradients
-(attn_bwd) are timed on the shapes of workloads 2 and 3 ("backward").
+(attn_bwd) are timed on the shapes of workloads 2 and 3 ("backward"), and
+attention with values of their own width (attn_fwd_dv) on workload 3's
+shape ("value_width").
 
 --calib-copy runs only a plain device copy of a known size (used to scale
 the HBM byte counters of a profiler run).
@@ -344,6 +346,34 @@ def measure_cached_steps(torch, ra, wl, dev):
     return out
 
 
+VALUE_WIDTHS = ((128, 64), (64, 128))
+
+
+def measure_value_widths(torch, ra, wl, dev):
+    """attn_fwd_dv (values of their own width) on workload 3's shape (B2 Hq32
+    Hkv8 T4096, causal) with (d_k, d_v) = (128, 64) and (64, 128).  FLOPs:
+    2 (d_k + d_v) per visible pair (the two products)."""
+    w = wl.WORKLOADS[3]
+    out = {}
+    for dk, dv in VALUE_WIDTHS:
+        q, k, _ = (x.to(dev) for x in wl.random_qkv(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, dk, seed=3001))
+        _, _, v = (x.to(dev) for x in wl.random_qkv(w.B, w.Hq, w.Hkv, 1, w.Tk, dv, seed=3002))
+        o = torch.empty(w.B, w.Hq, w.Tq, dv, dtype=q.dtype, device=dev)
+        call = ra._fwd_dv_call(q, k, v, o, None, dk ** -0.5, True, 0, None)
+        timer = Timer(torch)
+        t_est = timer(call, 3, 1) * 1e-3
+        ms = timer(call, max(10, int(0.05 / t_est)), max(5, int(0.03 / t_est)))
+        flops = 2.0 * (dk + dv) * w.B * w.Hq * n_visible(w.Tq, w.Tk, True, 0)
+        tf = flops / (ms * 1e-3) / 1e12
+        name = f"bf16_B{w.B}_Hq{w.Hq}_Hkv{w.Hkv}_T{w.Tq}_dk{dk}_dv{dv}"
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                     "pct_of_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 1)}
+        print(f"# value width {name}: {ms * 1e3:.1f} us = {tf:.1f} TFLOP/s", file=sys.stderr)
+        del q, k, v, o
+        torch.cuda.empty_cache()
+    return out
+
+
 BACKWARD_WORKLOADS = (2, 3)
 
 
@@ -548,6 +578,7 @@ def main():
         line["also"] = also
         line["cached_steps"] = measure_cached_steps(torch, ra, wl, dev)
         line["backward"] = measure_backward(torch, ra, wl, dev)
+        line["value_width"] = measure_value_widths(torch, ra, wl, dev)
 
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -245,6 +245,25 @@ int attn_decode_step(void* q, const void* k_new, const void* v_new, void* k_cach
                      void* stream, void* workspace, size_t ws_bytes, float* lse);
 
 /*
+ * attn_fwd_dv -- attn_fwd with a value width d_v of its own: q and k rows
+ * have d_k channels, v and o rows d_v ("The Transformer architecture" --
+ * Scaled dot-product attention: only q and k must share a width; the
+ * values need the keys' token count, not their width).  softmax(scale Q K^T
+ * + M) V as attn_fwd; scale is typically 1/sqrt(d_k).
+ *
+ *   q   [B][Hq][Tq][d_k]     k   [B][Hkv][Tk][d_k]
+ *   v   [B][Hkv][Tk][d_v]    o   [B][Hq][Tq][d_v], fully overwritten
+ *   lse optional float32 [B][Hq][Tq] (as attn_fwd_ws)
+ * Supported: bf16 with d_k, d_v in {64, 128} (every Tq on the prefill
+ * kernel, no workspace); float32 with d_k, d_v <= 256, multiples of 4.
+ * d_k == d_v gives the same result as attn_fwd.  Other arguments, checks
+ * and status codes as attn_fwd.
+ */
+int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                int Tq, int Tk, int d_k, int d_v, float scale, int causal, int q_offset,
+                int dtype, void* stream, float* lse);
+
+/*
  * attn_fwd_rope -- RoPE and attention of one prefill in two launches: k is
  * rotated in place at positions 0 .. Tk - 1 (the key rows a cache keeps,
  * "The Transformer architecture" -- Hands-on), and the attention of

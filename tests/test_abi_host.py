@@ -243,3 +243,21 @@ def test_attn_fwd_rope_workspace_bytes():
     assert lib.attn_fwd_rope_workspace_bytes(4096, 128) == 4096 * 64 * 8
     assert lib.attn_fwd_rope_workspace_bytes(16, 96) == 0
     assert lib.attn_fwd_rope_workspace_bytes(0, 64) == 0
+
+
+def fwd_dv(q=A, k=Bp, v=C, o=D, B=1, Hq=4, Hkv=2, Tq=16, Tk=16, dk=64, dv=128, causal=1,
+           q_offset=0, dtype=BF16, lse=None, scale=0.125):
+    return rocattn.library().attn_fwd_dv(q, k, v, o, B, Hq, Hkv, Tq, Tk, dk, dv, scale, causal,
+                                         q_offset, dtype, None, lse)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(v=None), -1), (dict(dtype=3), -3), (dict(dv=96), -4), (dict(dk=32), -4),
+    (dict(dtype=F32, dv=258), -4), (dict(dtype=F32, dk=6), -4), (dict(dv=0), -2),
+    (dict(Hq=6, Hkv=4), -2), (dict(q_offset=-1), -5), (dict(scale=float("nan")), -6),
+    (dict(v=C + 8), -7), (dict(lse=0x7F000001), -7),
+    (dict(o=C + 4096), -2),                               # o inside v (16 x 128 values per head)
+    (dict(o=A + 16 * 64 * 2 * 3), -2),                    # o starts inside q's last head
+])
+def test_attn_fwd_dv_rejects(kw, status):
+    assert fwd_dv(**kw) == status

@@ -832,3 +832,42 @@ def test_rope_angle_table_matches_oracle(Tk, d, base):
     diff = np.abs(got.astype(np.float64) - want.astype(np.float64))
     assert np.all(diff <= ulp), float(np.max(diff / ulp))
     assert np.mean(got == want) > 0.999
+
+
+# ---- values of their own width (d_v != d_k)
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,Tq,Tk,dk,dv,causal,qo", [
+    (torch.bfloat16, 2, 8, 2, 300, 300, 64, 128, True, 0),
+    (torch.bfloat16, 1, 8, 4, 300, 300, 128, 64, True, 0),
+    (torch.bfloat16, 1, 4, 2, 70, 1030, 128, 64, True, 960),
+    (torch.bfloat16, 2, 4, 4, 129, 200, 64, 128, False, 0),
+    (torch.bfloat16, 4, 32, 8, 1, 777, 64, 128, True, 776),     # one row: the prefill kernel
+    (torch.float32, 1, 4, 2, 100, 100, 64, 32, True, 0),
+    (torch.float32, 2, 2, 1, 33, 70, 8, 24, False, 0),
+    (torch.float32, 1, 2, 2, 17, 40, 256, 4, True, 23),
+])
+def test_attn_fwd_dv_matches_oracle(dtype, B, Hq, Hkv, Tq, Tk, dk, dv, causal, qo):
+    say("attn_fwd_dv", dtype, B, Hq, Hkv, Tq, Tk, dk, dv, causal, qo)
+    q, k, _ = wl.random_qkv(B, Hq, Hkv, Tq, Tk, dk, dtype, seed=400 + Tq)
+    v = _rand((B, Hkv, Tk, dv), dtype, 401 + dv)
+    scale = dk ** -0.5
+    qd, kd, vd = gpu(q, k, v)
+    lse = torch.empty(B, Hq, Tq, dtype=torch.float32, device=DEV)
+    o = ra.attn_fwd_dv(qd, kd, vd, scale=scale, causal=causal, q_offset=qo, lse=lse)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (B, Hq, Tq, dv)
+    want, want_lse = oracle.attn(q, k, v, scale, causal=causal, q_offset=qo, return_lse=True)
+    err = float(np.max(np.abs(f64(o) - want)))
+    assert err <= TOL[dtype], err
+    lse_tol = 1e-4 if dtype == torch.float32 else 2.0e-3
+    assert float(np.max(np.abs(f64(lse) - want_lse))) <= lse_tol
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 64), (torch.bfloat16, 128), (torch.float32, 64)])
+def test_attn_fwd_dv_equal_widths_is_attn_fwd_bit_exact(dtype, d):
+    say("attn_fwd_dv equal widths", dtype, d)
+    q, k, v = gpu(*wl.random_qkv(2, 8, 2, 300, 300, d, dtype, seed=41))
+    a = ra.attn_fwd_dv(q, k, v, scale=0.1)
+    b = ra.attn_fwd(q, k, v, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

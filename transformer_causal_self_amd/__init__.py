@@ -16,6 +16,7 @@ or a call is made with CPU tensors, the call raises.
     status_string(code)
     attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o=None, scale=None,
                      base=10000.0, pairing="split", workspace=None, lse=None)
+    attn_fwd_dv(q, k, v, o=None, scale=None, ...) -> o   (v of another width)
     attn_fwd_rope(q, k, v, o=None, ..., base=10000.0, pairing="split") -> o
     attn_bwd(q, k, v, o, dO, lse, scale=None, causal=True, q_offset=0) -> (dq, dk, dv)
     bind_attn_fwd_ws(...), bind_rope_apply(...), bind_attn_decode_step(...),
@@ -37,7 +38,7 @@ LIBRARY = os.path.join(HERE, "librocattn.so")
 
 # the C ABI, as declared in include/rocattn.h
 SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_strided", "attn_workspace_bytes",
-           "rope_apply", "rope_apply_ex", "attn_decode_step", "attn_fwd_rope",
+           "rope_apply", "rope_apply_ex", "attn_decode_step", "attn_fwd_dv", "attn_fwd_rope",
            "attn_fwd_rope_workspace_bytes", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_status_string")
 
@@ -85,6 +86,8 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_step.restype = i
         lib.attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
                                          ctypes.c_double, i, i, vp, vp, sz, vp]
+        lib.attn_fwd_dv.restype = i
+        lib.attn_fwd_dv.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp, vp]
         lib.attn_fwd_rope.restype = i
         lib.attn_fwd_rope.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, ctypes.c_double, i,
                                       i, vp, vp, sz, vp]
@@ -161,8 +164,11 @@ def _fwd_args(q, k, v, o, scale, causal, q_offset, rows=False):
 def attn_fwd(q, k, v, o=None, scale=None, causal=True, q_offset=0, stream=None):
     """softmax(scale q k^T + M) v on the GPU; returns o ([B, Hq, Tq, d]).
     Views with contiguous rows (e.g. [B, T, H, d] tensors transposed to
-    [B, H, T, d]) go through attn_fwd_strided."""
+    [B, H, T, d]) go through attn_fwd_strided; values of another width than
+    the keys go through attn_fwd_dv."""
     import torch
+    if v.dim() == 4 and q.dim() == 4 and v.shape[3] != q.shape[3]:
+        return attn_fwd_dv(q, k, v, o, scale, causal, q_offset, stream=stream)
     if o is None:
         o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if not all(t.is_contiguous() for t in (q, k, v, o)):
@@ -175,6 +181,41 @@ def attn_fwd(q, k, v, o=None, scale=None, causal=True, q_offset=0, stream=None):
                             qo, dt, _stream(q, stream))
     if st != OK:
         raise RocattnError("attn_fwd", st)
+    return o
+
+
+def _fwd_dv_call(q, k, v, o, lse, scale, causal, q_offset, stream):
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_dev(n, t, q.dtype)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be dense (contiguous)")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q: [B, Hq, Tq, d_k]; k: [B, Hkv, Tk, d_k]; v: [B, Hkv, Tk, d_v]")
+    B, Hq, Tq, dk = q.shape
+    Hkv, Tk, dv = k.shape[1], k.shape[2], v.shape[3]
+    if (k.shape[0] != B or k.shape[3] != dk or tuple(v.shape[:3]) != tuple(k.shape[:3])
+            or tuple(o.shape) != (B, Hq, Tq, dv)):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}, o {tuple(o.shape)}")
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, Hq, Tq):
+            raise ValueError("lse must be [B, Hq, Tq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, dk, dv, float(scale),
+            int(bool(causal)), int(q_offset), _dtype_code(q), _stream(q, stream), _ptr(lse))
+    return Bound("attn_fwd_dv", library().attn_fwd_dv, args, (q, k, v, o, lse))
+
+
+def attn_fwd_dv(q, k, v, o=None, scale=None, causal=True, q_offset=0, lse=None, stream=None):
+    """Attention with values of their own width: q, k [.., d_k], v [.., d_v];
+    returns o [B, Hq, Tq, d_v] (scale defaults to 1/sqrt(d_k))."""
+    import torch
+    if o is None:
+        o = torch.empty(q.shape[:3] + (v.shape[3],), dtype=q.dtype, device=q.device)
+    _fwd_dv_call(q, k, v, o, lse, scale, causal, q_offset, stream)()
     return o
 
 

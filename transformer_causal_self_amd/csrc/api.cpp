@@ -369,6 +369,49 @@ ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, 
     return launch(p, dtype, s, workspace, ws_bytes);
 }
 
+ROCATTN_API int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, int B, int Hq,
+                            int Hkv, int Tq, int Tk, int d_k, int d_v, float scale, int causal,
+                            int q_offset, int dtype, void* stream, float* lse) {
+    if (dtype != ROCATTN_F32 && dtype != ROCATTN_BF16) return ROCATTN_ERR_DTYPE;
+    if (!q || !k || !v || !o) return ROCATTN_ERR_NULL;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || d_k <= 0 || d_v <= 0)
+        return ROCATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ROCATTN_ERR_SHAPE;
+    for (int d : {d_k, d_v}) {
+        if (dtype == ROCATTN_BF16) {
+            if (d != 64 && d != 128) return ROCATTN_ERR_HEADDIM;
+        } else if (d > 256 || d % 4 != 0) {
+            return ROCATTN_ERR_HEADDIM;
+        }
+    }
+    if (dtype == ROCATTN_F32 && (Hq > 65535 || B > 65535)) return ROCATTN_ERR_SHAPE;
+    if (causal && q_offset < 0) return ROCATTN_ERR_OFFSET;
+    if (causal && (long long)q_offset + Tq > INT_MAX) return ROCATTN_ERR_OFFSET;
+    if (!isfinite(scale)) return ROCATTN_ERR_SCALE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ROCATTN_ERR_ALIGN;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ROCATTN_ERR_ALIGN;
+    const long long nq = count4(B, Hq, Tq, d_k), nk = count4(B, Hkv, Tk, d_k);
+    const long long nv = count4(B, Hkv, Tk, d_v), no = count4(B, Hq, Tq, d_v);
+    if (nq < 0 || nk < 0 || nv < 0 || no < 0) return ROCATTN_ERR_SHAPE;
+    if (count4(B, Hq, (Tq + 127) / 128, 1) > INT_MAX) return ROCATTN_ERR_SHAPE;
+    const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
+    const size_t qb = (size_t)nq * elt, kb = (size_t)nk * elt, vb = (size_t)nv * elt, ob = (size_t)no * elt;
+    if (overlaps(o, ob, q, qb) || overlaps(o, ob, k, kb) || overlaps(o, ob, v, vb)) return ROCATTN_ERR_SHAPE;
+    if (lse) {
+        const size_t lb = (size_t)B * Hq * Tq * sizeof(float);
+        if (overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, vb) ||
+            overlaps(lse, lb, o, ob))
+            return ROCATTN_ERR_SHAPE;
+    }
+    FwdParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d_k, scale, causal, q_offset);
+    p.dv = d_v;
+    p.vs = {(long long)Hkv * Tk * d_v, (long long)Tk * d_v, d_v};
+    p.os = {(long long)Hq * Tq * d_v, (long long)Tq * d_v, d_v};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == ROCATTN_F32 ? rocattn::launch_fwd_f32(p, s) : rocattn::launch_prefill_bf16(p, s);
+    return e == hipSuccess ? ROCATTN_OK : ROCATTN_ERR_HIP;
+}
+
 ROCATTN_API size_t attn_fwd_rope_workspace_bytes(int Tk, int d_head) {
     if (Tk <= 0 || (d_head != 64 && d_head != 128)) return 0;
     return (size_t)Tk * (size_t)(d_head / 2) * 2 * sizeof(float);

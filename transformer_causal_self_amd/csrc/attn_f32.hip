@@ -1,5 +1,6 @@
-// attn_f32.hip -- float32 causal attention forward for any head size
-// d <= 256 with d % 4 == 0.
+// attn_f32.hip -- float32 causal attention forward for any head sizes
+// d_k, d_v <= 256 that are multiples of 4 (q and k rows have d_k channels,
+// v and o rows d_v).
 //
 // Computes O = softmax(scale * Q K^T + M) V ("Transformer" (ai-notes) --
 // Scaled dot-product attention) in one pass over the keys without forming
@@ -11,7 +12,7 @@
 //
 // Layout of the work: a workgroup of 256 lanes owns 64 query rows of one
 // (batch, query head); four neighbouring lanes share a row, each holding a
-// quarter of the head dimension of q and of the accumulator, and combine
+// quarter of the channels of q and of the accumulator, and combine
 // their partial dot products with two lane exchanges.  Key/value tiles of 32
 // rows are staged in LDS.  This kernel favours simplicity over speed: it is
 // the float32 correctness path (the bf16 MFMA kernels carry the throughput).
@@ -25,18 +26,18 @@ namespace {
 constexpr int kRows = 64;   // query rows per workgroup
 constexpr int kKeys = 32;   // keys per LDS tile
 
-template <int DQ>  // DQ >= d / 4, a power of two
+template <int DQ>  // DQ >= max(d_k, d_v) / 4, a power of two
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
     extern __shared__ float smem[];
-    const int d = p.d;
+    const int d = p.d, dv = p.dv ? p.dv : p.d;
     float* Ks = smem;                 // [kKeys][d]
-    float* Vs = smem + kKeys * d;     // [kKeys][d]
+    float* Vs = smem + kKeys * d;     // [kKeys][dv]
 
     const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
     const int hk = hq / (p.Hq / p.Hkv);
     const int tid = threadIdx.x;
     const int r = tid >> 2, part = tid & 3;
-    const int dq = d >> 2;
+    const int dq = d >> 2, dvq = dv >> 2;
     const int i = qt * kRows + r;
     const bool row_ok = i < p.Tq;
 
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
     float qr[DQ], acc[DQ];
 #pragma unroll
     for (int c = 0; c < DQ; ++c) {
-        qr[c] = (c < dq) ? qg[q_row + part * dq + c] : 0.f;
+        qr[c] = (c < dq) ? qg[q_row + part * dq + c] : 0.f;   // acc uses c < dvq
         acc[c] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
@@ -60,17 +61,20 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
 
     for (int j0 = 0; j0 < kv_end; j0 += kKeys) {
         __syncthreads();
-        const int n4 = kKeys * d / 4;
-        for (int x = tid; x < n4; x += 256) {
+        for (int x = tid; x < kKeys * d / 4; x += 256) {
             const int e = x * 4;
             const int jj = e / d, cc = e - jj * d;
             const int j = j0 + jj;
-            float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
-            if (j < p.Tk) {
-                kk = *reinterpret_cast<const float4*>(kg + k_base + j * p.ks.t + cc);
-                vv = *reinterpret_cast<const float4*>(vg + v_base + j * p.vs.t + cc);
-            }
+            float4 kk = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < p.Tk) kk = *reinterpret_cast<const float4*>(kg + k_base + j * p.ks.t + cc);
             *reinterpret_cast<float4*>(Ks + e) = kk;
+        }
+        for (int x = tid; x < kKeys * dv / 4; x += 256) {
+            const int e = x * 4;
+            const int jj = e / dv, cc = e - jj * dv;
+            const int j = j0 + jj;
+            float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < p.Tk) vv = *reinterpret_cast<const float4*>(vg + v_base + j * p.vs.t + cc);
             *reinterpret_cast<float4*>(Vs + e) = vv;
         }
         __syncthreads();
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
             l += pj;
 #pragma unroll
             for (int c = 0; c < DQ; ++c)
-                if (c < dq) acc[c] = fmaf(pj, Vs[jj * d + part * dq + c], acc[c]);
+                if (c < dvq) acc[c] = fmaf(pj, Vs[jj * dv + part * dvq + c], acc[c]);
         }
         m = m_new;
     }
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
         const float inv = 1.f / l;
 #pragma unroll
         for (int c = 0; c < DQ; ++c)
-            if (c < dq) og[o_row + part * dq + c] = acc[c] * inv;
+            if (c < dvq) og[o_row + part * dvq + c] = acc[c] * inv;
         if (p.lse && part == 0)
             p.lse[(size_t)(b * p.Hq + hq) * p.Tq + i] = m + logf(l);
     }
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
 template <int DQ>
 hipError_t launch_dq(const FwdParams& p, hipStream_t stream) {
     dim3 grid((p.Tq + kRows - 1) / kRows, p.Hq, p.B);
-    size_t lds = sizeof(float) * 2 * kKeys * p.d;
+    size_t lds = sizeof(float) * kKeys * (p.d + (p.dv ? p.dv : p.d));
     hipLaunchKernelGGL(attn_fwd_f32_kernel<DQ>, grid, dim3(256), lds, stream, p);
     return hipGetLastError();
 }
@@ -129,7 +133,7 @@ hipError_t launch_dq(const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
-    const int dq = p.d / 4;
+    const int dq = (p.dv > p.d ? p.dv : p.d) / 4;
     if (dq <= 4) return launch_dq<4>(p, stream);
     if (dq <= 8) return launch_dq<8>(p, stream);
     if (dq <= 16) return launch_dq<16>(p, stream);

@@ -62,28 +62,34 @@
 namespace rocattn {
 namespace {
 
-// Tile shape and occupancy per head size (chosen by measurement):
-//   d = 64:  64-key tiles, four waves per SIMD (about 120 VGPRs)
-//   d = 128: 32-key tiles, three waves per SIMD (about 145 VGPRs)
-template <int D>
+// Tile shape and occupancy per head size (chosen by measurement); DK is the
+// width of q and k rows, DV that of v and o rows:
+//   DK = DV = 64:  64-key tiles, four waves per SIMD (about 120 VGPRs)
+//   otherwise:     32-key tiles, three waves per SIMD (about 145-160 VGPRs)
+template <int DK, int DV>
 struct Cfg {
-    static constexpr int BN = D == 64 ? 64 : 32;    // keys per tile
-    static constexpr int WPE = D == 64 ? 4 : 3;     // waves per SIMD
+    static constexpr bool SMALL = DK == 64 && DV == 64;
+    static constexpr int BN = SMALL ? 64 : 32;      // keys per tile
+    static constexpr int WPE = SMALL ? 4 : 3;       // waves per SIMD
     static constexpr int NW = 4;                    // waves per workgroup
     static constexpr int RB = 1;                    // 32-row blocks per wave (the code allows more)
     static constexpr int BM = NW * RB * 32;         // query rows per workgroup
-    static constexpr int NCH = D / 8;               // 16-byte chunks per key row
-    static constexpr int TB = BN * D * 2;           // bytes of one K or V tile
+    static constexpr int NCHK = DK / 8;             // 16-byte chunks per key row
+    static constexpr int NCHV = DV / 8;             // 16-byte chunks per value row
+    static constexpr int TBK = BN * DK * 2;         // bytes of one K tile
+    static constexpr int TBV = BN * DV * 2;         // bytes of one V tile
     static constexpr int NRING = 2;                 // tiles per ring
-    static constexpr int NQ = D / 16;               // 16-wide d slices of q.k
-    static constexpr int NDB = D / 32;              // 32-column blocks of the output
+    static constexpr int NQ = DK / 16;              // 16-wide slices of q.k
+    static constexpr int NDB = DV / 32;             // 32-column blocks of the output
     static constexpr int NKC = BN / 16;             // 16-key slices of a tile
     static constexpr int NKB = BN / 32;             // 32-key blocks of a tile
     static constexpr int NE = 16 * NKB;             // scores per lane per row block and tile
     static constexpr int CPL = NW * 64;             // lanes of a workgroup (all of them copy)
-    static constexpr int NINS = BN * NCH / CPL;     // 16-byte copies per lane per tile
-    static constexpr int RSTR = CPL / NCH;          // tile rows filled by one copy instruction
-    static_assert(BN % 32 == 0 && NINS >= 1, "tiles of whole 32-key blocks");
+    static constexpr int NINSK = BN * NCHK / CPL;   // 16-byte copies per lane per K tile
+    static constexpr int NINSV = BN * NCHV / CPL;   // ... per V tile
+    static constexpr int RSTRK = CPL / NCHK;        // K tile rows filled by one copy instruction
+    static constexpr int RSTRV = CPL / NCHV;        // ... V tile rows
+    static_assert(BN % 32 == 0 && NINSK >= 1 && NINSV >= 1, "tiles of whole 32-key blocks");
 };
 
 struct Args {
@@ -155,23 +161,26 @@ __device__ inline void rope_q_frags(bf16x8 (&f)[D / 16], const float2* tab, int 
     }
 }
 
-template <int D>
+template <int DK, int DV>
 struct Scores {
-    f32x16 s[Cfg<D>::RB][Cfg<D>::NKB];
+    f32x16 s[Cfg<DK, DV>::RB][Cfg<DK, DV>::NKB];
 };
 
-// DENSE: q, k, v and o are dense [B][H][T][D], so every token stride is the
-// compile-time D (the strided instantiation reads the strides from Args).
+// DENSE: q and k are dense [B][H][T][DK], v and o dense [B][H][T][DV], so
+// every token stride is a compile-time constant (the strided instantiation
+// reads the strides from Args).
 // ROPE: the query rows are turned by RoPE at load (a.rope holds the table).
-template <int D, bool DENSE, bool ROPE>
-__global__ __launch_bounds__(Cfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(Cfg<D>::WPE, Cfg<D>::WPE)))
+template <int DK, int DV, bool DENSE, bool ROPE>
+__global__ __launch_bounds__((Cfg<DK, DV>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(Cfg<DK, DV>::WPE, Cfg<DK, DV>::WPE)))
 void prefill_kernel(Args a) {
-    typedef Cfg<D> C;
-    constexpr int BN = C::BN, NW = C::NW, RB = C::RB, BM = C::BM, NCH = C::NCH, TB = C::TB;
+    typedef Cfg<DK, DV> C;
+    constexpr int BN = C::BN, NW = C::NW, RB = C::RB, BM = C::BM, NCHK = C::NCHK, NCHV = C::NCHV;
+    constexpr int TBK = C::TBK, TBV = C::TBV;
     constexpr int NRING = C::NRING, NQ = C::NQ, NDB = C::NDB, NKC = C::NKC, NKB = C::NKB;
-    constexpr int NE = C::NE, CPL = C::CPL, NINS = C::NINS, RSTR = C::RSTR;
+    constexpr int NE = C::NE, CPL = C::CPL;
     (void)NW;
-    __shared__ __attribute__((aligned(1024))) char lds[2 * NRING * TB];  // K ring, then V ring
+    __shared__ __attribute__((aligned(1024))) char lds[NRING * (TBK + TBV)];  // K ring, then V ring
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -220,7 +229,7 @@ void prefill_kernel(Args a) {
     for (int rb = 0; rb < RB; ++rb) {
         const int row = iq[rb] < a.Tq ? iq[rb] : a.Tq - 1;
         const uint4* src = reinterpret_cast<const uint4*>(
-            a.q + b * a.qsb + hq * a.qsh + (long long)row * (DENSE ? D : a.qst) + 8 * h);
+            a.q + b * a.qsb + hq * a.qsh + (long long)row * (DENSE ? DK : a.qst) + 8 * h);
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
             uint4 u = src[2 * m];
@@ -228,7 +237,7 @@ void prefill_kernel(Args a) {
             qf[rb][m] = __builtin_bit_cast(bf16x8, u);
         }
         if constexpr (ROPE)
-            rope_q_frags<D>(qf[rb], a.rope + (size_t)(a.rope_pos0 + row) * (D / 2), a.rope_adj, h);
+            rope_q_frags<DK>(qf[rb], a.rope + (size_t)(a.rope_pos0 + row) * (DK / 2), a.rope_adj, h);
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
             uint4 u = __builtin_bit_cast(uint4, qf[rb][m]);
@@ -254,47 +263,57 @@ void prefill_kernel(Args a) {
     //      past n is never read: its copy re-reads tile n-1 into the slot it
     //      would occupy, which holds no live data then.  Rows past the last
     //      key re-read the last key (finite values; those keys are masked).
-    const unsigned kring = lds_addr(lds), vring = kring + NRING * TB;
+    const unsigned kring = lds_addr(lds), vring = kring + NRING * TBK;
     const bf16* kh = a.k + b * a.ksb + hk * a.ksh;
     const bf16* vh = a.v + b * a.vsb + hk * a.vsh;
-    const int kst = DENSE ? D : a.kst, vst = DENSE ? D : a.vst;   // elements between key rows
+    const int kst = DENSE ? DK : a.kst, vst = DENSE ? DV : a.vst;   // elements between key rows
     const int cl = wave * 64 + lane;
-    const int cp_r0 = cl / NCH, cp_p = cl % NCH;
-    const unsigned cp_kcol = 16u * (unsigned)(cp_p ^ swz_k<D>(cp_r0));
-    const unsigned cp_vcol = 16u * (unsigned)(cp_p ^ swz_v<D>(cp_r0));
+    const int cpk_r0 = cl / NCHK, cpk_p = cl % NCHK;   // K tile slot of this lane
+    const int cpv_r0 = cl / NCHV, cpv_p = cl % NCHV;   // V tile slot
+    const unsigned cp_kcol = 16u * (unsigned)(cpk_p ^ swz_k<DK>(cpk_r0));
+    const unsigned cp_vcol = 16u * (unsigned)(cpv_p ^ swz_v<DV>(cpv_r0));
     const unsigned cp_lds = (unsigned)(wave * 64 * 16);
-    auto kslot = [&](int t) { return kring + (unsigned)((t % NRING) * TB); };
-    auto vslot = [&](int t) { return vring + (unsigned)((t % NRING) * TB); };
+    auto kslot = [&](int t) { return kring + (unsigned)((t % NRING) * TBK); };
+    auto vslot = [&](int t) { return vring + (unsigned)((t % NRING) * TBV); };
     // Offset of the copies of a tile that lies wholly inside the keys: the
     // same for every such tile and copy instruction (the swizzle repeats
     // every RSTR rows; only the scalar source base moves).
-    const unsigned cpk = (unsigned)cp_r0 * (unsigned)(kst * 2) + cp_kcol;
-    const unsigned cpv = (unsigned)cp_r0 * (unsigned)(vst * 2) + cp_vcol;
-    auto copy_full = [&](const bf16* head, int rs, int t, unsigned slot, unsigned off) {
+    const unsigned cpk = (unsigned)cpk_r0 * (unsigned)(kst * 2) + cp_kcol;
+    const unsigned cpv = (unsigned)cpv_r0 * (unsigned)(vst * 2) + cp_vcol;
+    // NI copy instructions per lane, RS tile rows apart (C::NINSK / RSTRK for
+    // K tiles, C::NINSV / RSTRV for V tiles)
+    auto copy_full = [&](const bf16* head, int rs, int t, unsigned slot, unsigned off, auto ni, auto rstr) {
+        constexpr int NI = decltype(ni)::value, RS = decltype(rstr)::value;
 #pragma unroll
-        for (int i = 0; i < NINS; ++i)
-            copy16(head + (long long)(t * BN + i * RSTR) * rs, off, slot + (unsigned)(i * CPL * 16) + cp_lds);
+        for (int i = 0; i < NI; ++i)
+            copy16(head + (long long)(t * BN + i * RS) * rs, off, slot + (unsigned)(i * CPL * 16) + cp_lds);
     };
-    auto copy_tile = [&](const bf16* head, int rs, int t, unsigned slot, unsigned col) {
+    auto copy_tile = [&](const bf16* head, int rs, int t, unsigned slot, unsigned col, int r0, auto ni,
+                         auto rstr) {
+        constexpr int NI = decltype(ni)::value, RS = decltype(rstr)::value;
         const int j0 = min(t, n - 1) * BN;
 #pragma unroll
-        for (int i = 0; i < NINS; ++i) {
-            const int row = min(cp_r0 + i * RSTR, a.Tk - 1 - j0);
+        for (int i = 0; i < NI; ++i) {
+            const int row = min(r0 + i * RS, a.Tk - 1 - j0);
             copy16(head + (long long)j0 * rs, (unsigned)row * (unsigned)(rs * 2) + col,
                    slot + (unsigned)(i * CPL * 16) + cp_lds);
         }
     };
+    constexpr IC<C::NINSK> nik{};
+    constexpr IC<C::NINSV> niv{};
+    constexpr IC<C::RSTRK> rsk{};
+    constexpr IC<C::RSTRV> rsv{};
 
     // ---- per-lane fragment offsets in a tile (bytes).  The row term, the
     //      swizzled chunk term and the in-chunk term occupy disjoint bits, so
     //      slice m (block cb) is the slice-0 offset XOR 32m (64cb).
     // K operand (A of S^T): key row li, logical chunk 2m + h
-    const unsigned koff = 2u * (unsigned)(li * D + 8 * (h ^ swz_k<D>(li)));
+    const unsigned koff = 2u * (unsigned)(li * DK + 8 * (h ^ swz_k<DK>(li)));
     // V^T operand via transpose reads: supplying lane (16g + 4r + qq) points
     // at V[key_base + 4(g/2) + r][32 cb + 16(g%2) + 4qq] (logical column)
     const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
     const unsigned voff =
-        2u * (unsigned)((4 * (tg >> 1) + tr) * D + 16 * (tg & 1) + 4 * tq + 8 * swz_v<D>(tr));
+        2u * (unsigned)((4 * (tg >> 1) + tr) * DV + 16 * (tg & 1) + 4 * tq + 8 * swz_v<DV>(tr));
     // The ring bases are 1024-byte aligned and the slot, block and slice
     // strides are multiples of 1024, so the XOR (bits 5-7) commutes with
     // adding them: every fragment read is a per-lane base plus a constant
@@ -305,12 +324,12 @@ void prefill_kernel(Args a) {
 #pragma unroll
     for (int cb = 0; cb < NDB; ++cb) vaddr[cb] = vring + (voff ^ (64u * cb));
     auto kfrag = [&](int P, int kb, int m) {
-        return *(lds_bf16x8*)(uintptr_t)(kaddr[m] + (unsigned)(P * TB + kb * 32 * D * 2));
+        return *(lds_bf16x8*)(uintptr_t)(kaddr[m] + (unsigned)(P * TBK + kb * 32 * DK * 2));
     };
     auto vfrag = [&](int P, int cb, int kc) {
-        const unsigned addr = vaddr[cb] + (unsigned)(P * TB + 16 * kc * D * 2);
+        const unsigned addr = vaddr[cb] + (unsigned)(P * TBV + 16 * kc * DV * 2);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 16u * D));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 16u * DV));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
@@ -332,7 +351,7 @@ void prefill_kernel(Args a) {
     auto key_of = [&](int e) { return 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3); };
 
     // S^T(tile in slot P) = K Q^T, plain order
-    auto scores = [&](int P, Scores<D>& S) {
+    auto scores = [&](int P, Scores<DK, DV>& S) {
 #pragma unroll
         for (int m = 0; m < NQ; ++m)
 #pragma unroll
@@ -344,7 +363,7 @@ void prefill_kernel(Args a) {
                         kf, qf[rb][m], m == 0 ? f32x16{} : S.s[rb][kb], 0, 0, 0);
             }
     };
-    auto mask_scores = [&](Scores<D>& S, int t) {
+    auto mask_scores = [&](Scores<DK, DV>& S, int t) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int lim = row_lim[rb] - (t * BN + 4 * h);
@@ -355,7 +374,7 @@ void prefill_kernel(Args a) {
     };
     // p = 2^(s c - m) for the score pair (e, e + 1) of row block rb, rounded
     // to bf16 into the B operand of P.V; the row sum adds the rounded weights
-    auto exp_pair = [&](const Scores<D>& S, int rb, int e, float nm, float& sa, float& sb) {
+    auto exp_pair = [&](const Scores<DK, DV>& S, int rb, int e, float nm, float& sa, float& sb) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(S.s[rb][e >> 4][e & 15], cs, nm));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(S.s[rb][e >> 4][(e + 1) & 15], cs, nm));
         bf16x2 pk;
@@ -370,7 +389,7 @@ void prefill_kernel(Args a) {
     // some weight would exceed 2^12, the rows concerned (both half-wave
     // lanes of a row) take the tile's max, rescale, and recompute (the other
     // rows get the very same weights); then add the tile to the row sums.
-    auto fix_weights = [&](const Scores<D>& S, float (&sa)[RB], float (&sb)[RB]) {
+    auto fix_weights = [&](const Scores<DK, DV>& S, float (&sa)[RB], float (&sb)[RB]) {
         bool big[RB], any = false;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -407,10 +426,11 @@ void prefill_kernel(Args a) {
     // ---- prologue: copies of tiles 0 .. NRING-2; tile 0 lands before the barrier
 #pragma unroll
     for (int t = 0; t < NRING - 1; ++t) {
-        copy_tile(kh, kst, t, kslot(t), cp_kcol);
-        copy_tile(vh, vst, t, vslot(t), cp_vcol);
+        copy_tile(kh, kst, t, kslot(t), cp_kcol, cpk_r0, nik, rsk);
+        copy_tile(vh, vst, t, vslot(t), cp_vcol, cpv_r0, niv, rsv);
     }
-    wait_vm<(NRING - 2) * 2 * NINS>();
+    static_assert(NRING == 2, "the prologue waits for every copy");
+    wait_vm<0>();
     __syncthreads();
 
     // One tile step: issue the copies of tile t + 1 (into the slots of tile
@@ -418,18 +438,17 @@ void prefill_kernel(Args a) {
     // its end tile t + 1 has landed.  Overlap of the matrix and vector work
     // comes from the other workgroups on the CU.  Steps come in pairs so that
     // the ring slot of each (t % 2) is a compile-time constant.
-    static_assert(NRING == 2, "the step pairs assume a two-tile ring");
-    Scores<D> S;
+    Scores<DK, DV> S;
     bool first = true;
     auto step = [&](int t, auto slot) {
         constexpr int P = decltype(slot)::value;
         const int tc = t + 1;
         if (tc < n && (tc + 1) * BN <= a.Tk) {
-            copy_full(kh, kst, tc, kring + (unsigned)((1 - P) * TB), cpk);
-            copy_full(vh, vst, tc, vring + (unsigned)((1 - P) * TB), cpv);
+            copy_full(kh, kst, tc, kring + (unsigned)((1 - P) * TBK), cpk, nik, rsk);
+            copy_full(vh, vst, tc, vring + (unsigned)((1 - P) * TBV), cpv, niv, rsv);
         } else {
-            copy_tile(kh, kst, tc, kring + (unsigned)((1 - P) * TB), cp_kcol);
-            copy_tile(vh, vst, tc, vring + (unsigned)((1 - P) * TB), cp_vcol);
+            copy_tile(kh, kst, tc, kring + (unsigned)((1 - P) * TBK), cp_kcol, cpk_r0, nik, rsk);
+            copy_tile(vh, vst, tc, vring + (unsigned)((1 - P) * TBV), cp_vcol, cpv_r0, niv, rsv);
         }
         if (t <= last) {
             scores(P, S);
@@ -479,7 +498,7 @@ void prefill_kernel(Args a) {
         const float l_tot = pair_sum(l_run[rb]);
         if (iq[rb] < a.Tq) {
             const float inv = 1.f / l_tot;
-            bf16* orow = a.o + b * a.osb + hq * a.osh + (long long)iq[rb] * (DENSE ? D : a.ost);
+            bf16* orow = a.o + b * a.osb + hq * a.osh + (long long)iq[rb] * (DENSE ? DV : a.ost);
 #pragma unroll
             for (int cb = 0; cb < NDB; ++cb)
 #pragma unroll
@@ -495,10 +514,10 @@ void prefill_kernel(Args a) {
     }
 }
 
-template <int D>
+template <int DK, int DV>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-    const bool dense = p.qs.t == D && p.ks.t == D && p.vs.t == D && p.os.t == D;
-    typedef Cfg<D> C;
+    const bool dense = p.qs.t == DK && p.ks.t == DK && p.vs.t == DV && p.os.t == DV;
+    typedef Cfg<DK, DV> C;
     Args a;
     a.q = static_cast<const bf16*>(p.q);
     a.k = static_cast<const bf16*>(p.k);
@@ -522,13 +541,20 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     a.rope_adj = p.rope_adj;
     a.rope_pos0 = p.rope_pos0;
     const long long nwg = (long long)a.n_qt * a.G * a.R;
-    if (p.rope_tab) {   // dense layouts only (the fused-RoPE entry takes dense tensors)
+    if constexpr (DK != DV) {   // one instantiation: dense, no RoPE (what attn_fwd_dv takes)
+        if (p.rope_tab || !dense) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, true, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0,
+                           stream, a);
+    } else if (p.rope_tab) {   // dense layouts only (the fused-RoPE entry takes dense tensors)
         if (!dense) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((prefill_kernel<D, true, true>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, true, true>), dim3((unsigned)nwg), dim3(C::NW * 64), 0,
+                           stream, a);
     } else if (dense) {
-        hipLaunchKernelGGL((prefill_kernel<D, true, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, true, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0,
+                           stream, a);
     } else {
-        hipLaunchKernelGGL((prefill_kernel<D, false, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, false, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0,
+                           stream, a);
     }
     return hipGetLastError();
 }
@@ -536,7 +562,9 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const FwdParams& p, hipStream_t stream) {
-    return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
+    const int dv = p.dv ? p.dv : p.d;
+    if (p.d == 64) return dv == 64 ? launch_d<64, 64>(p, stream) : launch_d<64, 128>(p, stream);
+    return dv == 128 ? launch_d<128, 128>(p, stream) : launch_d<128, 64>(p, stream);
 }
 
 }  // namespace rocattn

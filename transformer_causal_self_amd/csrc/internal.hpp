@@ -32,6 +32,7 @@ struct FwdParams {
     void* o;
     float* lse;      // may be null; always dense [B][Hq][Tq]
     int B, Hq, Hkv, Tq, Tk, d;
+    int dv = 0;      // width of v and o rows when it differs from d (0: d)
     float scale;
     int causal;
     int q_offset;
