@@ -871,3 +871,63 @@ def test_attn_fwd_dv_equal_widths_is_attn_fwd_bit_exact(dtype, d):
     b = ra.attn_fwd(q, k, v, scale=0.1)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_bwd_workload3_full():
+    """The GQA shape the bench times the gradients on (B2 Hq32 Hkv8 T4096
+    d128, causal): dq of the last 32 rows of every head against the oracle,
+    and the softmax's column sums for dk and dv."""
+    w = wl.WORKLOADS[3]
+    say("bwd", w.name)
+    q, k, v = wl.inputs(w)
+    dO = _rand(q.shape, torch.bfloat16, 3003)
+    dq, dk, dv = _gpu_bwd(q, k, v, dO, w.scale, True, 0)
+    T = w.Tq
+    tail = slice(T - 32, T)
+    want_dq, _, _ = oracle.attn_bwd(q[:, :, tail], k, v, dO[:, :, tail], w.scale, causal=True,
+                                    q_offset=T - 32)
+    assert _grad_err(dq[:, :, tail], want_dq) <= TOL[torch.bfloat16]
+    dk64, dv64, dO64 = f64(dk), f64(dv), f64(dO)
+    R = w.Hq // w.Hkv
+    dO_grp = dO64.reshape(w.B, w.Hkv, R, T, w.d).sum(axis=2)   # rows of a K/V head's group
+    bound_k = 2.0 ** -8 * np.abs(dk64).sum(axis=2) + 1e-3
+    assert np.all(np.abs(dk64.sum(axis=2)) <= bound_k)
+    bound_v = 2.0 ** -8 * (np.abs(dv64).sum(axis=2) + np.abs(dO_grp).sum(axis=2)) + 1e-3
+    assert np.all(np.abs(dv64.sum(axis=2) - dO_grp.sum(axis=2)) <= bound_v)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+def test_attn_fwd_dv_workload3_shape(dk, dv):
+    """attn_fwd_dv at the size the bench times it (B2 Hq32 Hkv8 T4096,
+    causal): the last 64 rows of every head against the oracle (a row needs
+    only its own query), and rows 0 (= v_0, bit for bit)."""
+    w = wl.WORKLOADS[3]
+    say("attn_fwd_dv full", dk, dv)
+    q, k, _ = wl.random_qkv(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, dk, seed=3001)
+    _, _, v = wl.random_qkv(w.B, w.Hq, w.Hkv, 1, w.Tk, dv, seed=3002)
+    o = ra.attn_fwd_dv(*gpu(q, k, v), scale=dk ** -0.5)
+    torch.cuda.synchronize()
+    o = o.cpu()
+    T = w.Tq
+    want = oracle.attn(q[:, :, T - 64:], k, v, dk ** -0.5, q_offset=T - 64)
+    err = float(np.max(np.abs(f64(o[:, :, T - 64:]) - want)))
+    assert err <= TOL[torch.bfloat16], err
+    rep = w.Hq // w.Hkv
+    assert torch.equal(o[:, :, 0], v[:, :, 0].repeat_interleave(rep, dim=1))
+
+
+def test_attn_fwd_rope_workload4_equals_unfused_bit_exact():
+    """The fused RoPE prefill at the long-context size the bench steps it on
+    (B1 Hq32 Hkv8 T16384 d128) gives the bits of rope_apply then attention
+    (whose sampled rows the end-to-end test checks against the oracle)."""
+    w = wl.WORKLOADS[4]
+    say("attn_fwd_rope", w.name)
+    q, k, v = gpu(*wl.inputs(w))
+    k1 = k.clone()
+    o1 = ra.attn_fwd_rope(q, k1, v, scale=w.scale, base=w.rope_base)
+    q2, k2 = q.clone(), k.clone()
+    ra.rope_apply(q2, k2, pos0=0, base=w.rope_base)
+    o2 = ra.attn_fwd(q2, k2, v, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2)
+    assert torch.equal(o1, o2)
