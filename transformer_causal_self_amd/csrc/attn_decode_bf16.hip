@@ -32,7 +32,7 @@
 namespace rocattn {
 namespace {
 
-constexpr int kSplitTarget = 4096;  // workgroups the split aims for in total
+constexpr int kSplitTarget = 1536;  // workgroups the split aims for in total (swept: 1024-8192)
 constexpr int kLdsFloats = 16384;   // 64 KiB of LDS per workgroup at most
 
 struct DecArgs {
