@@ -27,12 +27,14 @@
 //    which equals the softmax over the whole row.
 #include <math.h>
 
+#include <atomic>
+
 #include "internal.hpp"
 
 namespace rocattn {
 namespace {
 
-constexpr int kSplitTarget = 1536;  // workgroups the split aims for in total (swept: 1024-8192)
+constexpr int kSplitMax = 2048;     // workgroups the split may use in total (bounds the workspace)
 constexpr int kLdsFloats = 16384;   // 64 KiB of LDS per workgroup at most
 
 struct DecArgs {
@@ -241,20 +243,74 @@ int chunk_max(int R, int D) {
 }
 
 int split_target(int G) {
-    const int s = (kSplitTarget + G - 1) / G;
+    const int s = (kSplitMax + G - 1) / G;
     return s < 1 ? 1 : s;
 }
 
-// chunk length and split count for kv_len visible keys
+// Workgroups of decode_split_kernel<D, pad_r(R)> one CU holds at once by
+// its registers alone (asked of the runtime once per instantiation).
+int resident_by_regs(int R, int D) {
+    static std::atomic<int> cache[2][3];
+    const int rp = pad_r(R), i = D == 64 ? 0 : 1, j = rp == 4 ? 0 : (rp == 8 ? 1 : 2);
+    int n = cache[i][j].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    const void* f = D == 64 ? (rp == 4 ? (const void*)decode_split_kernel<64, 4>
+                                       : rp == 8 ? (const void*)decode_split_kernel<64, 8>
+                                                 : (const void*)decode_split_kernel<64, 16>)
+                            : (rp == 4 ? (const void*)decode_split_kernel<128, 4>
+                                       : rp == 8 ? (const void*)decode_split_kernel<128, 8>
+                                                 : (const void*)decode_split_kernel<128, 16>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) != hipSuccess || n < 1) n = 1;
+    cache[i][j].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Chunk length and split count for kv_len visible keys.  A chunk is one
+// workgroup and the step is HBM-bound, so a CU's time is about the chunks it
+// gets times their length (plus a fixed cost worth ~256 keys), as long as
+// enough workgroups sit on it at once to keep the memory busy (about 3;
+// fewer stretch the time in proportion).  Longer chunks need more LDS, so
+// fewer fit on a CU.  The split count S is chosen to minimise
+//     ceil(G S / CUs) (C + 256) max(1, 3 / resident),
+//     resident = min(workgroups that fit a CU, ceil(G S / CUs)),
+// over ceil(kv_len / chunk_max) <= S <= max(that, ceil(kSplitMax / G)).
+// (Measured on the decode shapes tried, it ranks the splits as they time.)
 void plan(int G, int R, int D, int kv_len, int* C_out, int* S_out) {
     const int c_max = chunk_max(R, D);
-    const int s_target = split_target(G);
-    int C = (kv_len + s_target - 1) / s_target;
-    C = (C + 63) & ~63;
-    if (C < 64) C = 64;
-    if (C > c_max) C = c_max;
-    *C_out = C;
-    *S_out = (kv_len + C - 1) / C;
+    const int rp = pad_r(R);
+    int dev = 0, cus = 256, lds_cu = 160 * 1024;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int x;
+        if (hipDeviceGetAttribute(&x, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && x > 0) cus = x;
+        if (hipDeviceGetAttribute(&x, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+            x > 0)
+            lds_cu = x;
+    }
+    const int by_regs = resident_by_regs(R, D);
+    const int s_lo = (kv_len + c_max - 1) / c_max;
+    const int s_hi = s_lo > split_target(G) ? s_lo : split_target(G);
+    double best = 0.0;
+    int best_C = c_max, best_S = s_lo;
+    for (int S = s_lo; S <= s_hi; ++S) {
+        int C = (kv_len + S - 1) / S;
+        C = (C + 63) & ~63;
+        if (C < 64) C = 64;
+        if (C > c_max) C = c_max;
+        const int S_eff = (kv_len + C - 1) / C;
+        if (S_eff != S) continue;   // another S gives this chunk length
+        const long long lds = (long long)sizeof(float) * (2LL * rp * C + 4LL * rp * D);
+        const int fit = (int)(lds_cu / lds) < by_regs ? (int)(lds_cu / lds) : by_regs;
+        const long long per_cu = ((long long)G * S + cus - 1) / cus;
+        const double resident = fit < per_cu ? (double)(fit > 0 ? fit : 1) : (double)per_cu;
+        const double cost = (double)per_cu * (C + 256) * (resident < 3.0 ? 3.0 / resident : 1.0);
+        if (S == s_lo || cost < best) {
+            best = cost;
+            best_C = C;
+            best_S = S;
+        }
+    }
+    *C_out = best_C;
+    *S_out = best_S;
 }
 
 template <int D, int RP>
