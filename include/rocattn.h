@@ -98,7 +98,9 @@ typedef enum {
  *
  * Supported head sizes: bf16 d_head in {64, 128}; f32 d_head <= 256 with
  * d_head % 4 == 0.  bf16 with Tq == 1 runs the split-K decode kernels, which
- * need a workspace: attn_fwd takes it from the stream-ordered allocator
+ * need a workspace, and a small bf16 prefill (fewer than 512 tiles of 128
+ * query rows over all heads) is split over the keys when it has one:
+ * attn_fwd takes attn_workspace_bytes() from the stream-ordered allocator
  * (hipMallocAsync / hipFreeAsync on `stream`); use attn_fwd_ws to pass one.
  * Returns a rocattn_status.
  */
@@ -107,9 +109,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o,
              float scale, int causal, int q_offset, int dtype, void* stream);
 
 /*
- * attn_workspace_bytes -- bytes of device workspace attn_fwd_ws needs for
- * these sizes (0 when the chosen kernels need none).  Returns 0 for
- * arguments attn_fwd would reject.
+ * attn_workspace_bytes -- bytes of device workspace attn_fwd_ws uses for
+ * these sizes: required for a bf16 decode step (Tq == 1); for a small dense
+ * bf16 prefill, optional (the partial results of its key splits, 4 (d + 2)
+ * bytes per query row and split); 0 when the chosen kernels use none.  The
+ * split count depends on the sizes only (not on q_offset or causal).
+ * Returns 0 for arguments attn_fwd would reject.
  */
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d_head, int dtype);
 
@@ -118,9 +123,12 @@ size_t attn_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d_head, 
  * log-sum-exp output.
  *
  *   workspace, ws_bytes  device buffer of at least attn_workspace_bytes()
- *             bytes (may be NULL when that is 0); contents on entry are
- *             ignored and on return are unspecified.  Calls that share a
- *             workspace must be ordered on one stream.
+ *             bytes (may be NULL when that is 0).  A bf16 decode step
+ *             requires it (ERR_WORKSPACE); a small prefill uses it only when
+ *             it is at least that large and otherwise runs unsplit (the two
+ *             differ by float32 summation order, within the bf16 contract).
+ *             Contents on entry are ignored and on return are unspecified.
+ *             Calls that share a workspace must be ordered on one stream.
  *   lse       NULL, or float32 [B][Hq][Tq]: lse = log(sum_j exp(scale q_i.k_j))
  *             over the visible keys j (natural log), for a later backward
  *             pass or for merging partial attentions.

@@ -465,7 +465,10 @@ def _dense_and_strided(q, k, v, scale, causal, q_offset, make_views, lse=False):
     (it returns q, k, v views holding the same values, and an output view)."""
     qd, kd, vd = gpu(q, k, v)
     B, Hq, Tq, d = q.shape
-    nb = ra.attn_workspace_bytes(B, Hq, k.shape[1], Tq, k.shape[2], d, q.dtype)
+    # only the workspace a call requires (a decode step's): with the optional
+    # one a small dense prefill splits over the keys and a strided one does
+    # not, and the two then round differently
+    nb = ra.attn_workspace_bytes(B, Hq, k.shape[1], Tq, k.shape[2], d, q.dtype) if Tq == 1 else 0
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=DEV) if nb else None
     want = torch.empty_like(qd)
     lw = torch.empty(B, Hq, Tq, dtype=torch.float32, device=DEV) if lse else None
@@ -868,7 +871,9 @@ def test_attn_fwd_dv_equal_widths_is_attn_fwd_bit_exact(dtype, d):
     say("attn_fwd_dv equal widths", dtype, d)
     q, k, v = gpu(*wl.random_qkv(2, 8, 2, 300, 300, d, dtype, seed=41))
     a = ra.attn_fwd_dv(q, k, v, scale=0.1)
-    b = ra.attn_fwd(q, k, v, scale=0.1)
+    # attn_fwd_ws without a workspace: the kernel attn_fwd_dv runs (attn_fwd
+    # itself would split this small prefill over the keys)
+    b = ra.attn_fwd_ws(q, k, v, torch.empty_like(q), None, None, scale=0.1)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
@@ -931,3 +936,33 @@ def test_attn_fwd_rope_workload4_equals_unfused_bit_exact():
     torch.cuda.synchronize()
     assert torch.equal(k1, k2)
     assert torch.equal(o1, o2)
+
+
+# ---- small prefills split over the keys (a workspace of attn_workspace_bytes
+#      lets a launch that would leave the chip idle use more workgroups)
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tk,d,causal,qo", [
+    (1, 32, 8, 512, 4096, 128, True, 3584),    # a chunk at the end of a cache
+    (1, 8, 2, 300, 2000, 64, True, 1700),
+    (1, 4, 4, 129, 1500, 128, False, 0),
+    (2, 2, 1, 70, 3000, 64, True, 2930),
+    (1, 4, 2, 1000, 1000, 128, True, 0),       # split ranges where early rows see nothing
+])
+def test_prefill_split_matches_oracle(B, Hq, Hkv, Tq, Tk, d, causal, qo):
+    say("prefill split", B, Hq, Hkv, Tq, Tk, d, causal, qo)
+    nb = ra.attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, torch.bfloat16)
+    assert nb > 0   # these shapes take the split
+    q, k, v = wl.random_qkv(B, Hq, Hkv, Tq, Tk, d, torch.bfloat16, seed=500 + Tq)
+    qd, kd, vd = gpu(q, k, v)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    o1 = torch.empty_like(qd)
+    lse1 = torch.empty(B, Hq, Tq, dtype=torch.float32, device=DEV)
+    ra.attn_fwd_ws(qd, kd, vd, o1, ws, lse1, scale=d ** -0.5, causal=causal, q_offset=qo)
+    o2 = torch.empty_like(qd)    # no workspace: one workgroup per query tile
+    ra.attn_fwd_ws(qd, kd, vd, o2, None, None, scale=d ** -0.5, causal=causal, q_offset=qo)
+    torch.cuda.synchronize()
+    want, want_lse = oracle.attn(q, k, v, d ** -0.5, causal=causal, q_offset=qo, return_lse=True)
+    for o in (o1, o2):
+        err = float(np.max(np.abs(f64(o) - want)))
+        assert err <= TOL[torch.bfloat16], err
+    assert float(np.max(np.abs(f64(lse1) - want_lse))) <= 2.0e-3

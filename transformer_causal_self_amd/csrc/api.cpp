@@ -73,19 +73,55 @@ bool uses_decode(int dtype, int Tq, int Hq, int Hkv, int d) {
     return dtype == ROCATTN_BF16 && Tq == 1 && rocattn::decode_bf16_supported(Hq, Hkv, d);
 }
 
-size_t workspace_for(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
+// Workspace a call cannot do without: the split-K decode's partial results.
+size_t workspace_required(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
     if (!uses_decode(dtype, Tq, Hq, Hkv, d)) return 0;
     return rocattn::decode_workspace_bytes(B, Hq, Hkv, Tk, d);
 }
 
+// Workspace a call uses when given: the required bytes, or for a small bf16
+// prefill the partial results of its key splits (optional).
+size_t workspace_for(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
+    const size_t req = workspace_required(B, Hq, Hkv, Tq, Tk, d, dtype);
+    if (req > 0 || dtype != ROCATTN_BF16) return req;
+    return rocattn::prefill_split_bytes(B, Hq, Tq, d, rocattn::prefill_splits(B, Hq, Tq, Tk, d, d));
+}
+
+// Bytes of the caller's workspace a call will use: the required bytes
+// (ERR_WORKSPACE when missing or short, signalled by returning SIZE_MAX), or
+// the optional bytes when the caller gave at least that much, else 0.
+size_t workspace_use(size_t req, size_t want, const void* ws, size_t ws_bytes) {
+    if (req > 0) return (ws && ws_bytes >= req) ? req : SIZE_MAX;
+    return (want > 0 && ws && ws_bytes >= want) ? want : 0;
+}
+
 int launch(const FwdParams& p, int dtype, hipStream_t stream, void* ws, size_t ws_bytes) {
     hipError_t e;
-    if (dtype == ROCATTN_F32)
+    if (dtype == ROCATTN_F32) {
         e = rocattn::launch_fwd_f32(p, stream);
-    else if (uses_decode(dtype, p.Tq, p.Hq, p.Hkv, p.d))
+    } else if (uses_decode(dtype, p.Tq, p.Hq, p.Hkv, p.d)) {
         e = rocattn::launch_decode_bf16(p, ws, ws_bytes, stream);
-    else
-        e = rocattn::launch_prefill_bf16(p, stream);
+    } else {
+        // a small prefill is split over the keys when the caller's workspace
+        // holds the partial results (and the layout is dense); otherwise one
+        // workgroup per (query tile, head) as usual
+        const int ks = rocattn::prefill_splits(p.B, p.Hq, p.Tq, p.Tk, p.d, p.d);
+        const size_t need = rocattn::prefill_split_bytes(p.B, p.Hq, p.Tq, p.d, ks);
+        const bool dense = p.qs.t == p.d && p.ks.t == p.d && p.vs.t == p.d && p.os.t == p.d;
+        if (ks > 1 && ws && ws_bytes >= need && dense) {
+            FwdParams q = p;
+            const long long rows = (long long)p.B * p.Hq * p.Tq;
+            q.nsplit = ks;
+            q.part_o = static_cast<float*>(ws);
+            q.part_ml = q.part_o + (size_t)rows * ks * p.d;
+            e = rocattn::launch_prefill_bf16(q, stream);
+            if (e == hipSuccess)
+                e = rocattn::launch_combine_bf16(q.part_o, q.part_ml, p.o, p.lse, rows, ks, p.Hq, p.Tq, p.os,
+                                                 p.d, stream);
+        } else {
+            e = rocattn::launch_prefill_bf16(p, stream);
+        }
+    }
     return e == hipSuccess ? ROCATTN_OK : ROCATTN_ERR_HIP;
 }
 
@@ -197,7 +233,7 @@ ROCATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, i
     const FwdParams p = make_params(q, k, v, o, nullptr, B, Hq, Hkv, Tq, Tk, d_head, scale,
                                     causal, q_offset);
     const size_t wsb = workspace_for(B, Hq, Hkv, Tq, Tk, d_head, dtype);
-    if (wsb == 0) return launch(p, dtype, s, nullptr, 0);
+    if (wsb == 0) return launch(p, dtype, s, nullptr, 0);   // else allocated for the call
     void* ws = nullptr;
     if (hipMallocAsync(&ws, wsb, s) != hipSuccess) return ROCATTN_ERR_HIP;
     st = launch(p, dtype, s, ws, wsb);
@@ -222,9 +258,10 @@ ROCATTN_API int attn_fwd_ws(const void* q, const void* k, const void* v, void* o
     int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d_head, scale, causal, q_offset, dtype,
                        lse);
     if (st != ROCATTN_OK) return st;
-    const size_t wsb = workspace_for(B, Hq, Hkv, Tq, Tk, d_head, dtype);
+    const size_t wsb = workspace_use(workspace_required(B, Hq, Hkv, Tq, Tk, d_head, dtype),
+                                     workspace_for(B, Hq, Hkv, Tq, Tk, d_head, dtype), workspace, ws_bytes);
+    if (wsb == SIZE_MAX) return ROCATTN_ERR_WORKSPACE;
     if (wsb > 0) {
-        if (!workspace || ws_bytes < wsb) return ROCATTN_ERR_WORKSPACE;
         if (!aligned16(workspace)) return ROCATTN_ERR_ALIGN;
         const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
         const size_t qb = (size_t)B * Hq * Tq * d_head * elt;
@@ -236,7 +273,7 @@ ROCATTN_API int attn_fwd_ws(const void* q, const void* k, const void* v, void* o
     }
     const FwdParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d_head, scale, causal,
                                     q_offset);
-    return launch(p, dtype, static_cast<hipStream_t>(stream), workspace, ws_bytes);
+    return launch(p, dtype, static_cast<hipStream_t>(stream), wsb ? workspace : nullptr, wsb);
 }
 
 ROCATTN_API int attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
@@ -252,9 +289,10 @@ ROCATTN_API int attn_fwd_strided(const void* q, const void* k, const void* v, vo
     int status = check_strided(q, k, v, o, B, Hq, Hkv, Tq, Tk, d_head, scale, causal, q_offset,
                                dtype, lse, st);
     if (status != ROCATTN_OK) return status;
-    const size_t wsb = workspace_for(B, Hq, Hkv, Tq, Tk, d_head, dtype);
+    const size_t wsb = workspace_use(workspace_required(B, Hq, Hkv, Tq, Tk, d_head, dtype),
+                                     workspace_for(B, Hq, Hkv, Tq, Tk, d_head, dtype), workspace, ws_bytes);
+    if (wsb == SIZE_MAX) return ROCATTN_ERR_WORKSPACE;
     if (wsb > 0) {
-        if (!workspace || ws_bytes < wsb) return ROCATTN_ERR_WORKSPACE;
         if (!aligned16(workspace)) return ROCATTN_ERR_ALIGN;
         const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
         const size_t eq = (size_t)extent(B, Hq, Tq, d_head, st[0]) * elt;
@@ -269,7 +307,7 @@ ROCATTN_API int attn_fwd_strided(const void* q, const void* k, const void* v, vo
     FwdParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d_head, scale, causal,
                               q_offset);
     p.qs = st[0]; p.ks = st[1]; p.vs = st[2]; p.os = st[3];
-    return launch(p, dtype, static_cast<hipStream_t>(stream), workspace, ws_bytes);
+    return launch(p, dtype, static_cast<hipStream_t>(stream), wsb ? workspace : nullptr, wsb);
 }
 
 ROCATTN_API int rope_apply_ex(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head,
@@ -349,9 +387,10 @@ ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, 
             if (overlaps(lse, lb, bufs[i], lens[i])) return ROCATTN_ERR_SHAPE;
     }
     const int Tk = pos + Tn;
-    const size_t wsb = workspace_for(B, Hq, Hkv, Tn, Tk, d_head, dtype);
+    const size_t wsb = workspace_use(workspace_required(B, Hq, Hkv, Tn, Tk, d_head, dtype),
+                                     workspace_for(B, Hq, Hkv, Tn, Tk, d_head, dtype), workspace, ws_bytes);
+    if (wsb == SIZE_MAX) return ROCATTN_ERR_WORKSPACE;
     if (wsb > 0) {
-        if (!workspace || ws_bytes < wsb) return ROCATTN_ERR_WORKSPACE;
         if (!aligned16(workspace)) return ROCATTN_ERR_ALIGN;
         for (int i = 0; i < 6; ++i)
             if (overlaps(workspace, wsb, bufs[i], lens[i])) return ROCATTN_ERR_SHAPE;
@@ -366,7 +405,7 @@ ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, 
                               pos);
     p.ks = {(long long)Hkv * Tmax * d_head, (long long)Tmax * d_head, d_head};
     p.vs = p.ks;
-    return launch(p, dtype, s, workspace, ws_bytes);
+    return launch(p, dtype, s, wsb ? workspace : nullptr, wsb);
 }
 
 ROCATTN_API int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, int B, int Hq,

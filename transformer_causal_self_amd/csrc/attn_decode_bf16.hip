@@ -60,6 +60,7 @@ struct CombArgs {
     float* lse;
     int S;
     int Hq;
+    int Tq;          // query rows per head (1 for a decode step)
     Strides os;
 };
 
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(CombArgs a) {
-    const size_t row = blockIdx.x;             // b * Hq + hq
+    const size_t row = blockIdx.x;             // (b * Hq + hq) * Tq + i
     const int col = threadIdx.x;
     const float* mlr = a.ml + row * a.S * 2;
     const float* op = a.o_part + row * a.S * D + col;
@@ -229,8 +230,56 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(CombArgs a) {
             acc = fmaf(w, ov[u], acc);
         }
     }
-    const int b = (int)(row / a.Hq), hq = (int)(row - (size_t)b * a.Hq);
-    a.o[b * a.os.b + hq * a.os.h + col] = (bf16)(acc / den);
+    const size_t bh = row / a.Tq;
+    const int i = (int)(row - bh * a.Tq);
+    const int b = (int)(bh / a.Hq), hq = (int)(bh - (size_t)b * a.Hq);
+    a.o[b * a.os.b + hq * a.os.h + (long long)i * a.os.t + col] = (bf16)(acc / den);
+    if (a.lse && col == 0) a.lse[row] = (M + log2f(den)) * kLn2;
+}
+
+// The same merge for a prefill's key splits (S <= 8 partials per row, many
+// rows): D / 4 lanes per row, four columns each, 256 / (D / 4) rows per
+// block, every partial of a lane loaded at once.
+template <int D>
+__global__ __launch_bounds__(256) void combine_rows_kernel(CombArgs a, long long rows) {
+    constexpr int TPR = D / 4, RPB = 256 / TPR;
+    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int col = (threadIdx.x % TPR) * 4;
+    if (row >= rows) return;
+    const float* mlr = a.ml + row * a.S * 2;
+    const float* op = a.o_part + row * a.S * D + col;
+    float mv[8], lv[8];
+    float4 ov[8];
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const bool ok = s < a.S;
+        mv[s] = ok ? mlr[2 * s] : -INFINITY;
+        lv[s] = ok ? mlr[2 * s + 1] : 0.f;
+        ov[s] = ok ? *reinterpret_cast<const float4*>(op + (size_t)s * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+        M = fmaxf(M, mv[s]);
+    }
+    float den = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const float w = s < a.S ? exp2f(mv[s] - M) : 0.f;
+        den = fmaf(w, lv[s], den);
+        acc.x = fmaf(w, ov[s].x, acc.x);
+        acc.y = fmaf(w, ov[s].y, acc.y);
+        acc.z = fmaf(w, ov[s].z, acc.z);
+        acc.w = fmaf(w, ov[s].w, acc.w);
+    }
+    const float inv = 1.f / den;
+    const long long bh = row / a.Tq;
+    const int i = (int)(row - bh * a.Tq);
+    const int b = (int)(bh / a.Hq), hq = (int)(bh - (long long)b * a.Hq);
+    bf16x4 val;
+    val[0] = (bf16)(acc.x * inv);
+    val[1] = (bf16)(acc.y * inv);
+    val[2] = (bf16)(acc.z * inv);
+    val[3] = (bf16)(acc.w * inv);
+    *reinterpret_cast<bf16x4*>(a.o + b * a.os.b + hq * a.os.h + (long long)i * a.os.t + col) = val;
     if (a.lse && col == 0) a.lse[row] = (M + log2f(den)) * kLn2;
 }
 
@@ -349,6 +398,7 @@ hipError_t launch_dec_d(const FwdParams& p, float* o_part, float* ml, int C, int
     c.lse = p.lse;
     c.S = S;
     c.Hq = p.Hq;
+    c.Tq = 1;
     c.os = p.os;
     hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(p.B * p.Hq), dim3(D), 0, stream, c);
     return hipGetLastError();
@@ -359,6 +409,28 @@ int visible_keys(int Tk, int causal, int q_offset) {
 }
 
 }  // namespace
+
+hipError_t launch_combine_bf16(const float* part_o, const float* part_ml, void* o, float* lse,
+                               long long rows, int S, int Hq, int Tq, const Strides& os, int d,
+                               hipStream_t stream) {
+    CombArgs c;
+    c.o_part = part_o;
+    c.ml = part_ml;
+    c.o = static_cast<bf16*>(o);
+    c.lse = lse;
+    c.S = S;
+    c.Hq = Hq;
+    c.Tq = Tq;
+    c.os = os;
+    if (S > 8) return hipErrorInvalidValue;
+    if (d == 64)
+        hipLaunchKernelGGL(combine_rows_kernel<64>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, c,
+                           rows);
+    else
+        hipLaunchKernelGGL(combine_rows_kernel<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, c,
+                           rows);
+    return hipGetLastError();
+}
 
 bool decode_bf16_supported(int Hq, int Hkv, int d) {
     return (d == 64 || d == 128) && Hq / Hkv <= 16;

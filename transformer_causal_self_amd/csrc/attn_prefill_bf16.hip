@@ -114,6 +114,11 @@ struct Args {
     // i at position rope_pos0 + i; rope_adj picks the channel pairing
     const float2* rope;
     int rope_adj, rope_pos0;
+    // split over the keys: ks workgroups per (query tile, head), each writing
+    // its unnormalised output [row][ks][DV] and (max, weight sum) [row][ks][2]
+    int ks;
+    float* part_o;
+    float* part_ml;
 };
 
 // RoPE of a lane's query fragments (channels 16m + 8h .. +7 of one row)
@@ -170,7 +175,10 @@ struct Scores {
 // every token stride is a compile-time constant (the strided instantiation
 // reads the strides from Args).
 // ROPE: the query rows are turned by RoPE at load (a.rope holds the table).
-template <int DK, int DV, bool DENSE, bool ROPE>
+// SPLIT: a.ks workgroups share a (query tile, head), each taking one
+// contiguous run of its key tiles and writing partial results that
+// combine_kernel merges (for launches too small to fill the chip).
+template <int DK, int DV, bool DENSE, bool ROPE, bool SPLIT = false>
 __global__ __launch_bounds__((Cfg<DK, DV>::NW * 64))
 __attribute__((amdgpu_waves_per_eu(Cfg<DK, DV>::WPE, Cfg<DK, DV>::WPE)))
 void prefill_kernel(Args a) {
@@ -188,8 +196,16 @@ void prefill_kernel(Args a) {
     const int h = lane >> 5, li = lane & 31;
 
     // ---- which (query tile, batch, query head) this workgroup owns
-    int qt, g, rep;
-    {
+    int qt, g, rep, split = 0;
+    if constexpr (SPLIT) {   // longest first, the splits of a tile side by side
+        split = (int)(blockIdx.x % a.ks);
+        const int w = (int)(blockIdx.x / a.ks);
+        const int per = a.G * a.R;
+        const int rank = w / per, rem = w - rank * per;
+        g = rem / a.R;
+        rep = rem % a.R;
+        qt = a.n_qt - 1 - rank;
+    } else {
         // Workgroup w runs on XCD w % 8, as the (w / 8)-th of that XCD, and
         // an XCD hands its workgroups round-robin to its 32 CUs.  Sizes go
         // longest-first; reversing every other run of 32 evens out the sum
@@ -249,6 +265,12 @@ void prefill_kernel(Args a) {
     // ---- visibility limits (the wave's are wave-uniform)
     const int kv_end = a.causal ? min(a.Tk, a.q_offset + i0 + BM) : a.Tk;
     const int n = (kv_end + BN - 1) / BN;    // key tiles of the workgroup
+    int t_lo = 0, t_hi = n;                  // the tiles this workgroup visits
+    if constexpr (SPLIT) {
+        const int per = (n + a.ks - 1) / a.ks;
+        t_lo = min(n, split * per);
+        t_hi = min(n, t_lo + per);
+    }
     int row_lim[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) row_lim[rb] = a.causal ? min(a.Tk - 1, a.q_offset + iq[rb]) : a.Tk - 1;
@@ -423,11 +445,12 @@ void prefill_kernel(Args a) {
         for (int rb = 0; rb < RB; ++rb) l_run[rb] += sa[rb] + sb[rb];
     };
 
-    // ---- prologue: copies of tiles 0 .. NRING-2; tile 0 lands before the barrier
+    // ---- prologue: copies of tiles t_lo .. t_lo + NRING-2 (slot = tile - t_lo);
+    //      tile t_lo lands before the barrier
 #pragma unroll
     for (int t = 0; t < NRING - 1; ++t) {
-        copy_tile(kh, kst, t, kslot(t), cp_kcol, cpk_r0, nik, rsk);
-        copy_tile(vh, vst, t, vslot(t), cp_vcol, cpv_r0, niv, rsv);
+        copy_tile(kh, kst, t_lo + t, kslot(t), cp_kcol, cpk_r0, nik, rsk);
+        copy_tile(vh, vst, t_lo + t, vslot(t), cp_vcol, cpv_r0, niv, rsv);
     }
     static_assert(NRING == 2, "the prologue waits for every copy");
     wait_vm<0>();
@@ -460,6 +483,10 @@ void prefill_kernel(Args a) {
 #pragma unroll
                     for (int e = 0; e < NE; ++e) mx = fmaxf(mx, S.s[rb][e >> 4][e & 15]);
                     m_run[rb] = pair_max(mx) * cs;
+                    // a split's first tile may hold no key some rows see (then
+                    // none of its tiles does): keep their reference finite
+                    if constexpr (SPLIT)
+                        if (m_run[rb] == -INFINITY) m_run[rb] = 0.f;
                 }
                 first = false;
             }
@@ -486,11 +513,34 @@ void prefill_kernel(Args a) {
         wait_vm<0>();   // tile t + 1 has landed
         __syncthreads();
     };
-    for (int t = 0; t < n; t += 2) {
+    for (int t = t_lo; t < t_hi; t += 2) {
         step(t, IC<0>{});
-        if (t + 1 < n) step(t + 1, IC<1>{});
+        if (t + 1 < t_hi) step(t + 1, IC<1>{});
     }
     wait_vm<0>();   // no copy into LDS outlives the workgroup
+
+    if constexpr (SPLIT) {   // partial output (relative to m_run), max and weight sum
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float l_tot = pair_sum(l_run[rb]);
+            if (iq[rb] < a.Tq) {
+                const size_t prow = ((size_t)(b * a.Hq + hq) * a.Tq + iq[rb]) * a.ks + split;
+                float* po = a.part_o + prow * DV;
+#pragma unroll
+                for (int cb = 0; cb < NDB; ++cb)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        *reinterpret_cast<float4*>(po + 32 * cb + 8 * g4 + 4 * h) =
+                            make_float4(oacc[rb][cb][4 * g4], oacc[rb][cb][4 * g4 + 1],
+                                        oacc[rb][cb][4 * g4 + 2], oacc[rb][cb][4 * g4 + 3]);
+                if (h == 0) {
+                    a.part_ml[2 * prow] = l_tot > 0.f ? m_run[rb] : -INFINITY;
+                    a.part_ml[2 * prow + 1] = l_tot;
+                }
+            }
+        }
+        return;
+    }
 
     // ---- epilogue: O = O^T / l; lane holds columns 32cb + 8g4 + 4h .. +3 of row iq[rb]
 #pragma unroll
@@ -541,6 +591,19 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     a.rope_adj = p.rope_adj;
     a.rope_pos0 = p.rope_pos0;
     const long long nwg = (long long)a.n_qt * a.G * a.R;
+    a.ks = p.nsplit;
+    a.part_o = p.part_o;
+    a.part_ml = p.part_ml;
+    if (p.nsplit > 1) {   // split over the keys: dense, no RoPE, one width
+        if constexpr (DK != DV) {
+            return hipErrorInvalidValue;
+        } else {
+            if (p.rope_tab || !dense) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((prefill_kernel<DK, DV, true, false, true>), dim3((unsigned)(nwg * p.nsplit)),
+                               dim3(C::NW * 64), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     if constexpr (DK != DV) {   // one instantiation: dense, no RoPE (what attn_fwd_dv takes)
         if (p.rope_tab || !dense) return hipErrorInvalidValue;
         hipLaunchKernelGGL((prefill_kernel<DK, DV, true, false>), dim3((unsigned)nwg), dim3(C::NW * 64), 0,
@@ -560,6 +623,29 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Key splits: the launch has n_qt * B * Hq workgroups of 128 query rows; with
+// fewer than two per CU of the 256 (a short chunk of queries over a long
+// cache, a single short sequence) the chip idles, so each (query tile,
+// head) is split over the keys into ks workgroups -- enough for about two
+// per CU, at most 8, and each keeping at least 4 key tiles.  Decided from
+// the sizes alone so the workspace can be sized before the call.
+int prefill_splits(int B, int Hq, int Tq, int Tk, int d, int dv) {
+    constexpr long long kWant = 512;   // workgroups a split launch aims for (two per CU)
+    const long long nwg = (long long)((Tq + 127) / 128) * B * Hq;
+    if (nwg <= 0 || nwg >= kWant || d != dv) return 1;
+    const int bn = (d == 64 && dv == 64) ? 64 : 32;
+    const long long tiles = (Tk + bn - 1) / bn;
+    long long ks = (kWant + nwg - 1) / nwg;
+    if (ks > 8) ks = 8;
+    if (ks > tiles / 4) ks = tiles / 4;
+    return ks < 2 ? 1 : (int)ks;
+}
+
+size_t prefill_split_bytes(int B, int Hq, int Tq, int dv, int ks) {
+    if (ks < 2) return 0;
+    return sizeof(float) * (size_t)B * Hq * Tq * ks * (size_t)(dv + 2);
+}
 
 hipError_t launch_prefill_bf16(const FwdParams& p, hipStream_t stream) {
     const int dv = p.dv ? p.dv : p.d;

@@ -42,11 +42,28 @@ struct FwdParams {
     const float* rope_tab = nullptr;
     int rope_adj = 0;      // 0: split-half pairs (p, p + d/2); 1: adjacent (2p, 2p + 1)
     int rope_pos0 = 0;
+    // bf16 prefill split over the keys (nsplit > 1): partial outputs
+    // [B*Hq*Tq][nsplit][d] and (max, weight sum) [B*Hq*Tq][nsplit][2] in float32
+    int nsplit = 1;
+    float* part_o = nullptr;
+    float* part_ml = nullptr;
 };
 
 // Prefill (any Tq) bf16 MFMA kernel, d in {64, 128}: four-wave workgroups of
 // 128 query rows, several workgroups per CU.
 hipError_t launch_prefill_bf16(const FwdParams& p, hipStream_t stream);
+
+// Key splits for a bf16 prefill of this size (1: none): used when one
+// workgroup per (128 query rows, head) would leave most of the chip idle.
+int prefill_splits(int B, int Hq, int Tq, int Tk, int d, int dv);
+size_t prefill_split_bytes(int B, int Hq, int Tq, int dv, int ks);
+
+// Merge S <= 8 partial results per row: o = sum_s 2^(m_s - M) o_s / sum_s
+// 2^(m_s - M) l_s (M = max_s m_s) into bf16 o (row r = (b Hq + hq) Tq + i
+// at o + b os.b + hq os.h + i os.t) and, when lse is set, lse[r].
+hipError_t launch_combine_bf16(const float* part_o, const float* part_ml, void* o, float* lse,
+                               long long rows, int S, int Hq, int Tq, const Strides& os, int d,
+                               hipStream_t stream);
 
 // Split-K decode (Tq == 1) bf16 kernels; d in {64, 128}, Hq / Hkv <= 16.
 bool decode_bf16_supported(int Hq, int Hkv, int d);
