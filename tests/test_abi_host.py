@@ -261,3 +261,18 @@ def fwd_dv(q=A, k=Bp, v=C, o=D, B=1, Hq=4, Hkv=2, Tq=16, Tk=16, dk=64, dv=128, c
 ])
 def test_attn_fwd_dv_rejects(kw, status):
     assert fwd_dv(**kw) == status
+
+
+def test_prefill_split_workspace_bytes():
+    """A small bf16 prefill reports the optional workspace of its key splits
+    (4 (d + 2) bytes per query row and split); a launch that already has two
+    workgroups of 128 query rows per CU (512), or float32, reports none."""
+    lib = rocattn.library()
+    # 4 query tiles x 32 heads = 128 workgroups -> 4 splits of 128 key tiles
+    assert lib.attn_workspace_bytes(1, 32, 8, 512, 4096, 128, BF16) == 4 * 130 * 32 * 512 * 4
+    # at most 8 splits, each of at least 4 key tiles (64 keys at d 64)
+    assert lib.attn_workspace_bytes(1, 4, 4, 100, 4096, 64, BF16) == 4 * 66 * 4 * 100 * 8
+    assert lib.attn_workspace_bytes(1, 4, 4, 100, 512, 64, BF16) == 4 * 66 * 4 * 100 * 2
+    assert lib.attn_workspace_bytes(1, 4, 4, 100, 64, 64, BF16) == 0       # one key tile: no split
+    assert lib.attn_workspace_bytes(1, 32, 8, 2048, 2048, 128, BF16) == 0  # 512 workgroups
+    assert lib.attn_workspace_bytes(1, 32, 8, 512, 4096, 128, F32) == 0
