@@ -215,6 +215,22 @@ int rope_apply_ex(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head, i
                   double base, int dtype, void* stream, int pairing);
 
 /*
+ * rope_apply_pos -- rope_apply_ex with a position per token: token t of
+ * sequence b sits at positions[b * T + t] (the pages take the angles from
+ * the cache position onward, "The Transformer architecture" -- Hands-on;
+ * here each sequence of a batch may sit at its own position, or a packed
+ * row at any positions).  The angles and the rotation are rope_apply_ex's,
+ * so positions[b][t] = pos0 + t gives rope_apply_ex's bits.
+ *
+ *   positions  device int32 [B][T], 4-byte aligned, read only; any values
+ *              (the rotation is defined for every integer position).
+ * Other arguments, rounding and support as rope_apply_ex; positions may not
+ * overlap q or k (ERR_SHAPE).
+ */
+int rope_apply_pos(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head,
+                   const int* positions, double base, int dtype, void* stream, int pairing);
+
+/*
  * attn_decode_step -- one cached generation step, Tn new tokens per
  * sequence ("The Transformer architecture" -- Hands-on: the new keys and
  * values are written into the cache along the token axis at cache.pos, RoPE

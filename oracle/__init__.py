@@ -12,6 +12,7 @@ Functions (each cites its passage in ``attn_oracle.c``):
     attn_rows(q, k, v, rows, scale, causal=True, q_offset=0)
     rope(x, pos0=0, base=10000.0, pairing="split")
     rope_table(T, d, pos0=0, base=10000.0) -> float32 [T, d/2, 2] (cos, sin)
+    rope_positions(x, positions, base=10000.0, pairing="split")   (rope per token)
     attn_bwd(q, k, v, dO, scale, causal=True, q_offset=0) -> (dq, dk, dv)
     decode_step(q, k_new, v_new, k_cache, v_cache, pos, scale, base=10000.0,
                 pairing="split")   (a composition of rope and attn)
@@ -165,6 +166,20 @@ class Oracle:
             raise ValueError(f"oracle_rope_table rejected its arguments (status {st})")
         return out
 
+    def rope_positions(self, x, positions, base: float = 10000.0, pairing: str = "split"):
+        """Rotated copy of x[B,H,T,d] with token t of sequence b at position
+        positions[b][t]: oracle_rope applied to each token at its own pos0
+        (a composition of the function above, no arithmetic of its own)."""
+        x = _as_f64(x)
+        B, H, T, d = x.shape
+        pos = np.asarray(positions, dtype=np.int64).reshape(B, T)
+        y = np.empty_like(x)
+        for b in range(B):
+            for t in range(T):
+                y[b:b + 1, :, t:t + 1] = self.rope(np.ascontiguousarray(x[b:b + 1, :, t:t + 1]),
+                                                   int(pos[b, t]), base, pairing)
+        return y
+
     def decode_step(self, q, k_new, v_new, k_cache, v_cache, pos, scale, base=10000.0,
                     pairing="split"):
         """One cached generation step, as "The Transformer architecture" --
@@ -220,6 +235,10 @@ def rope(*args, **kwargs):
 
 def rope_table(*args, **kwargs):
     return default().rope_table(*args, **kwargs)
+
+
+def rope_positions(*args, **kwargs):
+    return default().rope_positions(*args, **kwargs)
 
 
 def attn_bwd(*args, **kwargs):

@@ -505,6 +505,30 @@ def pin_rope_table(orc):
     assert np.max(np.abs(got - want)) > 0.0   # the table is float32, the oracle's angles are not
 
 
+def pin_rope_per_token_positions(orc):
+    """RoPE at a position per token: consecutive positions pos0 + t give the
+    scalar-offset rotation exactly; tokens are rotated independently
+    (permuting tokens with their positions permutes the result); and two
+    rotated vectors' dot product depends only on their position difference
+    ("The Transformer architecture" -- Hands-on; "Transformer" (ai-notes) --
+    RoPE)."""
+    r = _rng(23)
+    x = r.standard_normal((2, 3, 7, 16))
+    pos = np.array([[40 + t for t in range(7)], [3 + t for t in range(7)]])
+    y = orc.rope_positions(x, pos)
+    assert np.array_equal(y[0:1], orc.rope(x[0:1], 40)) and np.array_equal(y[1:2], orc.rope(x[1:2], 3))
+    perm = np.array([3, 0, 6, 1, 5, 2, 4])
+    pos2 = r.integers(0, 5000, size=(2, 7))
+    y2 = orc.rope_positions(x, pos2)
+    y3 = orc.rope_positions(np.ascontiguousarray(x[:, :, perm]), pos2[:, perm])
+    assert np.array_equal(y3, y2[:, :, perm])
+    q = r.standard_normal((1, 1, 1, 32)); k = r.standard_normal((1, 1, 1, 32))
+    qq = orc.rope_positions(np.repeat(q, 2, axis=2), [[5, 1005]])   # the same q at two positions
+    kk = orc.rope_positions(np.repeat(k, 2, axis=2), [[2, 1002]])
+    s0 = float(qq[0, 0, 0] @ kk[0, 0, 0]); s1 = float(qq[0, 0, 1] @ kk[0, 0, 1])
+    assert abs(s0 - s1) < 1e-9
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]
 
 

@@ -276,3 +276,18 @@ def test_prefill_split_workspace_bytes():
     assert lib.attn_workspace_bytes(1, 4, 4, 100, 64, 64, BF16) == 0       # one key tile: no split
     assert lib.attn_workspace_bytes(1, 32, 8, 2048, 2048, 128, BF16) == 0  # 512 workgroups
     assert lib.attn_workspace_bytes(1, 32, 8, 512, 4096, 128, F32) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=None), -1), (dict(q=None), -1), (dict(pairing=2), -2), (dict(dtype=4), -3),
+    (dict(d=7), -4), (dict(base=0.0), -6), (dict(pos=0x70000002), -7), (dict(q=A + 8), -7),
+    (dict(pos=A + 16), -2),                      # positions overlap q
+    (dict(k=A + 64), -2),                        # k overlaps q
+])
+def test_rope_apply_pos_rejects(kw, status):
+    args = dict(q=A, k=Bp, B=2, Hq=4, Hkv=2, T=8, d=64, pos=0x70000000, base=10000.0, dtype=BF16,
+                pairing=0)
+    args.update(kw)
+    assert rocattn.library().rope_apply_pos(args["q"], args["k"], args["B"], args["Hq"], args["Hkv"],
+                                            args["T"], args["d"], args["pos"], args["base"],
+                                            args["dtype"], None, args["pairing"]) == status

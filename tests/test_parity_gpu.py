@@ -966,3 +966,38 @@ def test_prefill_split_matches_oracle(B, Hq, Hkv, Tq, Tk, d, causal, qo):
         err = float(np.max(np.abs(f64(o) - want)))
         assert err <= TOL[torch.bfloat16], err
     assert float(np.max(np.abs(f64(lse1) - want_lse))) <= 2.0e-3
+
+
+# ---- RoPE with a position per token
+
+@pytest.mark.parametrize("dtype,d,pairing", [(torch.bfloat16, 128, "split"), (torch.bfloat16, 64, "adjacent"),
+                                             (torch.float32, 6, "split")])
+def test_rope_apply_pos_matches_oracle(dtype, d, pairing):
+    say("rope per token", dtype, d, pairing)
+    B, Hq, Hkv, T = 3, 8, 2, 37
+    q = _rand((B, Hq, T, d), dtype, 61)
+    k = _rand((B, Hkv, T, d), dtype, 62)
+    pos = torch.from_numpy(np.random.default_rng(63).integers(0, 20000, size=(B, T)).astype(np.int32))
+    qd, kd, pd = gpu(q, k, pos)
+    ra.rope_apply_pos(qd, kd, pd, pairing=pairing)
+    torch.cuda.synchronize()
+    for got, x in ((qd, q), (kd, k)):
+        want = oracle.rope_positions(x, pos.numpy(), pairing=pairing)
+        assert np.all(np.abs(f64(got) - want) <= rope_tol(want, dtype))
+
+
+def test_rope_apply_pos_consecutive_is_rope_apply_bit_exact():
+    """positions[b][t] = pos0_b + t gives rope_apply's bits, sequence by sequence."""
+    say("rope per token vs scalar")
+    B, Hq, Hkv, T, d = 4, 8, 2, 100, 128
+    q = _rand((B, Hq, T, d), torch.bfloat16, 71).cuda()
+    k = _rand((B, Hkv, T, d), torch.bfloat16, 72).cuda()
+    starts = [0, 17, 4093, 123456]
+    pos = torch.tensor([[s + t for t in range(T)] for s in starts], dtype=torch.int32, device=DEV)
+    q1, k1 = q.clone(), k.clone()
+    ra.rope_apply_pos(q1, k1, pos)
+    for b, s in enumerate(starts):
+        qb, kb = q[b:b + 1].clone(), k[b:b + 1].clone()
+        ra.rope_apply(qb, kb, pos0=s)
+        torch.cuda.synchronize()
+        assert torch.equal(q1[b:b + 1], qb) and torch.equal(k1[b:b + 1], kb)

@@ -38,7 +38,7 @@ LIBRARY = os.path.join(HERE, "librocattn.so")
 
 # the C ABI, as declared in include/rocattn.h
 SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_strided", "attn_workspace_bytes",
-           "rope_apply", "rope_apply_ex", "attn_decode_step", "attn_fwd_dv", "attn_fwd_rope",
+           "rope_apply", "rope_apply_ex", "rope_apply_pos", "attn_decode_step", "attn_fwd_dv", "attn_fwd_rope",
            "attn_fwd_rope_workspace_bytes", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_status_string")
 
@@ -86,6 +86,8 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_step.restype = i
         lib.attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
                                          ctypes.c_double, i, i, vp, vp, sz, vp]
+        lib.rope_apply_pos.restype = i
+        lib.rope_apply_pos.argtypes = [vp, vp, i, i, i, i, i, vp, ctypes.c_double, i, vp, i]
         lib.attn_fwd_dv.restype = i
         lib.attn_fwd_dv.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp, vp]
         lib.attn_fwd_rope.restype = i
@@ -307,6 +309,31 @@ def rope_apply(q, k=None, pos0=0, base=10000.0, stream=None, pairing="split"):
     """Rotate q (and k) in place by position pos0 + t; pairing "split"
     (channels p, p + d/2) or "adjacent" (channels 2p, 2p + 1)."""
     _rope_call(q, k, pos0, base, stream, pairing)()
+    return q, k
+
+
+def rope_apply_pos(q, k=None, positions=None, base=10000.0, stream=None, pairing="split"):
+    """RoPE in place with a position per token: positions is an int32 GPU
+    tensor [B, T] (token t of sequence b at positions[b, t])."""
+    import torch
+    if pairing not in PAIRING:
+        raise ValueError(f"pairing must be one of {sorted(PAIRING)}")
+    _check_dev("q", q)
+    if k is not None:
+        _check_dev("k", k, q.dtype)
+        if k.dim() != 4 or k.shape[0] != q.shape[0] or tuple(k.shape[2:]) != tuple(q.shape[2:]):
+            raise ValueError("k must be [B, Hkv, T, d] with q's B, T and d")
+    if positions is None:
+        raise ValueError("positions (int32 [B, T]) is required")
+    _check_dev("positions", positions, torch.int32)
+    B, Hq, T, d = q.shape
+    if tuple(positions.shape) != (B, T):
+        raise ValueError("positions must be [B, T]")
+    st = library().rope_apply_pos(_ptr(q), _ptr(k), B, Hq, k.shape[1] if k is not None else 0, T, d,
+                                  _ptr(positions), float(base), _dtype_code(q), _stream(q, stream),
+                                  PAIRING[pairing])
+    if st != OK:
+        raise RocattnError("rope_apply_pos", st)
     return q, k
 
 

@@ -336,6 +336,36 @@ ROCATTN_API int rope_apply_ex(void* q, void* k, int B, int Hq, int Hkv, int T, i
     return ROCATTN_OK;
 }
 
+ROCATTN_API int rope_apply_pos(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head,
+                               const int* positions, double base, int dtype, void* stream,
+                               int pairing) {
+    if (pairing != ROCATTN_ROPE_SPLIT_HALF && pairing != ROCATTN_ROPE_ADJACENT)
+        return ROCATTN_ERR_SHAPE;
+    if (dtype != ROCATTN_F32 && dtype != ROCATTN_BF16) return ROCATTN_ERR_DTYPE;
+    if (!q || !positions) return ROCATTN_ERR_NULL;
+    if (B <= 0 || Hq <= 0 || T <= 0 || d_head <= 0) return ROCATTN_ERR_SHAPE;
+    if (k && Hkv <= 0) return ROCATTN_ERR_SHAPE;
+    if (d_head % 2 != 0 || d_head > 256) return ROCATTN_ERR_HEADDIM;
+    if (!isfinite(base) || !(base > 0.0)) return ROCATTN_ERR_SCALE;
+    if (!aligned16(q) || (k && !aligned16(k))) return ROCATTN_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(positions) & 3u) return ROCATTN_ERR_ALIGN;
+    const long long nq = count4(B, Hq, T, d_head);
+    const long long nk = k ? count4(B, Hkv, T, d_head) : 0;
+    if (nq < 0 || nk < 0) return ROCATTN_ERR_SHAPE;
+    if ((long long)B * T * (d_head / 2) > (long long)INT_MAX * 256) return ROCATTN_ERR_SHAPE;   // 1-D grid
+    const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
+    const size_t pb = (size_t)B * T * sizeof(int);
+    if (k && overlaps(q, (size_t)nq * elt, k, (size_t)nk * elt)) return ROCATTN_ERR_SHAPE;
+    if (overlaps(positions, pb, q, (size_t)nq * elt) || (k && overlaps(positions, pb, k, (size_t)nk * elt)))
+        return ROCATTN_ERR_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (rocattn::launch_rope_pos(q, B, Hq, T, d_head, positions, base, dtype, pairing, s) != hipSuccess)
+        return ROCATTN_ERR_HIP;
+    if (k && rocattn::launch_rope_pos(k, B, Hkv, T, d_head, positions, base, dtype, pairing, s) != hipSuccess)
+        return ROCATTN_ERR_HIP;
+    return ROCATTN_OK;
+}
+
 ROCATTN_API int rope_apply(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head, int pos0,
                            double base, int dtype, void* stream) {
     return rope_apply_ex(q, k, B, Hq, Hkv, T, d_head, pos0, base, dtype, stream,

@@ -82,6 +82,11 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_rope(void* x, long long n_seq, int T, int d, int pos0, double base,
                        int dtype, int pairing, hipStream_t stream, float* tab = nullptr);
 
+// RoPE with per-token positions: x [B][H][T][d], token t of sequence b at
+// position pos[b * T + t] (device int32 [B][T]).
+hipError_t launch_rope_pos(void* x, int B, int H, int T, int d, const int* pos, double base,
+                           int dtype, int pairing, hipStream_t stream);
+
 // Everything a backward launch needs (dense [B][H][T][d] tensors), validated
 // by the host API.
 struct BwdParams {

@@ -145,6 +145,81 @@ hipError_t launch_rope(void* x, long long n_seq, int T_len, int d, int pos0, dou
 
 
 // ---------------------------------------------------------------------------
+// Per-token positions: token t of sequence b sits at pos[b * T + t] (the
+// scalar pos0 + t of rope_kernel generalised, e.g. sequences of a batch at
+// different cache positions).  A lane owns kPairs pairs of one (b, t), forms
+// their angles once (the same arithmetic as rope_kernel) and turns that
+// token in every head of sequence b.
+namespace {
+
+template <typename T, int kPairs, bool ADJ>
+__global__ __launch_bounds__(kThreads) void rope_pos_kernel(T* __restrict__ x, int B, int H, int T_len,
+                                                            int d, const int* __restrict__ pos,
+                                                            double neg_log2_base_over_half) {
+    const int half = d >> 1;
+    const int groups = half / kPairs;
+    const long long slot = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (slot >= (long long)B * T_len * groups) return;
+    const long long bt = slot / groups;
+    const int p0 = (int)(slot - bt * groups) * kPairs;
+    const int b = (int)(bt / T_len), t = (int)(bt - (long long)b * T_len);
+    float cs[kPairs], sn[kPairs];
+    const double at = (double)pos[bt];
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) {
+        const double inv_freq = exp2((double)(p0 + u) * neg_log2_base_over_half);
+        double sv, cv;
+        rope_sincos(at * inv_freq, sv, cv);
+        cs[u] = (float)cv;
+        sn[u] = (float)sv;
+    }
+    T* base = x + ((size_t)b * H * T_len + t) * d + (ADJ ? 2 * p0 : p0);
+#pragma unroll 4
+    for (int hh = 0; hh < H; ++hh) {
+        T* lo = base + (size_t)hh * T_len * d;
+        T* hi = lo + (ADJ ? kPairs : half);
+        float e[2 * kPairs], y[2 * kPairs];
+        load_f32<T, kPairs>(lo, e);
+        load_f32<T, kPairs>(hi, e + kPairs);
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u) {
+            const int i1 = ADJ ? 2 * u : u, i2 = ADJ ? 2 * u + 1 : u + kPairs;
+            rope_turn(e[i1], e[i2], cs[u], sn[u], y[i1], y[i2]);
+        }
+        store_f32<T, kPairs>(lo, y);
+        store_f32<T, kPairs>(hi, y + kPairs);
+    }
+}
+
+template <typename T, int kPairs>
+hipError_t launch_rope_pos_t(T* x, int B, int H, int T_len, int d, const int* pos, double base,
+                             int pairing, hipStream_t stream) {
+    const int groups = (d / 2) / kPairs;
+    const long long slots = (long long)B * T_len * groups;
+    const dim3 grid((unsigned)((slots + kThreads - 1) / kThreads));
+    const double neg = -log2(base) / (double)(d / 2);
+    if (pairing)
+        hipLaunchKernelGGL((rope_pos_kernel<T, kPairs, true>), grid, dim3(kThreads), 0, stream, x, B, H, T_len,
+                           d, pos, neg);
+    else
+        hipLaunchKernelGGL((rope_pos_kernel<T, kPairs, false>), grid, dim3(kThreads), 0, stream, x, B, H, T_len,
+                           d, pos, neg);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rope_pos(void* x, int B, int H, int T_len, int d, const int* pos, double base,
+                           int dtype, int pairing, hipStream_t stream) {
+    const bool wide = (d / 2) % 4 == 0;
+    if (dtype == 0)
+        return wide ? launch_rope_pos_t<float, 4>(static_cast<float*>(x), B, H, T_len, d, pos, base, pairing, stream)
+                    : launch_rope_pos_t<float, 1>(static_cast<float*>(x), B, H, T_len, d, pos, base, pairing, stream);
+    return wide ? launch_rope_pos_t<bf16, 4>(static_cast<bf16*>(x), B, H, T_len, d, pos, base, pairing, stream)
+                : launch_rope_pos_t<bf16, 1>(static_cast<bf16*>(x), B, H, T_len, d, pos, base, pairing, stream);
+}
+
+// ---------------------------------------------------------------------------
 // Decode-step preparation ("The Transformer architecture" -- Hands-on: the new
 // keys and values are written into the cache at cache.pos along the token
 // axis, and RoPE is sliced from cache.pos): in one launch, rotate the Tn new
