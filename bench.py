@@ -378,7 +378,7 @@ BACKWARD_WORKLOADS = (2, 3)
 
 
 def measure_backward(torch, ra, wl, dev):
-    """attn_bwd (the three gradient kernels: row statistics, dQ, dK/dV) on
+    """attn_bwd (the two gradient kernels: dQ with the rows' statistics, dK/dV) on
     the workloads' shapes, with the upstream gradient a seeded N(0, 1) draw
     and o, lse from the forward on the same inputs.  FLOPs: the five matrix
     products of the gradients (S recomputed, dP, dV, dK, dQ) over the visible

@@ -14,12 +14,12 @@
 // query heads of its group ("The Transformer architecture" -- GQA), in a
 // fixed order, so results are deterministic.  D_i equals sum_j P_ij dP_ij.
 //
-// Three kernels, each a plain adaptation of the forward's tile scheme:
-//  * bwd_rowdot_kernel: per 32-row tile of a head, the rows' lse (as a
-//    base-2 exponent) and D = rowsum(dO * O) into the workspace, 64 floats
-//    per tile (32 lse, then 32 D; rows past Tq get 0), so a tile's row
-//    statistics are one contiguous 256-byte block.
-//  * bwd_dq_kernel: one workgroup = 4 waves x 32 query rows; it walks the
+// Two kernels, each a plain adaptation of the forward's tile scheme:
+//  * bwd_dq_kernel: one workgroup = 4 waves x 32 query rows.  First each
+//    row's statistics: lse as a base-2 exponent and D = rowsum(dO * O),
+//    which the wave also writes to the workspace, 64 floats per 32-row tile
+//    (32 lse, then 32 D; rows past Tq get 0), so the dK/dV kernel finds a
+//    tile's row statistics in one contiguous 256-byte block.  It then walks the
 //    32-key tiles of its rows like the forward (S^T = K Q^T with keys on the
 //    MFMA rows, one query per lane), forms dP^T = V dO^T the same way, then
 //    dQ^T += K^T dS^T with K^T read by the LDS transpose read.  Per tile the
@@ -77,33 +77,6 @@ struct BCfg {
 __device__ inline int row_of(int e) { return 8 * (e >> 2) + (e & 3); }
 
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdArgs a) {
-    constexpr int LPR = D / 8;    // lanes per row, 8 elements each
-    const int rows_pad = a.n_rt * 32;
-    const long long rows = (long long)a.B * a.Hq * rows_pad;
-    const long long r = ((long long)blockIdx.x * 256 + threadIdx.x) / LPR;
-    const int part = threadIdx.x % LPR;
-    const long long bh = r / rows_pad;
-    const int i = (int)(r - bh * rows_pad);
-    const bool ok = r < rows && i < a.Tq;
-    float s = 0.f;
-    if (ok) {
-        const long long row = bh * a.Tq + i;
-        const bf16x8 g = *reinterpret_cast<const bf16x8*>(a.dO + row * D + 8 * part);
-        const bf16x8 o = *reinterpret_cast<const bf16x8*>(a.o + row * D + 8 * part);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf((float)g[e], (float)o[e], s);
-    }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (r < rows && part == 0) {
-        float* t = a.stats + (bh * a.n_rt + (i >> 5)) * 64;
-        t[i & 31] = ok ? a.lse[bh * a.Tq + i] * kLog2e : 0.f;
-        t[32 + (i & 31)] = s;
-    }
-}
-
 // Per-lane tile addressing shared by the two gradient kernels.
 template <int D>
 struct TileLanes {
@@ -199,9 +172,26 @@ void bwd_dq_kernel(BwdArgs a) {
     bf16x8 qf[NQ], gf[NQ];
     load_row_frags<D>(a.q + (long long)bh * a.Tq * D, iq, row_ok, h, qf);
     load_row_frags<D>(a.dO + (long long)bh * a.Tq * D, iq, row_ok, h, gf);
-    const float* tstats = a.stats + ((long long)bh * a.n_rt + (i0w >> 5)) * 64;
-    const float Lr = row_ok ? tstats[li] : 0.f;
-    const float Dv = row_ok ? tstats[32 + li] : 0.f;
+    // the row's statistics: lse as a base-2 exponent, and D = rowsum(dO * O)
+    // from the lane's half of the channels plus the other half-wave's; the
+    // wave's 32-row block of them goes to the workspace for the dK/dV kernel
+    float Dv;
+    {
+        bf16x8 of[NQ];
+        load_row_frags<D>(a.o + (long long)bh * a.Tq * D, iq, row_ok, h, of);
+        float part = 0.f;
+#pragma unroll
+        for (int m = 0; m < NQ; ++m)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) part = fmaf((float)gf[m][j], (float)of[m][j], part);
+        Dv = pair_sum(part);
+    }
+    const float Lr = row_ok ? a.lse[rowid] * kLog2e : 0.f;
+    if ((i0w >> 5) < a.n_rt && h == 0) {
+        float* tstats = a.stats + ((long long)bh * a.n_rt + (i0w >> 5)) * 64;
+        tstats[li] = Lr;
+        tstats[32 + li] = Dv;
+    }
 
     const int kv_end = a.causal ? min(a.Tk, a.q_offset + qt * C::BM + C::BM) : a.Tk;
     const int n = (kv_end + BN - 1) / BN;
@@ -456,12 +446,7 @@ void bwd_dkv_kernel(BwdArgs a) {
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     typedef BCfg<D> C;
-    const long long rows = (long long)a.B * a.Hq * a.n_rt * 32;
-    const long long nthreads = rows * (D / 8);
-    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
-                       stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
     const long long n_qt = (a.Tq + C::BM - 1) / C::BM;
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(n_qt * a.B * a.Hq)), dim3(256), 0, stream, a);
     e = hipGetLastError();
