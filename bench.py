@@ -447,7 +447,7 @@ def cpu_baseline(w, seconds):
             t_total += time.perf_counter() - t0
             flops_done += full_flops
             passes += 1
-            if t_total >= seconds or passes >= 50:
+            if t_total >= seconds or passes >= 1000:
                 break
         sample = f"{passes} full pass(es) over the workload ({w.B * w.Hq * w.Tq} query rows)"
     else:
