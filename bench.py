@@ -247,9 +247,32 @@ def setup(w, torch, ra, wl, dev):
                 sep_b=sep_b, decode=decode, q=qd, k=kd, v=vd, o=od)
 
 
-def measure(w, args, torch, ra, wl, dev, steps=None, warmup=None):
+def single_launch_ms(torch, dev, fn, cold, n=21, scratch_bytes=512 << 20):
+    """Median time of single synchronised launches of fn; with cold=True
+    each follows a 512 MiB device write that evicts the inputs from L2 and
+    the 256 MB MALL."""
+    scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    fn()
+    for i in range(n):
+        if cold:
+            scratch.fill_(i & 0xFF)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    times.sort()
+    return times[len(times) // 2]
+
+
+def measure(w, args, torch, ra, wl, dev, steps=None, warmup=None, cold=False):
     """Times of one workload's step, attention and RoPE launches.  Without
-    explicit counts: about 30 ms of warm-up and 50 ms of timed steps."""
+    explicit counts: about 30 ms of warm-up and 50 ms of timed steps.  With
+    cold=True also the attention launch after a cache-evicting write."""
     s = setup(w, torch, ra, wl, dev)
     timer = Timer(torch)
     if steps is None or warmup is None:
@@ -260,6 +283,9 @@ def measure(w, args, torch, ra, wl, dev, steps=None, warmup=None):
     ms_attn = timer(s["attn_b"], steps, warmup)
     out = dict(workload=w.name, ms_per_step=ms_step, attn_ms=ms_attn,
                timing="back-to-back launches, arguments marshalled once")
+    if cold:
+        out["attn_ms_single_launch_warm"] = single_launch_ms(torch, dev, s["attn_b"], False)
+        out["attn_ms_single_launch_cold_mall"] = single_launch_ms(torch, dev, s["attn_b"], True)
     if s["sep_b"] is not None:
         out["ms_per_step_rope_then_attn"] = timer(s["sep_b"], steps, warmup)
     if not args.no_graph:  # the same steps as HIP graph replays, for comparison
@@ -509,7 +535,7 @@ def main():
         return
 
     w = wl.WORKLOADS[args.workload]
-    head = measure(w, args, torch, ra, wl, dev, args.steps, args.warmup)
+    head = measure(w, args, torch, ra, wl, dev, args.steps, args.warmup, cold=True)
     print(f"# {w.name}: step {head['ms_per_step'] * 1e3:.2f} us, attention "
           f"{head['attn_ms'] * 1e3:.2f} us = {head['attn_tflops']:.1f} TFLOP/s", file=sys.stderr)
 
@@ -559,6 +585,8 @@ def main():
         "roofline": roof,
         "timing": head["timing"],
         "ms_per_step_graph": head.get("ms_per_step_graph"),
+        "attn_ms_single_launch_warm": head.get("attn_ms_single_launch_warm"),
+        "attn_ms_single_launch_cold_mall": head.get("attn_ms_single_launch_cold_mall"),
         "ms_per_step_rope_then_attn": head.get("ms_per_step_rope_then_attn"),
         "graph_replay_matches_eager": head.get("graph_replay_matches_eager"),
     }
