@@ -400,9 +400,10 @@ def test_lse_matches_oracle(dtype, Tq, Tk, qo):
     want_o, want_lse = oracle.attn(q, k, v, 0.0884, q_offset=qo, return_lse=True)
     assert float(np.max(np.abs(f64(o) - want_o))) <= TOL[dtype]
     # bf16: the row sum adds the bf16-rounded weights that also feed the P.V
-    # product (V = 1 gives O = 1), each within a relative 2^-9 of the exact
-    # weight, so ln(sum) moves by at most -ln(1 - 2^-9) = 1.955e-3.
-    lse_tol = 1e-4 if dtype == torch.float32 else 2.0e-3
+    # product (V = 1 gives O = 1), each within a relative 2^-8 (bf16 keeps 8
+    # significant bits) of the exact weight, so ln(sum) moves by at most
+    # ln(1 + 2^-8) = 3.9e-3, reached when one weight dominates the row.
+    lse_tol = 1e-4 if dtype == torch.float32 else 4.0e-3
     assert float(np.max(np.abs(lse.double().numpy() - want_lse))) <= lse_tol
 
 
@@ -664,7 +665,7 @@ def test_decode_steps_replay_the_prefill():
 #      oracle's fp64 gradients on the same bf16 inputs and the GPU forward's
 #      own o and lse (the oracle recomputes its forward in fp64)
 #
-# Tolerance: the kernels round P and dS to bf16 (relative 2^-9) before the
+# Tolerance: the kernels round P and dS to bf16 (relative 2^-8) before the
 # matrix products and the results to bf16, so the error of a gradient entry
 # scales with the size of its terms; the bound is the forward's 1.5e-2 taken
 # relative to the tensor's largest entry (at least 1).
@@ -862,7 +863,7 @@ def test_attn_fwd_dv_matches_oracle(dtype, B, Hq, Hkv, Tq, Tk, dk, dv, causal, q
     want, want_lse = oracle.attn(q, k, v, scale, causal=causal, q_offset=qo, return_lse=True)
     err = float(np.max(np.abs(f64(o) - want)))
     assert err <= TOL[dtype], err
-    lse_tol = 1e-4 if dtype == torch.float32 else 2.0e-3
+    lse_tol = 1e-4 if dtype == torch.float32 else 4.0e-3
     assert float(np.max(np.abs(f64(lse) - want_lse))) <= lse_tol
 
 
@@ -965,7 +966,7 @@ def test_prefill_split_matches_oracle(B, Hq, Hkv, Tq, Tk, d, causal, qo):
     for o in (o1, o2):
         err = float(np.max(np.abs(f64(o) - want)))
         assert err <= TOL[torch.bfloat16], err
-    assert float(np.max(np.abs(f64(lse1) - want_lse))) <= 2.0e-3
+    assert float(np.max(np.abs(f64(lse1) - want_lse))) <= 4.0e-3
 
 
 # ---- RoPE with a position per token
