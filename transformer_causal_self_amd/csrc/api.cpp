@@ -328,10 +328,9 @@ ROCATTN_API int rope_apply_ex(void* q, void* k, int B, int Hq, int Hkv, int T, i
     const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
     if (k && overlaps(q, (size_t)nq * elt, k, (size_t)nk * elt)) return ROCATTN_ERR_SHAPE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (rocattn::launch_rope(q, (long long)B * Hq, T, d_head, pos0, base, dtype, pairing, s) != hipSuccess)
-        return ROCATTN_ERR_HIP;
-    if (k && rocattn::launch_rope(k, (long long)B * Hkv, T, d_head, pos0, base, dtype, pairing, s) !=
-                 hipSuccess)
+    // one launch turns q and k: they share every (position, pair) angle
+    if (rocattn::launch_rope(q, (long long)B * Hq, T, d_head, pos0, base, dtype, pairing, s, nullptr, k,
+                             k ? (long long)B * Hkv : 0) != hipSuccess)
         return ROCATTN_ERR_HIP;
     return ROCATTN_OK;
 }

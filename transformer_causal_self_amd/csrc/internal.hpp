@@ -79,8 +79,11 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 // with token t at position pos0 + t.
 // tab (optional): also store the float32 (cos, sin) of every pair at
 // positions pos0 .. pos0 + T - 1 into tab[position][d/2].
+// x2 (optional): a second tensor of n_seq2 sequences with the same T, d and
+// positions, turned by the same launch (q and k of one call).
 hipError_t launch_rope(void* x, long long n_seq, int T, int d, int pos0, double base,
-                       int dtype, int pairing, hipStream_t stream, float* tab = nullptr);
+                       int dtype, int pairing, hipStream_t stream, float* tab = nullptr,
+                       void* x2 = nullptr, long long n_seq2 = 0);
 
 // RoPE with per-token positions: x [B][H][T][d], token t of sequence b at
 // position pos[b * T + t] (device int32 [B][T]).

@@ -48,10 +48,13 @@ __device__ inline void store_f32(T* dst, const float* f) {
     *reinterpret_cast<Pack<T, NP>*>(dst) = v;
 }
 
-// grid.x: (token, pair-group) slots; grid.y: chunks of the n_seq head rows.
+// grid.x: (token, pair-group) slots; grid.y: chunks of the head rows, the
+// n_seq rows of x followed by the n_seq2 rows of x2 (q and k of one call
+// share the angles of a slot, so one launch turns both).
 // ADJ: adjacent pairing (the lane's 2 kPairs channels are contiguous).
 template <typename T, int kPairs, bool ADJ>  // kPairs channel pairs per lane
 __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long long n_seq,
+                                                        T* __restrict__ x2, long long n_seq2,
                                                         int rows_per_chunk, int T_len, int d,
                                                         int pos0, double neg_log2_base_over_half,
                                                         float2* __restrict__ tab) {
@@ -80,14 +83,14 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long 
     }
 
     const long long r0 = (long long)blockIdx.y * rows_per_chunk;
-    const long long r1 = min(n_seq, r0 + rows_per_chunk);
+    const long long r1 = min(n_seq + n_seq2, r0 + rows_per_chunk);
     const size_t row_stride = (size_t)T_len * d;
-    T* base = x + (size_t)t * d + (ADJ ? 2 * p0 : p0);
+    const size_t off = (size_t)t * d + (ADJ ? 2 * p0 : p0);
 #pragma unroll 4
     for (long long r = r0; r < r1; ++r) {
         // split-half: the kPairs first halves, then the kPairs second halves;
         // adjacent: 2 kPairs contiguous channels, pair u = (2u, 2u + 1)
-        T* lo = base + (size_t)r * row_stride;
+        T* lo = (r < n_seq ? x + (size_t)r * row_stride : x2 + (size_t)(r - n_seq) * row_stride) + off;
         T* hi = lo + (ADJ ? kPairs : half);
         float e[2 * kPairs], y[2 * kPairs];
         load_f32<T, kPairs>(lo, e);
@@ -103,8 +106,9 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, long 
 }
 
 template <typename T, int kPairs>
-hipError_t launch_rope_t(T* x, long long n_seq, int T_len, int d, int pos0, double base,
-                         int pairing, hipStream_t stream, float* tab) {
+hipError_t launch_rope_t(T* x, long long n_seq, T* x2, long long n_seq2, int T_len, int d, int pos0,
+                         double base, int pairing, hipStream_t stream, float* tab) {
+    const long long n_rows = n_seq + n_seq2;
     const int half = d / 2;
     const int groups = half / kPairs;
     const long long slots = (long long)T_len * groups;
@@ -114,33 +118,42 @@ hipError_t launch_rope_t(T* x, long long n_seq, int T_len, int d, int pos0, doub
     // capped at 2^17 / slots (at most 2^17 lanes' worth of angles)
     long long gy = (2048 + gx - 1) / gx;
     if (gy > (1LL << 17) / slots) gy = (1LL << 17) / slots;
-    if (gy > n_seq) gy = n_seq;
+    if (gy > n_rows) gy = n_rows;
     if (gy < 1) gy = 1;
-    const int rows_per_chunk = (int)((n_seq + gy - 1) / gy);
-    gy = (n_seq + rows_per_chunk - 1) / rows_per_chunk;
+    const int rows_per_chunk = (int)((n_rows + gy - 1) / gy);
+    gy = (n_rows + rows_per_chunk - 1) / rows_per_chunk;
     const double neg = -log2(base) / (double)half;
     dim3 grid((unsigned)gx, (unsigned)gy);
     if (pairing)
         hipLaunchKernelGGL((rope_kernel<T, kPairs, true>), grid, dim3(kThreads), 0, stream,
-                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg, reinterpret_cast<float2*>(tab));
+                           x, n_seq, x2, n_seq2, rows_per_chunk, T_len, d, pos0, neg,
+                           reinterpret_cast<float2*>(tab));
     else
         hipLaunchKernelGGL((rope_kernel<T, kPairs, false>), grid, dim3(kThreads), 0, stream,
-                           x, n_seq, rows_per_chunk, T_len, d, pos0, neg, reinterpret_cast<float2*>(tab));
+                           x, n_seq, x2, n_seq2, rows_per_chunk, T_len, d, pos0, neg,
+                           reinterpret_cast<float2*>(tab));
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_rope(void* x, long long n_seq, int T_len, int d, int pos0, double base,
-                       int dtype, int pairing, hipStream_t stream, float* tab) {
+                       int dtype, int pairing, hipStream_t stream, float* tab, void* x2,
+                       long long n_seq2) {
     // four pairs per lane (8-byte bf16 / 16-byte f32 accesses) when the half
     // head size allows it, else one pair per lane
     const bool wide = (d / 2) % 4 == 0;
-    if (dtype == 0)
-        return wide ? launch_rope_t<float, 4>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, pairing, stream, tab)
-                    : launch_rope_t<float, 1>(static_cast<float*>(x), n_seq, T_len, d, pos0, base, pairing, stream, tab);
-    return wide ? launch_rope_t<bf16, 4>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, pairing, stream, tab)
-                : launch_rope_t<bf16, 1>(static_cast<bf16*>(x), n_seq, T_len, d, pos0, base, pairing, stream, tab);
+    if (!x2) n_seq2 = 0;
+    if (dtype == 0) {
+        float* a = static_cast<float*>(x);
+        float* b = static_cast<float*>(x2);
+        return wide ? launch_rope_t<float, 4>(a, n_seq, b, n_seq2, T_len, d, pos0, base, pairing, stream, tab)
+                    : launch_rope_t<float, 1>(a, n_seq, b, n_seq2, T_len, d, pos0, base, pairing, stream, tab);
+    }
+    bf16* a = static_cast<bf16*>(x);
+    bf16* b = static_cast<bf16*>(x2);
+    return wide ? launch_rope_t<bf16, 4>(a, n_seq, b, n_seq2, T_len, d, pos0, base, pairing, stream, tab)
+                : launch_rope_t<bf16, 1>(a, n_seq, b, n_seq2, T_len, d, pos0, base, pairing, stream, tab);
 }
 
 
