@@ -120,3 +120,44 @@ def test_graph_attn_bwd(d):
         lambda: ra.attn_bwd(q, k, v, o, dO, lse, scale=d ** -0.5, causal=True, dq=dq, dk=dk, dv=dv,
                             workspace=ws),
         [dq, dk, dv])
+
+
+def test_two_streams_concurrently():
+    """Calls on two streams at once, each with its own workspace (the split
+    decode on one, the small-prefill split on the other), give the bits of
+    the same calls made one after another: the library keeps no state shared
+    between calls beyond read-only plans."""
+    say("two streams")
+    qa, ka, va = dev(*wl.random_qkv(2, 8, 2, 1, 3000, 128, torch.bfloat16, seed=95))
+    qb, kb, vb = dev(*wl.random_qkv(1, 8, 2, 300, 2000, 64, torch.bfloat16, seed=96))
+    na = ra.attn_workspace_bytes(2, 8, 2, 1, 3000, 128, torch.bfloat16)
+    nb = ra.attn_workspace_bytes(1, 8, 2, 300, 2000, 64, torch.bfloat16)
+    wsa = torch.empty(na, dtype=torch.uint8, device=DEV)
+    wsb = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    oa, ob = torch.empty_like(qa), torch.empty_like(qb)
+    lb = torch.empty(1, 8, 300, dtype=torch.float32, device=DEV)
+
+    def run_a():
+        ra.attn_fwd_ws(qa, ka, va, oa, wsa, None, scale=128 ** -0.5, causal=True, q_offset=2999)
+
+    def run_b():
+        ra.attn_fwd_ws(qb, kb, vb, ob, wsb, lb, scale=0.125, causal=True, q_offset=1700)
+
+    run_a()
+    run_b()
+    torch.cuda.synchronize()
+    want = [oa.clone(), ob.clone(), lb.clone()]
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    for r in range(5):
+        for x in (oa, ob, lb):
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sa):
+            for _ in range(3):
+                run_a()
+        with torch.cuda.stream(sb):
+            for _ in range(3):
+                run_b()
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip((oa, ob, lb), want)):
+            assert torch.equal(x, y), f"round {r}: output {i} differs"
