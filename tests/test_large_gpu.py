@@ -1,0 +1,130 @@
+"""GPU parity at the largest sizes: a cache of 2^21 tokens for each of two
+sequences, so K and V hold 2^32 elements each and the second sequence
+starts 4 GiB into them (64-bit offsets in every kernel's addressing).
+
+The inputs are built so that the exact result has a closed form the test
+computes in float64 without materialising the tensors on the host: every
+key is zero except a few spikes, so each visible key gets weight e^0 = 1
+and a spike key e^s; values are quarters of small integers periodic in the
+token and channel, plus 1/16 of the (batch, K/V head) index (all exact in
+bf16, |o| < 2 so that the output's own bf16 rounding stays under 4e-3).  For a row that sees
+keys 0 .. L-1 the softmax of the pages ("Attention is All You Need" —
+scaled dot-product attention) then gives
+    o[c] = (sum_j v[j][c] + sum_spikes (e^s - 1) v[j*][c]) / (L + sum_spikes (e^s - 1)).
+e^s (1.4e6) is comparable to L (2^21), so each spike carries a fifth to a
+third of a row's weight: a spike missed, or a value slice read from another
+(batch, head), moves the result by 0.06 or more, against the 1.5e-2 bound.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_causal_self_amd as ra
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+B, HQ, HKV, TK, D = 2, 16, 8, 1 << 21, 128
+SPIKE = 20.0         # the spike key's channel 0; q is 8 e_0
+QVAL = 8.0
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def spikes():
+    return [3, TK // 2 + 1, TK - 5]
+
+
+def value_offset(b, hk):
+    return 7 * hk + 3 * b
+
+
+@pytest.fixture(scope="module")
+def cache():
+    if torch.cuda.get_device_properties(0).total_memory < 40 << 30:
+        pytest.skip("needs 16 GiB of device memory for the cache")
+    k = torch.zeros(B, HKV, TK, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty(B, HKV, TK, D, dtype=torch.bfloat16, device=DEV)
+    j = torch.arange(TK, device=DEV, dtype=torch.int64).view(TK, 1)
+    c = torch.arange(D, device=DEV, dtype=torch.int64).view(1, D)
+    for b in range(B):
+        for hk in range(HKV):
+            v[b, hk] = (0.25 * (((j + c + value_offset(b, hk)) % 7) - 3).float()
+                        + 0.0625 * (b * HKV + hk)).to(torch.bfloat16)
+            for js in spikes():
+                k[b, hk, js, 0] = SPIKE
+    torch.cuda.synchronize()
+    yield k, v
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def expected(b, hk, L, scale):
+    """o[c] over keys 0 .. L-1 of (b, hk), in float64."""
+    off = value_offset(b, hk)
+    cnt = np.array([(L - r + 6) // 7 if r < L else 0 for r in range(7)], dtype=np.float64)
+    cc = np.arange(D)
+    mean = 0.0625 * (b * HKV + hk)
+    num = np.full(D, L * mean)
+    for r in range(7):
+        num += cnt[r] * 0.25 * (((r + cc + off) % 7) - 3)
+    den = float(L)
+    w = math.exp(QVAL * SPIKE * scale)
+    for js in spikes():
+        if js < L:
+            num += (w - 1.0) * (0.25 * (((js + cc + off) % 7) - 3) + mean)
+            den += w - 1.0
+    return num / den
+
+
+def test_decode_over_two_million_tokens(cache):
+    k, v = cache
+    scale = D ** -0.5
+    say("decode large", B, HQ, HKV, TK, D)
+    q = torch.zeros(B, HQ, 1, D, dtype=torch.bfloat16, device=DEV)
+    q[..., 0] = QVAL
+    nb = ra.attn_workspace_bytes(B, HQ, HKV, 1, TK, D, torch.bfloat16)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, HQ, 1, dtype=torch.float32, device=DEV)
+    ra.attn_fwd_ws(q, k, v, o, ws, lse, scale=scale, causal=True, q_offset=TK - 1)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    err = 0.0
+    for b in range(B):
+        for h in range(HQ):
+            want = expected(b, h // (HQ // HKV), TK, scale)
+            err = max(err, float(np.max(np.abs(got[b, h, 0] - want))))
+    say("max abs err", err)
+    assert err <= 1.5e-2
+
+
+def test_prefill_chunk_at_the_end_of_the_cache(cache):
+    """64 new rows at positions Tk-64 .. Tk-1 (the last spike is visible to
+    the last rows only), through the small-prefill split and without it."""
+    k, v = cache
+    scale = D ** -0.5
+    Tq = 64
+    qo = TK - Tq
+    say("prefill chunk large", B, HQ, HKV, Tq, TK, D, qo)
+    q = torch.zeros(B, HQ, Tq, D, dtype=torch.bfloat16, device=DEV)
+    q[..., 0] = QVAL
+    nb = ra.attn_workspace_bytes(B, HQ, HKV, Tq, TK, D, torch.bfloat16)
+    for use_ws in (True, False):
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=DEV) if (use_ws and nb) else None
+        o = torch.empty_like(q)
+        ra.attn_fwd_ws(q, k, v, o, ws, None, scale=scale, causal=True, q_offset=qo)
+        torch.cuda.synchronize()
+        got = o.float().cpu().numpy()
+        err = 0.0
+        for b in range(B):
+            for h in range(HQ):
+                for i in (0, 1, Tq - 6, Tq - 5, Tq - 1):
+                    want = expected(b, h // (HQ // HKV), qo + i + 1, scale)
+                    err = max(err, float(np.max(np.abs(got[b, h, i] - want))))
+        say("workspace", use_ws, "max abs err", err)
+        assert err <= 1.5e-2
