@@ -184,7 +184,8 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
  *
  *   q         [B][Hq][T][d_head], rotated in place.
  *   k         [B][Hkv][T][d_head] rotated in place, or NULL (q only; Hkv is
- *             then ignored).
+ *             then ignored).  k may not overlap q (ERR_SHAPE); one launch
+ *             turns both, sharing each (position, pair) angle.
  *   pos0      position of token 0 (>= 0).
  *   base      frequency base (10000 in the original schedule), finite, > 0.
  *   dtype     rocattn_dtype of q and k.
