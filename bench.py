@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the causal attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
                     [--no-also] [--no-cpu] [--cpu-seconds S] [--no-graph]
+                    [--calib-copy | --calib-mfma | --calib-hbm]
 
 A step is one pass of the hot path over one batch of the workload's seeded
 synthetic inputs, resident in HBM before timing starts:
@@ -13,36 +14,48 @@ synthetic inputs, resident in HBM before timing starts:
     decode (workload 5): RoPE on the new query row, then the split-K decode.
 For the RoPE prefills the same step as two calls (rope_apply on q and k,
 then attention) is timed beside it ("ms_per_step_rope_then_attn").
-The headline workload (default 2: bf16 B8 H12 T1024 d64, causal MHA) is timed
-for K steps between HIP events on the stream the kernels run on, after W
-warm-up steps; the JSON line reports causal-adjusted TFLOP/s.  The K steps
-are launched back to back through the C ABI with their arguments checked and
-marshalled once (Bound calls), so short kernels are not timed against
-Python's argument checks.  For comparison the same steps are also timed as
-replays of a HIP graph holding 10 steps (unless --no-graph), after checking
-that a one-step graph replayed three times (inputs restored, outputs
-poisoned in between) reproduces the eager step bit for bit.  The default
-W = 1000 warm-up steps (about 25 ms on the headline workload) let the GPU
-clocks settle: the first few hundred launches after idle run up to 15 %
-slower.  The other workloads are timed the same way with about 30 ms of
-warm-up and 50 ms of timed steps each.
+
+The headline workload (default 4: bf16 GQA + RoPE prefill B1 Hq32 Hkv8
+T16384 d128, the largest configuration; it fits one GPU) is timed for K
+steps after W warm-up steps (at least 10): an event is recorded on the
+stream the kernels run on before the first step and after every step, so
+the line carries the mean step time (total / K, "ms_per_step", from which
+"value" is computed) and the median of the K step times
+("ms_per_step_median").  The K steps are launched back to back through the
+C ABI with their arguments checked and marshalled once (Bound calls), so
+short kernels are not timed against Python's argument checks.  For
+comparison the same steps are also timed as replays of a HIP graph holding
+10 steps (unless --no-graph), after checking that a one-step graph replayed
+three times (inputs restored, outputs poisoned in between) reproduces the
+eager step bit for bit.  The other workloads are timed the same way with
+at least 10 warm-up steps (about 30 ms) and at least 50 timed steps (about
+50 ms) each.
 
 FLOPs (causal-adjusted): 4 * B * Hq * d * N_vis, N_vis = sum_i min(Tk,
 q_offset + i + 1), i.e. two matrix products over the visible (query, key)
-pairs only.  Algorithmic bytes of attention: elt * d * (2 B Hq Tq + 2 B Hkv Tk)
-(q and o once, k and v once per K/V head).  RoPE bytes: read + write of q
-and k.
+pairs only ("Transformer" (ai-notes) -- Discussion (Compute)).  Algorithmic
+bytes of attention: elt * d * (2 B Hq Tq + 2 B Hkv Tk) (q and o once, k and
+v once per K/V head).  RoPE bytes: read + write of q and k.
+
+Roofline of every workload: its arithmetic intensity (FLOPs / algorithmic
+bytes) against the ridge of the published peaks (2516.6 TFLOP/s dense bf16
+/ 8000 GB/s = 314.6 FLOP/B) decides the bound -- "mfma" at or above the
+ridge, "hbm" below; "frac" is the fraction of that bound's peak, and the
+fractions of both peaks are reported beside it.  Measured ceilings (a
+matrix-core loop and a streaming read, librocattn_calib.so) are reported in
+"measured_peaks" next to the published ones.
 
 Also printed in the same line (unless --no-also): the other workloads'
-per-kernel rates, each timed the same way, so every part of the path has a
-live number; and a CPU baseline: the fp64 oracle timed on the host cores
-on a bounded sample of the headline workload.  The attention gradients
+rates, each timed the same way, so every part of the path has a live
+number; and a CPU baseline: the fp64 oracle timed on the host cores on a
+bounded sample of the headline workload.  The attention gradients
 (attn_bwd) are timed on the shapes of workloads 2 and 3 ("backward"), and
 attention with values of their own width (attn_fwd_dv) on workload 3's
 shape ("value_width").
 
 --calib-copy runs only a plain device copy of a known size (used to scale
-the HBM byte counters of a profiler run).
+the HBM byte counters of a profiler run); --calib-mfma and --calib-hbm run
+only the matrix-core loop or the streaming read and print their rates.
 """
 from __future__ import annotations
 
@@ -114,29 +127,36 @@ def measured_traffic(kernel, workload_name):
 
 
 class Timer:
-    """HIP events around n runs of fn() on the current stream: direct
-    launches, or (graph=True) replays of a HIP graph holding REPS runs."""
+    """HIP events around n runs of fn() on the current stream (the stream
+    the bindings launch on): direct launches, or (graph=True) replays of a
+    HIP graph holding REPS runs.  Returns the mean time per run in ms; for
+    direct launches, last_times holds each run's own time (an event is
+    recorded before the first run and after every run)."""
 
     REPS = 10
+    MIN_WARMUP = 10
 
     def __init__(self, torch, graph=False):
         self.torch = torch
         self.eager = not graph
+        self.last_times = []
 
     def __call__(self, fn, n, warmup):
         torch = self.torch
-        for _ in range(warmup):
+        for _ in range(max(warmup, self.MIN_WARMUP)):
             fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         if self.eager:
-            e0.record()
-            for _ in range(n):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            ev[0].record()
+            for i in range(n):
                 fn()
-            e1.record()
+                ev[i + 1].record()
             torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / n  # ms
+            self.last_times = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+            return ev[0].elapsed_time(ev[n]) / n  # ms
         reps = min(self.REPS, n)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -152,6 +172,37 @@ class Timer:
         torch.cuda.synchronize()
         del g
         return e0.elapsed_time(e1) / (n_replay * reps)  # ms
+
+    def median(self):
+        t = sorted(self.last_times)
+        return t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+
+
+RIDGE = PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3   # FLOP per byte where the two roofs meet
+
+
+def roofline(flops, nbytes, ms, dtype, ms_median=None):
+    """Bound from the arithmetic intensity against the ridge of the published
+    peaks, the fraction of that bound's peak, and both fractions."""
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    intensity = flops / nbytes
+    if dtype == "f32":
+        bound, achieved, peak, unit = "alu", tf, PEAK_F32_TFLOPS, "TFLOP/s"
+    elif intensity >= RIDGE:
+        bound, achieved, peak, unit = "mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", gbs, PEAK_HBM_GBS, "GB/s"
+    r = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+         "intensity_flop_per_byte": intensity, "ridge_flop_per_byte": RIDGE,
+         "tflops": tf, "gbs": gbs}
+    if dtype != "f32":
+        r["frac_of_mfma_peak"] = tf / PEAK_BF16_TFLOPS
+        r["frac_of_hbm_peak"] = gbs / PEAK_HBM_GBS
+    if ms_median is not None:
+        r["achieved_median"] = achieved * ms / ms_median
+        r["frac_median"] = r["achieved_median"] / peak
+    return r
 
 
 def check_graph_replay(torch, fn, outputs, inputs, replays=3):
@@ -271,18 +322,23 @@ def single_launch_ms(torch, dev, fn, cold, n=21, scratch_bytes=512 << 20):
 
 def measure(w, args, torch, ra, wl, dev, steps=None, warmup=None, cold=False):
     """Times of one workload's step, attention and RoPE launches.  Without
-    explicit counts: about 30 ms of warm-up and 50 ms of timed steps.  With
-    cold=True also the attention launch after a cache-evicting write."""
+    explicit counts: about 30 ms (at least 10 steps) of warm-up and 50 ms (at
+    least 50 steps) of timed steps.  With cold=True also the attention launch
+    after a cache-evicting write."""
     s = setup(w, torch, ra, wl, dev)
     timer = Timer(torch)
     if steps is None or warmup is None:
         t_est = timer(s["step_b"], 3, 1) * 1e-3
-        warmup = max(5, int(0.03 / t_est))
-        steps = max(10, int(0.05 / t_est))
+        warmup = max(10, int(0.03 / t_est))
+        steps = max(50, int(0.05 / t_est))
     ms_step = timer(s["step_b"], steps, warmup)
+    ms_step_median = timer.median()
     ms_attn = timer(s["attn_b"], steps, warmup)
-    out = dict(workload=w.name, ms_per_step=ms_step, attn_ms=ms_attn,
-               timing="back-to-back launches, arguments marshalled once")
+    ms_attn_median = timer.median()
+    out = dict(workload=w.name, steps=steps, warmup=max(warmup, Timer.MIN_WARMUP),
+               ms_per_step=ms_step, ms_per_step_median=ms_step_median,
+               attn_ms=ms_attn, attn_ms_median=ms_attn_median,
+               timing="back-to-back launches, arguments marshalled once; an event after every step")
     if cold:
         out["attn_ms_single_launch_warm"] = single_launch_ms(torch, dev, s["attn_b"], False)
         out["attn_ms_single_launch_cold_mall"] = single_launch_ms(torch, dev, s["attn_b"], True)
@@ -301,9 +357,8 @@ def measure(w, args, torch, ra, wl, dev, steps=None, warmup=None, cold=False):
     out["attn_kernel"] = kernel
     out["attn_tflops"] = fl / (ms_attn * 1e-3) / 1e12
     out["attn_gbs"] = by / (ms_attn * 1e-3) / 1e9
-    peak_flops = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
-    out["attn_pct_mfma_peak"] = 100.0 * out["attn_tflops"] / peak_flops
-    out["attn_pct_hbm_peak"] = 100.0 * out["attn_gbs"] / PEAK_HBM_GBS
+    out["roofline_attn"] = roofline(fl, by, ms_attn, w.dtype, ms_attn_median)
+    out["roofline_step"] = roofline(fl, by, ms_step, w.dtype, ms_step_median)
     if s["rope"] is not None:
         ms_rope = timer(s["rope_b"], steps, warmup)
         rb = rope_bytes(w, s["decode"])
@@ -501,16 +556,100 @@ def calib_copy(torch, dev, nbytes=1 << 30, reps=5):
                       "reps": reps}))
 
 
+CALIB_LIBRARY = os.path.join(ROOT, "transformer_causal_self_amd", "librocattn_calib.so")
+
+
+def calib_library():
+    import ctypes
+    if not os.path.exists(CALIB_LIBRARY):
+        raise RuntimeError(f"{CALIB_LIBRARY} is not built: run __graft_entry__.build()")
+    lib = ctypes.CDLL(CALIB_LIBRARY)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.calib_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.calib_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.calib_mfma_loop_flops.restype = ctypes.c_double
+    lib.calib_stream_read.argtypes = [vp, sz, ctypes.c_int, vp, vp]
+    lib.calib_stream_copy.argtypes = [vp, vp, sz, ctypes.c_int, vp]
+    return lib
+
+
+MFMA_LOOP_WG, MFMA_LOOP_ITERS = 2048, 4000    # 8 waves per SIMD (two rounds of 4); ~2 ms
+STREAM_BYTES, STREAM_WG = 2 << 30, 4096       # 2 GiB: far past the 256 MB MALL
+
+
+def measured_peaks(torch, dev, reps=10):
+    """The matrix-core loop and the streaming read and copy of
+    librocattn_calib.so, timed with events on the current stream (median of
+    `reps` launches after 3 warm-up launches)."""
+    lib = calib_library()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def med(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    sink = torch.empty(max(MFMA_LOOP_WG, STREAM_WG), dtype=torch.float32, device=dev)
+
+    def mfma():
+        if lib.calib_mfma_loop(MFMA_LOOP_WG, MFMA_LOOP_ITERS, sink.data_ptr(), stream) != 0:
+            raise RuntimeError("calib_mfma_loop failed")
+
+    ms_mfma = med(mfma)
+    tf = lib.calib_mfma_loop_flops(MFMA_LOOP_WG, MFMA_LOOP_ITERS) / (ms_mfma * 1e-3) / 1e12
+    src = torch.empty(STREAM_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+
+    def read():
+        if lib.calib_stream_read(src.data_ptr(), STREAM_BYTES, STREAM_WG, sink.data_ptr(), stream) != 0:
+            raise RuntimeError("calib_stream_read failed")
+
+    ms_read = med(read)
+    half = STREAM_BYTES // 2
+    dst = torch.empty(half, dtype=torch.uint8, device=dev)
+
+    def copy():
+        if lib.calib_stream_copy(src.data_ptr(), dst.data_ptr(), half, STREAM_WG, stream) != 0:
+            raise RuntimeError("calib_stream_copy failed")
+
+    ms_copy = med(copy)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {
+        "mfma_bf16_loop_tflops": tf,
+        "mfma_bf16_loop_frac_of_published": tf / PEAK_BF16_TFLOPS,
+        "hbm_stream_read_gbs": STREAM_BYTES / (ms_read * 1e-3) / 1e9,
+        "hbm_stream_copy_gbs": 2 * half / (ms_copy * 1e-3) / 1e9,
+        "published": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS},
+        "how": (f"v_mfma_f32_32x32x16_bf16 loop, {MFMA_LOOP_WG} workgroups x 4 waves x "
+                f"{MFMA_LOOP_ITERS} rounds of 4 products; 16-byte streaming read of "
+                f"{STREAM_BYTES >> 30} GiB and copy of {half >> 30} GiB, {STREAM_WG} workgroups; "
+                f"median of {reps} launches"),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-also", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--calib-mfma", action="store_true")
+    ap.add_argument("--calib-hbm", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP graph replay comparison")
     args = ap.parse_args()
@@ -533,11 +672,15 @@ def main():
     if args.calib_copy:
         calib_copy(torch, dev)
         return
+    if args.calib_mfma or args.calib_hbm:
+        print(json.dumps(measured_peaks(torch, dev)))
+        return
 
     w = wl.WORKLOADS[args.workload]
-    head = measure(w, args, torch, ra, wl, dev, args.steps, args.warmup, cold=True)
-    print(f"# {w.name}: step {head['ms_per_step'] * 1e3:.2f} us, attention "
-          f"{head['attn_ms'] * 1e3:.2f} us = {head['attn_tflops']:.1f} TFLOP/s", file=sys.stderr)
+    head = measure(w, args, torch, ra, wl, dev, args.steps, args.warmup, cold=(args.workload == 2))
+    print(f"# {w.name}: step {head['ms_per_step'] * 1e3:.2f} us (median "
+          f"{head['ms_per_step_median'] * 1e3:.2f}), attention {head['attn_ms'] * 1e3:.2f} us",
+          file=sys.stderr)
 
     decode = head["attn_kernel"] == "decode_bf16"
     step_s = head["ms_per_step"] * 1e-3
@@ -548,19 +691,21 @@ def main():
         metric_val = head["step_flops"] / step_s / 1e12
         unit = "TFLOP/s"
 
-    # roofline of the dominant kernel, from its own event-timed launches
+    # Roofline of the dominant kernel from the event-timed steps.  For the
+    # RoPE prefills a step is one attn_fwd_rope call: the prefill kernel plus
+    # the RoPE pass on k (about 1 % of the step at 16384 keys), so the rate
+    # is a slight underestimate of the prefill kernel's own.
     kernel = head["attn_kernel"]
-    if decode:
-        achieved = head["attn_gbs"]
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS}
+    if w.rope and not decode:
+        roof = dict(head["roofline_step"])
+        roof["kernel"] = f"{kernel} (query-load RoPE) + rope pass on k: one attn_fwd_rope call"
+        roof["launch_us"] = head["ms_per_step"] * 1e3
+        roof["launch_us_median"] = head["ms_per_step_median"] * 1e3
     else:
-        peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
-        achieved = head["attn_tflops"]
-        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved,
-                "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
-    roof["kernel"] = kernel
-    roof["launch_us"] = head["attn_ms"] * 1e3
+        roof = dict(head["roofline_attn"])
+        roof["kernel"] = kernel
+        roof["launch_us"] = head["attn_ms"] * 1e3
+        roof["launch_us_median"] = head["attn_ms_median"] * 1e3
     roof["algorithmic_bytes"] = head["attn_bytes"]
     roof["algorithmic_flops"] = head["step_flops"]
     roof["traffic"] = measured_traffic(kernel, w.name)
@@ -571,8 +716,9 @@ def main():
         "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": head["warmup"],
         "ms_per_step": head["ms_per_step"],
+        "ms_per_step_median": head["ms_per_step_median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -580,16 +726,22 @@ def main():
         "data": "synthetic (seeded N(0, sigma^2) q/k/v, see transformer_causal_self_amd/workloads.py)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tq": w.Tq,
                    "Tk": w.Tk, "d_head": w.d, "causal": w.causal, "q_offset": w.q_offset,
-                   "scale": w.scale, "rope": w.rope, "parallelism": "single GPU"},
+                   "scale": w.scale, "rope": w.rope, "sigma": w.sigma, "parallelism": "single GPU"},
         "pct_of_peak": 100.0 * roof["frac"],
         "roofline": roof,
         "timing": head["timing"],
+        "attn_ms_plain_prefill": head["attn_ms"],
         "ms_per_step_graph": head.get("ms_per_step_graph"),
         "attn_ms_single_launch_warm": head.get("attn_ms_single_launch_warm"),
         "attn_ms_single_launch_cold_mall": head.get("attn_ms_single_launch_cold_mall"),
         "ms_per_step_rope_then_attn": head.get("ms_per_step_rope_then_attn"),
         "graph_replay_matches_eager": head.get("graph_replay_matches_eager"),
     }
+    line["measured_peaks"] = measured_peaks(torch, dev)
+    mp = line["measured_peaks"]
+    roof["frac_of_measured_peak"] = (roof["tflops"] / mp["mfma_bf16_loop_tflops"] if roof["bound"] == "mfma"
+                                     else roof["gbs"] / mp["hbm_stream_read_gbs"] if roof["bound"] == "hbm"
+                                     else None)
 
     if not args.no_also:
         also = {}
@@ -597,7 +749,7 @@ def main():
             if key == args.workload:
                 continue
             wo = wl.WORKLOADS[key]
-            r = measure(wo, args, torch, ra, wl, dev)
+            r = measure(wo, args, torch, ra, wl, dev, cold=(key == 2))
             r = {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in r.items()}
             r["attn_traffic"] = measured_traffic(r["attn_kernel"], wo.name)
             also[str(key)] = r

@@ -72,7 +72,8 @@ typedef enum {
     ROCATTN_OK = 0,
     ROCATTN_ERR_NULL = -1,      /* a required pointer is NULL */
     ROCATTN_ERR_SHAPE = -2,     /* a size <= 0, Hq % Hkv != 0, overlap of o with an input,
-                                   or a tensor too large for 64-bit element offsets */
+                                   a tensor too large for 64-bit element offsets, or
+                                   Tq + Tk > INT_MAX - 1024 (row/key limits are 32-bit) */
     ROCATTN_ERR_DTYPE = -3,     /* dtype not a rocattn_dtype */
     ROCATTN_ERR_HEADDIM = -4,   /* d_head not supported for this dtype / entry point */
     ROCATTN_ERR_OFFSET = -5,    /* causal with q_offset < 0: row 0 would see no key */
@@ -92,7 +93,8 @@ typedef enum {
  *             attention, any finite value (a temperature; 0 gives the mean of
  *             the visible values).
  *   causal    non-zero: causal rule above; zero: no mask.
- *   q_offset  position of query row 0 (causal only; must be >= 0).
+ *   q_offset  position of query row 0 (causal only; must be >= 0).  Any
+ *             q_offset >= Tk - 1 makes every key visible to every row.
  *   dtype     rocattn_dtype of q, k, v and o.
  *   stream    hipStream_t.
  *

@@ -16,8 +16,12 @@ pytestmark = pytest.mark.skipif(not os.path.exists(rocattn.LIBRARY),
                                 reason="librocattn.so not built")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+CALIB_HEADER = os.path.join(ROOT, "include", "rocattn_calib.h")
+CALIB_LIBRARY = os.path.join(os.path.dirname(rocattn.LIBRARY), "librocattn_calib.so")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
@@ -30,6 +34,24 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(rocattn.LIBRARY)
     for name in declared_functions():
         assert hasattr(lib, name), name
+
+
+@pytest.mark.skipif(not os.path.exists(CALIB_LIBRARY), reason="librocattn_calib.so not built")
+def test_calib_library_exports_every_declared_symbol():
+    names = declared_functions(CALIB_HEADER)
+    assert names == ["calib_mfma_loop", "calib_mfma_loop_flops", "calib_stream_copy", "calib_stream_read"]
+    lib = ctypes.CDLL(CALIB_LIBRARY)
+    for name in names:
+        assert hasattr(lib, name), name
+    lib.calib_mfma_loop_flops.restype = ctypes.c_double
+    # 4 waves x 4 products of 32 x 32 x 16 multiply-adds per round
+    assert lib.calib_mfma_loop_flops(3, 5) == 2.0 * 32 * 32 * 16 * 4 * 5 * 4 * 3
+    # rejected before any launch
+    assert lib.calib_mfma_loop(0, 5, ctypes.c_void_p(0x1000), None) == -1
+    assert lib.calib_stream_read(ctypes.c_void_p(0x1008), ctypes.c_size_t(64), 4,
+                                 ctypes.c_void_p(0x2000), None) == -7
+    assert lib.calib_stream_copy(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1010), ctypes.c_size_t(64), 4,
+                                 None) == -2
 
 
 def test_status_strings():
@@ -57,6 +79,8 @@ def fwd(q=A, k=Bp, v=C, o=D, B=1, Hq=4, Hkv=2, Tq=16, Tk=16, d=64, scale=0.125, 
     (dict(dtype=2), -3), (dict(dtype=-1), -3),
     (dict(d=96), -4), (dict(d=32), -4), (dict(d=258, dtype=F32), -4), (dict(d=6, dtype=F32), -4),
     (dict(q_offset=-1), -5),
+    (dict(q_offset=2**31 - 16), -5),      # q_offset + Tq past INT_MAX
+    (dict(Tq=2**30, Tk=2**30 - 1000, Hq=1, Hkv=1), -2),   # Tq + Tk past the 32-bit row/key limits
     (dict(scale=float("inf")), -6), (dict(scale=float("nan")), -6),
     (dict(q=A + 8), -7), (dict(o=D + 2), -7),
     (dict(o=A), -2),                      # output aliases q

@@ -8,8 +8,8 @@ key is zero except a few spikes, so each visible key gets weight e^0 = 1
 and a spike key e^s; values are quarters of small integers periodic in the
 token and channel, plus 1/16 of the (batch, K/V head) index (all exact in
 bf16, |o| < 2 so that the output's own bf16 rounding stays under 4e-3).  For a row that sees
-keys 0 .. L-1 the softmax of the pages ("Attention is All You Need" —
-scaled dot-product attention) then gives
+keys 0 .. L-1 the softmax of "Transformer" (ai-notes) -- Scaled
+dot-product attention then gives
     o[c] = (sum_j v[j][c] + sum_spikes (e^s - 1) v[j*][c]) / (L + sum_spikes (e^s - 1)).
 e^s (1.4e6) is comparable to L (2^21), so each spike carries a fifth to a
 third of a row's weight: a spike missed, or a value slice read from another

@@ -1,9 +1,11 @@
-"""Compile librocattn.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Compile librocattn.so (the HIP kernels and the C ABI) for gfx950 with hipcc,
+and librocattn_calib.so (the matrix-core and streaming microbenchmarks the
+benchmark quotes beside the published peaks).
 
     python -m transformer_causal_self_amd.build
 
 Objects are compiled in parallel into ``_build/`` and linked in place, so
-the shared library sits next to the Python binding that loads it.
+the shared libraries sit next to the Python binding that loads them.
 """
 from __future__ import annotations
 
@@ -20,6 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "librocattn.so")
 SOURCES = ["api.cpp", "attn_f32.hip", "attn_prefill_bf16.hip",
            "attn_decode_bf16.hip", "attn_bwd_bf16.hip", "rope.hip"]
+CALIB_LIBRARY = os.path.join(HERE, "librocattn_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -49,19 +53,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link librocattn.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIBRARY + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIBRARY)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link librocattn.so and librocattn_calib.so;
+    returns the attention library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIBRARY)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_LIBRARY)
     if verbose:
-        print(LIBRARY, file=sys.stderr)
+        print(LIBRARY, CALIB_LIBRARY, file=sys.stderr)
     return LIBRARY
 
 

@@ -34,6 +34,18 @@ long long count4(long long a, long long b, long long c, long long d) {
     return n;
 }
 
+// The kernels form row and key limits such as q_offset + (first row of a
+// tile) + (tile rows) in 32-bit integers, with q_offset clamped to Tk first
+// (clamped_offset): Tq + Tk plus a tile's rows must stay below INT_MAX.
+bool sizes_fit_int(int Tq, int Tk) { return (long long)Tq + Tk <= (long long)INT_MAX - 1024; }
+
+// A causal offset at or past Tk - 1 makes every key visible to every row,
+// exactly as Tk does; clamping keeps q_offset + Tq within 32 bits in the
+// kernels' limit arithmetic (given sizes_fit_int).
+int clamped_offset(int causal, int q_offset, int Tk) {
+    return causal ? (q_offset < Tk ? q_offset : Tk) : 0;
+}
+
 int check_fwd(const void* q, const void* k, const void* v, const void* o, int B, int Hq,
               int Hkv, int Tq, int Tk, int d, float scale, int causal, int q_offset,
               int dtype, const float* lse) {
@@ -49,6 +61,7 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, int B,
     }
     if (causal && q_offset < 0) return ROCATTN_ERR_OFFSET;
     if (causal && (long long)q_offset + Tq > INT_MAX) return ROCATTN_ERR_OFFSET;
+    if (!sizes_fit_int(Tq, Tk)) return ROCATTN_ERR_SHAPE;
     if (!isfinite(scale)) return ROCATTN_ERR_SCALE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ROCATTN_ERR_ALIGN;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ROCATTN_ERR_ALIGN;
@@ -133,7 +146,7 @@ FwdParams make_params(const void* q, const void* k, const void* v, void* o, floa
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Tq = Tq; p.Tk = Tk; p.d = d;
     p.scale = scale;
     p.causal = causal ? 1 : 0;
-    p.q_offset = causal ? q_offset : 0;
+    p.q_offset = clamped_offset(causal, q_offset, Tk);
     // dense [B][H][T][d]
     p.qs = {(long long)Hq * Tq * d, (long long)Tq * d, d};
     p.os = p.qs;
@@ -190,6 +203,7 @@ int check_strided(const void* q, const void* k, const void* v, const void* o, in
     }
     if (causal && q_offset < 0) return ROCATTN_ERR_OFFSET;
     if (causal && (long long)q_offset + Tq > INT_MAX) return ROCATTN_ERR_OFFSET;
+    if (!sizes_fit_int(Tq, Tk)) return ROCATTN_ERR_SHAPE;
     if (!isfinite(scale)) return ROCATTN_ERR_SCALE;
     const size_t elt = dtype == ROCATTN_F32 ? 4 : 2;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ROCATTN_ERR_ALIGN;
@@ -390,6 +404,7 @@ ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, 
         if (Hq > 65535 || B > 65535) return ROCATTN_ERR_SHAPE;
     }
     if (pos < 0 || (long long)pos + Tn > Tmax) return ROCATTN_ERR_OFFSET;
+    if (!sizes_fit_int(Tn, Tmax)) return ROCATTN_ERR_SHAPE;
     if (!isfinite(scale)) return ROCATTN_ERR_SCALE;
     if (!isfinite(rope_base) || !(rope_base > 0.0)) return ROCATTN_ERR_SCALE;
     if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
@@ -455,6 +470,7 @@ ROCATTN_API int attn_fwd_dv(const void* q, const void* k, const void* v, void* o
     if (dtype == ROCATTN_F32 && (Hq > 65535 || B > 65535)) return ROCATTN_ERR_SHAPE;
     if (causal && q_offset < 0) return ROCATTN_ERR_OFFSET;
     if (causal && (long long)q_offset + Tq > INT_MAX) return ROCATTN_ERR_OFFSET;
+    if (!sizes_fit_int(Tq, Tk)) return ROCATTN_ERR_SHAPE;
     if (!isfinite(scale)) return ROCATTN_ERR_SCALE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ROCATTN_ERR_ALIGN;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ROCATTN_ERR_ALIGN;
@@ -545,6 +561,7 @@ ROCATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void
     if (d_head != 64 && d_head != 128) return ROCATTN_ERR_HEADDIM;
     if (causal && q_offset < 0) return ROCATTN_ERR_OFFSET;
     if (causal && (long long)q_offset + Tq > INT_MAX) return ROCATTN_ERR_OFFSET;
+    if (!sizes_fit_int(Tq, Tk)) return ROCATTN_ERR_SHAPE;
     if (!isfinite(scale)) return ROCATTN_ERR_SCALE;
     const void* in[6] = {q, k, v, o, dO, lse};
     void* out[3] = {dq, dk, dv};
@@ -578,7 +595,7 @@ ROCATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Tq = Tq; p.Tk = Tk; p.d = d_head;
     p.scale = scale;
     p.causal = causal ? 1 : 0;
-    p.q_offset = causal ? q_offset : 0;
+    p.q_offset = clamped_offset(causal, q_offset, Tk);
     return rocattn::launch_bwd_bf16(p, static_cast<hipStream_t>(stream)) == hipSuccess ? ROCATTN_OK
                                                                                         : ROCATTN_ERR_HIP;
 }
