@@ -142,6 +142,32 @@ int attn_fwd_ws(const void* q, const void* k, const void* v, void* o,
                 void* workspace, size_t ws_bytes, float* lse);
 
 /*
+ * attn_fwd_noalloc -- attn_fwd_ws that allocates nothing, for callers that
+ * cannot call hipMalloc: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Instead of a caller's workspace it
+ * uses the library's fixed scratch buffer of the current device
+ * (hipGetDevice; `stream` must belong to that device): 64 MiB of device
+ * memory per GPU, a static array that each GPU the library runs on holds
+ * until the process ends; its address is looked up once per device and no
+ * allocating call (hipMalloc, hipMallocAsync, hipFree, torch) is made.
+ *
+ *   Arguments as attn_fwd_ws without workspace / ws_bytes; lse optional.
+ *   A call whose required workspace (a bf16 decode step's partial results,
+ *   attn_workspace_bytes()) exceeds 64 MiB is rejected with ERR_WORKSPACE
+ *   before anything is launched; a small prefill uses the optional key
+ *   splits when their partials fit, else runs unsplit.  Results are
+ *   bit-identical to attn_fwd_ws with a workspace of attn_workspace_bytes()
+ *   bytes whenever that is at most 64 MiB.
+ *   Every call on one GPU shares its scratch buffer and leaves the last
+ *   call's partial results in it: calls that overlap on one GPU (other
+ *   streams, other host threads without ordering) race and must not be
+ *   issued.  Returns a rocattn_status.
+ */
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                     int B, int Hq, int Hkv, int Tq, int Tk, int d_head,
+                     float scale, int causal, int q_offset, int dtype, void* stream, float* lse);
+
+/*
  * attn_fwd_strided -- attn_fwd_ws on tensors laid out with arbitrary
  * batch / head / token strides, e.g. [B][T][H][d] ("BTHD") inputs sliced
  * from a fused projection and an output written straight in the

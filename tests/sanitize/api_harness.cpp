@@ -101,6 +101,10 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t) {
     EXPECT(p.workspace != nullptr);
     return hipSuccess;
 }
+hipError_t noalloc_scratch(void** ptr) {
+    *ptr = reinterpret_cast<void*>(0x7100000000ull);
+    return hipSuccess;
+}
 hipError_t launch_step_prep(void* q, const void* kn, const void* vn, void* kc, void* vc, int, int, int,
                             int Tn, int Tmax, int, int pos, double, int, int, hipStream_t) {
     ++launches;
@@ -155,6 +159,16 @@ int main() {
                        nullptr) == ROCATTN_ERR_SHAPE);   // workspace over q
     EXPECT(attn_workspace_bytes(1, 4, 2, 16, 16, 96, BF) == 0);
     EXPECT(attn_workspace_bytes(1, 4, 2, 16, 16, 64, 7) == 0);
+
+    // the entry point that allocates nothing: its fixed scratch serves a
+    // decode step of the decode workload's size; a larger one is refused
+    EXPECT(attn_fwd_noalloc(q, k, v, o, 32, 32, 8, 1, 8192, 128, 0.1f, 1, 8191, BF, nullptr, lse) == ROCATTN_OK);
+    EXPECT(attn_fwd_noalloc(q, k, v, o, 1, 4, 2, 300, 2000, 128, 0.1f, 1, 1700, BF, nullptr, nullptr) ==
+           ROCATTN_OK);
+    EXPECT(attn_fwd_noalloc(q, k, v, o, 1024, 32, 8, 1, 1 << 20, 128, 0.1f, 1, (1 << 20) - 1, BF, nullptr,
+                            nullptr) == ROCATTN_ERR_WORKSPACE);
+    EXPECT(attn_fwd_noalloc(q, k, v, o, 1, 4, 2, 16, 16, 96, 0.1f, 1, 0, BF, nullptr, nullptr) ==
+           ROCATTN_ERR_HEADDIM);
 
     // strided: BTHD views of q and o, dense k and v
     const long long st[12] = {16 * 4 * 64, 64, 4 * 64, 2 * 16 * 64, 16 * 64, 64,

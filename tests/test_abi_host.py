@@ -102,6 +102,20 @@ def test_attn_fwd_ws_rejects_small_workspace_and_bad_lse():
     assert lib.attn_fwd_ws(*args, 0x70000000, need, 0x7F000002) == -7  # misaligned lse
 
 
+def test_attn_fwd_noalloc_refuses_a_workspace_past_its_scratch():
+    """attn_fwd_noalloc serves splits from a fixed 64 MiB device buffer: a
+    decode step whose partial results need more is refused before anything
+    runs (fake pointers; nothing is dereferenced or launched)."""
+    lib = rocattn.library()
+    need = lib.attn_workspace_bytes(1024, 32, 8, 1, 1 << 20, 128, BF16)
+    assert need > 64 << 20
+    far = [ctypes.c_void_p(0x100000000000 * (i + 1)) for i in range(4)]   # 16 TiB apart: no overlap
+    assert lib.attn_fwd_noalloc(*far, 1024, 32, 8, 1, 1 << 20, 128, 0.088, 1, (1 << 20) - 1, BF16,
+                                None, None) == -8
+    assert lib.attn_fwd_noalloc(A, Bp, C, D, 1, 4, 2, 16, 16, 96, 0.088, 1, 0, BF16, None, None) == -4
+    assert lib.attn_fwd_noalloc(None, Bp, C, D, 1, 4, 2, 16, 16, 64, 0.088, 1, 0, BF16, None, None) == -1
+
+
 def test_workspace_bytes():
     lib = rocattn.library()
     assert lib.attn_workspace_bytes(8, 12, 12, 1024, 1024, 64, BF16) == 0     # prefill

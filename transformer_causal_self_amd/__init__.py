@@ -11,6 +11,8 @@ or a call is made with CPU tensors, the call raises.
     attn_fwd_ws(q, k, v, o, workspace, lse=None, scale=None, causal=True, q_offset=0)
         (tensors that are views with contiguous rows, e.g. [B, T, H, d] memory
         transposed to [B, H, T, d], go to attn_fwd_strided)
+    attn_fwd_noalloc(q, k, v, o, lse=None, scale=None, causal=True, q_offset=0)
+        (no workspace, no allocation: the library's fixed device scratch)
     attn_workspace_bytes(B, Hq, Hkv, Tq, Tk, d_head, dtype)
     rope_apply(q, k=None, pos0=0, base=10000.0, pairing="split"|"adjacent")
     status_string(code)
@@ -37,7 +39,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "librocattn.so")
 
 # the C ABI, as declared in include/rocattn.h
-SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_strided", "attn_workspace_bytes",
+SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_noalloc", "attn_fwd_strided", "attn_workspace_bytes",
            "rope_apply", "rope_apply_ex", "rope_apply_pos", "attn_decode_step", "attn_fwd_dv", "attn_fwd_rope",
            "attn_fwd_rope_workspace_bytes", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_status_string")
@@ -74,6 +76,8 @@ def library() -> ctypes.CDLL:
         lib.attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
         lib.attn_fwd_ws.restype = i
         lib.attn_fwd_ws.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, vp, sz, vp]
+        lib.attn_fwd_noalloc.restype = i
+        lib.attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, vp]
         lib.attn_fwd_strided.restype = i
         lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, ctypes.POINTER(ctypes.c_longlong),
                                          i, i, i, i, i, i, f, i, i, i, vp, vp, sz, vp]
@@ -266,6 +270,27 @@ def _attn_fwd_ws_call(q, k, v, o, workspace, lse, scale, causal, q_offset, strea
             _stream(q, stream), _ptr(workspace), ws_bytes, _ptr(lse))
     return Bound("attn_fwd_strided", library().attn_fwd_strided, args,
                  (q, k, v, o, workspace, lse, strides))
+
+
+def attn_fwd_noalloc(q, k, v, o, lse=None, scale=None, causal=True, q_offset=0, stream=None):
+    """attn_fwd_ws without a workspace argument and without any allocation:
+    the library's fixed 64 MiB device scratch buffer of the current device
+    serves the split-K partial results (dense tensors only).  Calls that
+    overlap on one GPU must not be issued (they share that buffer)."""
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{n} must be dense (contiguous)")
+    B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt = _fwd_args(q, k, v, o, scale, causal, q_offset)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, Hq, Tq):
+            raise ValueError("lse must be [B, Hq, Tq]")
+    st = library().attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Tq, Tk, d, sc, ca, qo, dt,
+                                    _stream(q, stream), _ptr(lse))
+    if st != OK:
+        raise RocattnError("attn_fwd_noalloc", st)
+    return o
 
 
 def attn_fwd_ws(q, k, v, o, workspace=None, lse=None, scale=None, causal=True, q_offset=0,

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "librocattn.so")
 SOURCES = ["api.cpp", "attn_f32.hip", "attn_prefill_bf16.hip",
-           "attn_decode_bf16.hip", "attn_bwd_bf16.hip", "rope.hip"]
+           "attn_decode_bf16.hip", "attn_bwd_bf16.hip", "rope.hip", "noalloc.hip"]
 CALIB_LIBRARY = os.path.join(HERE, "librocattn_calib.so")
 CALIB_SOURCES = ["calib.hip"]
 

@@ -290,6 +290,23 @@ ROCATTN_API int attn_fwd_ws(const void* q, const void* k, const void* v, void* o
     return launch(p, dtype, static_cast<hipStream_t>(stream), wsb ? workspace : nullptr, wsb);
 }
 
+ROCATTN_API int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int Hq,
+                                 int Hkv, int Tq, int Tk, int d_head, float scale, int causal,
+                                 int q_offset, int dtype, void* stream, float* lse) {
+    int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d_head, scale, causal, q_offset, dtype, lse);
+    if (st != ROCATTN_OK) return st;
+    const size_t req = workspace_required(B, Hq, Hkv, Tq, Tk, d_head, dtype);
+    if (req > rocattn::kNoAllocScratchBytes) return ROCATTN_ERR_WORKSPACE;
+    // the optional key splits of a small prefill only when their partials fit
+    const size_t want = workspace_for(B, Hq, Hkv, Tq, Tk, d_head, dtype);
+    const size_t use = want <= rocattn::kNoAllocScratchBytes ? want : req;
+    void* scratch = nullptr;
+    if (use > 0 && rocattn::noalloc_scratch(&scratch) != hipSuccess) return ROCATTN_ERR_HIP;
+    const FwdParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d_head, scale, causal,
+                                    q_offset);
+    return launch(p, dtype, static_cast<hipStream_t>(stream), use ? scratch : nullptr, use);
+}
+
 ROCATTN_API int attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
                                  const long long* strides, int B, int Hq, int Hkv, int Tq,
                                  int Tk, int d_head, float scale, int causal, int q_offset,

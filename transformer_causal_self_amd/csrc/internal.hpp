@@ -109,6 +109,11 @@ struct BwdParams {
     int q_offset;
 };
 
+// The fixed device scratch buffer of attn_fwd_noalloc: kNoAllocScratchBytes
+// per device, its address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Gradients dq, dk, dv of the bf16 attention, d in {64, 128}.
 size_t bwd_workspace_bytes(int B, int Hq, int Tq);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
