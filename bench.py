@@ -380,11 +380,13 @@ CACHED_STEPS = [
 
 
 def measure_cached_steps(torch, ra, wl, dev):
-    """attn_decode_step (RoPE on the new rows, cache append, attention in two
-    launches plus the split-K combine) against the same step as separate
-    calls (rope_apply on q and on the new keys, two cache copies, attention
-    over the cache prefix).  Inputs are seeded draws; each timed call rotates
-    q again in place, which leaves the amount of work unchanged."""
+    """attn_decode_step (one launch for a one-token step: RoPE of the new
+    query and key, cache append, split-K attention and the merge of its
+    chunks; RoPE and append, then the attention, for a chunk of rows)
+    against the same step as separate calls (rope_apply on q and on the new
+    keys, two cache copies, attention over the cache prefix).  Inputs are
+    seeded draws; each timed call rotates q again in place, which leaves the
+    amount of work unchanged."""
     out = {}
     for name, B, Hq, Hkv, Tn, Tmax, pos, d in CACHED_STEPS:
         q, kn, vn = (x.to(dev) for x in wl.random_qkv(B, Hq, Hkv, Tn, Tn, d, seed=2001))
@@ -393,14 +395,15 @@ def measure_cached_steps(torch, ra, wl, dev):
         vc = vc.view(B, Hkv, Tmax, d).contiguous()
         o = torch.empty_like(q)
         scale = 1.0 / (d ** 0.5)
+        ws = ra.decode_step_workspace(q, kc)
         nb = ra.attn_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d, torch.bfloat16)
-        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        ws_attn = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
         fused = ra.bind_attn_decode_step(q, kn, vn, kc, vc, pos, o, scale=scale, workspace=ws)
         k2 = kn.clone()
         rope_q = ra.bind_rope_apply(q, None, pos0=pos)
         rope_k = ra.bind_rope_apply(k2, None, pos0=pos)
         kview, vview = kc[:, :, :pos + Tn], vc[:, :, :pos + Tn]
-        attn = ra.bind_attn_fwd_ws(q, kview, vview, o, ws, None, scale=scale, causal=True,
+        attn = ra.bind_attn_fwd_ws(q, kview, vview, o, ws_attn, None, scale=scale, causal=True,
                                    q_offset=pos)
 
         def unfused():
@@ -422,7 +425,7 @@ def measure_cached_steps(torch, ra, wl, dev):
                      "tflops": round(flops / (ms_f * 1e-3) / 1e12, 2)}
         print(f"# {name}: fused step {ms_f * 1e3:.1f} us, separate calls {ms_u * 1e3:.1f} us",
               file=sys.stderr)
-        del q, kn, vn, kc, vc, o, ws, k2, kview, vview
+        del q, kn, vn, kc, vc, o, ws, ws_attn, k2, kview, vview
         torch.cuda.empty_cache()
     return out
 

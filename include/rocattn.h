@@ -272,8 +272,14 @@ int rope_apply_pos(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head,
  *      tokens pos .. pos + Tn - 1; v_new is copied into v_cache there;
  *   3. o = attention of the rotated q over cache tokens 0 .. pos + Tn - 1,
  *      causal, q_offset = pos (row i sees tokens <= pos + i).
- * Steps 1-2 are one launch; step 3 is the attention of attn_fwd_ws (the
- * split-K decode kernels for bf16 Tn == 1, else the prefill kernel).
+ * bf16 with Tn == 1 (one new token per sequence, d_head 64 or 128, at
+ * most 16 query heads per K/V head): the whole step is ONE launch -- the
+ * split-K decode kernel rotates q as it loads it, the chunk of keys holding
+ * pos rotates the new key, appends it and the new value and uses them, and
+ * the last chunk of each (batch, K/V head) to finish merges the chunks'
+ * partial results, writes o (and lse) and writes q back rotated.  Otherwise
+ * steps 1-2 are one launch and step 3 is the attention of attn_fwd_ws (the
+ * prefill kernel).
  *
  *   q         [B][Hq][Tn][d_head], rotated in place (read, then written).
  *   k_new, v_new  [B][Hkv][Tn][d_head], read only (k_new is not rotated in
@@ -285,13 +291,29 @@ int rope_apply_pos(void* q, void* k, int B, int Hq, int Hkv, int T, int d_head,
  *   pos       cache.pos: tokens already in the cache (0 <= pos, pos + Tn <= Tmax,
  *             else ERR_OFFSET).
  *   rope_base, pairing   as rope_apply_ex.
- *   scale, dtype, stream, workspace, ws_bytes, lse   as attn_fwd_ws;
- *             attn_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d_head, dtype) bytes
- *             suffice for every pos.
+ *   scale, dtype, stream, lse   as attn_fwd_ws.
+ *   workspace, ws_bytes  device buffer of at least
+ *             attn_decode_step_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d_head,
+ *             dtype) bytes (enough for every pos; ERR_WORKSPACE when
+ *             smaller).  For the one-launch step (bf16, Tn == 1) its last
+ *             4 * B * Hkv bytes are arrival counters that MUST be zero before
+ *             the first call with this workspace (clear them once after
+ *             allocating, e.g. hipMemset); every call leaves them zero, so
+ *             later steps need no clearing.  Calls that share a workspace
+ *             must be ordered on one stream, and the buffer must not be
+ *             handed to other entry points in between (they would overwrite
+ *             the counters).  Other steps use it as attn_fwd_ws does.
  * No written buffer (q, the caches, o, lse, workspace) may overlap another
  * buffer (ERR_SHAPE).  Head sizes as attn_fwd; the rotation needs an even
  * d_head.  Returns a rocattn_status.
  */
+/*
+ * attn_decode_step_workspace_bytes -- bytes of workspace attn_decode_step
+ * needs for these sizes and every pos with pos + Tn <= Tmax (see above);
+ * 0 for arguments it would reject.
+ */
+size_t attn_decode_step_workspace_bytes(int B, int Hq, int Hkv, int Tn, int Tmax, int d_head, int dtype);
+
 int attn_decode_step(void* q, const void* k_new, const void* v_new, void* k_cache,
                      void* v_cache, void* o, int B, int Hq, int Hkv, int Tn, int Tmax, int pos,
                      int d_head, float scale, double rope_base, int pairing, int dtype,

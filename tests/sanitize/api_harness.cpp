@@ -101,6 +101,20 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t) {
     EXPECT(p.workspace != nullptr);
     return hipSuccess;
 }
+size_t decode_step_counter_offset(int B, int Hq, int Hkv, int Tmax, int d) {
+    return (decode_workspace_bytes(B, Hq, Hkv, Tmax, d) + 255) & ~(size_t)255;
+}
+size_t decode_step_workspace_bytes(int B, int Hq, int Hkv, int Tmax, int d) {
+    return decode_step_counter_offset(B, Hq, Hkv, Tmax, d) + sizeof(unsigned) * (size_t)B * Hkv;
+}
+hipError_t launch_decode_step_bf16(const StepParams& sp, void* ws, size_t ws_bytes, hipStream_t) {
+    ++launches;
+    EXPECT(sp.q && sp.kn && sp.vn && sp.kc && sp.vc && sp.o && ws);
+    EXPECT(sp.pos >= 0 && sp.pos < sp.Tmax && sp.B > 0 && sp.Hq % sp.Hkv == 0);
+    EXPECT(ws_bytes >= decode_step_workspace_bytes(sp.B, sp.Hq, sp.Hkv, sp.Tmax, sp.d));
+    EXPECT(sp.pairing == 0 || sp.pairing == 1);
+    return hipSuccess;
+}
 hipError_t noalloc_scratch(void** ptr) {
     *ptr = reinterpret_cast<void*>(0x7100000000ull);
     return hipSuccess;
@@ -213,8 +227,11 @@ int main() {
            ROCATTN_ERR_HEADDIM);
 
     // cached generation step
-    const size_t sw = attn_workspace_bytes(32, 32, 8, 1, 8192, 128, BF);
+    const size_t sw = attn_decode_step_workspace_bytes(32, 32, 8, 1, 8192, 128, BF);
+    EXPECT(sw > attn_workspace_bytes(32, 32, 8, 1, 8192, 128, BF));   // the partials plus the counters
     void *kn = A(7), *vn = A(8), *kc = A(9), *vc = A(10);
+    EXPECT(attn_decode_step(q, kn, vn, kc, vc, o, 32, 32, 8, 1, 8192, 8191, 128, 0.088f, 10000.0, 0, BF, nullptr,
+                            ws, sw - 1, nullptr) == ROCATTN_ERR_WORKSPACE);
     EXPECT(attn_decode_step(q, kn, vn, kc, vc, o, 32, 32, 8, 1, 8192, 8191, 128, 0.088f, 10000.0, 0, BF, nullptr,
                             ws, sw, nullptr) == ROCATTN_OK);
     EXPECT(attn_decode_step(q, kn, vn, kc, vc, o, 32, 32, 8, 1, 8192, 8192, 128, 0.088f, 10000.0, 0, BF, nullptr,

@@ -84,8 +84,7 @@ def test_graph_attn_decode_step():
     vn = torch.randn(B, Hkv, Tn, d, generator=g).to(torch.bfloat16).to(DEV)
     kc = torch.randn(B, Hkv, Tmax, d, generator=g).to(torch.bfloat16).to(DEV)
     vc = torch.randn(B, Hkv, Tmax, d, generator=g).to(torch.bfloat16).to(DEV)
-    nb = ra.attn_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d, torch.bfloat16)
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=DEV)
+    ws = ra.decode_step_workspace(q, kc)   # zeroed once; every step leaves its counters zero
     o = torch.empty_like(q)
     replay_matches_eager(
         lambda: ra.attn_decode_step(q, kn, vn, kc, vc, pos, o=o, scale=d ** -0.5, workspace=ws),

@@ -688,6 +688,52 @@ def test_decode_step_equals_unfused_calls_bit_exact(Tn, pos):
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Tmax,pos,d,pairing,scale", [
+    (32, 32, 8, 8192, 8191, 128, "split", 0.0884),      # the decode workload's step
+    (3, 12, 1, 700, 0, 64, "adjacent", 0.125),          # first token, 12 query heads per K/V head
+    (2, 16, 1, 3000, 2500, 128, "split", -0.0884),      # 16 per K/V head, negative scale
+    (4, 8, 4, 1024, 1023, 64, "split", 0.125),          # 2 per K/V head
+    (1, 6, 2, 20000, 19999, 128, "adjacent", 0.0884),   # long cache, few heads: many chunks
+    (2, 4, 4, 100, 37, 128, "split", 0.0884),           # one query head per K/V head, short cache
+])
+def test_one_launch_decode_step(B, Hq, Hkv, Tmax, pos, d, pairing, scale):
+    """A one-token attn_decode_step is one launch: the same bits (o, lse, the
+    rotated q, both caches) as rope_apply on q and the new key, the cache
+    writes and attn_fwd_ws over the cache prefix; its arrival counters are
+    back at zero afterwards; o is within the contract of the oracle's
+    composition."""
+    say("one-launch step", B, Hq, Hkv, Tmax, pos, d, pairing, scale)
+    q = _rand((B, Hq, 1, d), torch.bfloat16, 121).cuda()
+    kn = _rand((B, Hkv, 1, d), torch.bfloat16, 122).cuda()
+    vn = _rand((B, Hkv, 1, d), torch.bfloat16, 123).cuda()
+    kc = _rand((B, Hkv, Tmax, d), torch.bfloat16, 124).cuda()
+    vc = _rand((B, Hkv, Tmax, d), torch.bfloat16, 125).cuda()
+    q0, kc0, vc0 = q.clone(), kc.clone(), vc.clone()
+    ws = ra.decode_step_workspace(q, kc)
+    lse1 = torch.empty(B, Hq, 1, dtype=torch.float32, device=DEV)
+    o1 = ra.attn_decode_step(q, kn, vn, kc, vc, pos, scale=scale, pairing=pairing, workspace=ws, lse=lse1)
+    # the same step as separate calls
+    q2, k2 = q0.clone(), kn.clone()
+    ra.rope_apply(q2, None, pos0=pos, pairing=pairing)
+    ra.rope_apply(k2, None, pos0=pos, pairing=pairing)
+    kc2, vc2 = kc0.clone(), vc0.clone()
+    kc2[:, :, pos:pos + 1] = k2
+    vc2[:, :, pos:pos + 1] = vn
+    nb = ra.attn_workspace_bytes(B, Hq, Hkv, 1, pos + 1, d, torch.bfloat16)
+    ws2 = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    o2 = torch.empty_like(q2)
+    lse2 = torch.empty_like(lse1)
+    ra.attn_fwd_ws(q2, kc2[:, :, :pos + 1], vc2[:, :, :pos + 1], o2, ws2, lse2, scale=scale, q_offset=pos)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(kc, kc2) and torch.equal(vc, vc2)
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
+    assert int(ws[-4 * B * Hkv:].count_nonzero()) == 0   # counters left at zero
+    want = oracle.decode_step(q0.cpu(), kn.cpu(), vn.cpu(), kc0.cpu(), vc0.cpu(), pos, scale, pairing=pairing)[0]
+    err = float(np.max(np.abs(f64(o1) - want)))
+    say("max abs err", err)
+    assert err <= TOL[torch.bfloat16], err
+
+
 def test_decode_steps_replay_the_prefill():
     """The pages' KV-cache check ("The Transformer architecture" -- Hands-on):
     a sequence fed one token at a time (then a chunk) through the cached step
@@ -702,8 +748,7 @@ def test_decode_steps_replay_the_prefill():
     full = ra.attn_fwd(qf, kf, v, scale=0.0884)
     kc = torch.zeros(B, Hkv, Tmax, d, dtype=torch.bfloat16, device=DEV)
     vc = torch.zeros_like(kc)
-    nb = ra.attn_workspace_bytes(B, Hq, Hkv, 1, Tmax, d, torch.bfloat16)
-    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    ws = ra.decode_step_workspace(q[:, :, :1], kc)   # zeroed once, reused by every one-token step
     outs = []
     for c0, c1 in [(t, t + 1) for t in range(200)] + [(200, 300)]:
         qs = q[:, :, c0:c1].contiguous()

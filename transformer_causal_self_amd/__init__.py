@@ -41,7 +41,7 @@ LIBRARY = os.path.join(HERE, "librocattn.so")
 # the C ABI, as declared in include/rocattn.h
 SYMBOLS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_noalloc", "attn_fwd_strided", "attn_workspace_bytes",
            "rope_apply", "rope_apply_ex", "rope_apply_pos", "attn_decode_step", "attn_fwd_dv", "attn_fwd_rope",
-           "attn_fwd_rope_workspace_bytes", "attn_bwd",
+           "attn_fwd_rope_workspace_bytes", "attn_bwd", "attn_decode_step_workspace_bytes",
            "attn_bwd_workspace_bytes", "attn_status_string")
 
 F32, BF16 = 0, 1
@@ -90,6 +90,8 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_step.restype = i
         lib.attn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
                                          ctypes.c_double, i, i, vp, vp, sz, vp]
+        lib.attn_decode_step_workspace_bytes.restype = sz
+        lib.attn_decode_step_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.rope_apply_pos.restype = i
         lib.rope_apply_pos.argtypes = [vp, vp, i, i, i, i, i, vp, ctypes.c_double, i, vp, i]
         lib.attn_fwd_dv.restype = i
@@ -407,18 +409,36 @@ def attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o=None, scale=None,
     """One cached step: rotate q in place and k_new into k_cache at tokens
     pos.., copy v_new into v_cache there, then attend over cache tokens
     0 .. pos + Tn - 1 (causal, q_offset = pos); returns o.  A workspace of
-    attn_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d, dtype) bytes is needed when
-    that is non-zero (it is allocated here when not given)."""
+    attn_decode_step_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d, dtype) bytes is
+    needed when that is non-zero; a caller's workspace must start zeroed
+    (decode_step_workspace() makes one) and is left reusable.  One is
+    allocated (zeroed) here when not given."""
     import torch
     if o is None:
         o = torch.empty_like(q)
     if workspace is None:
-        nb = attn_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
-                                  k_cache.shape[2], q.shape[3], q.dtype)
-        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+        workspace = decode_step_workspace(q, k_cache)
     _decode_step_call(q, k_new, v_new, k_cache, v_cache, pos, o, scale, base, pairing,
                       workspace, lse, stream)()
     return o
+
+
+def attn_decode_step_workspace_bytes(B, Hq, Hkv, Tn, Tmax, d_head, dtype) -> int:
+    if not isinstance(dtype, int):
+        import torch
+        dtype = F32 if dtype == torch.float32 else BF16
+    return int(library().attn_decode_step_workspace_bytes(int(B), int(Hq), int(Hkv), int(Tn), int(Tmax),
+                                                          int(d_head), dtype))
+
+
+def decode_step_workspace(q, k_cache):
+    """A zeroed workspace for attn_decode_step on tensors shaped like q
+    ([B, Hq, Tn, d]) and k_cache ([B, Hkv, Tmax, d]), or None when none is
+    needed.  It can serve every later step of the same sizes."""
+    import torch
+    nb = attn_decode_step_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
+                                          k_cache.shape[2], q.shape[3], q.dtype)
+    return torch.zeros(nb, dtype=torch.uint8, device=q.device) if nb else None
 
 
 def bind_attn_decode_step(q, k_new, v_new, k_cache, v_cache, pos, o, scale=None,

@@ -448,8 +448,14 @@ ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, 
             if (overlaps(lse, lb, bufs[i], lens[i])) return ROCATTN_ERR_SHAPE;
     }
     const int Tk = pos + Tn;
-    const size_t wsb = workspace_use(workspace_required(B, Hq, Hkv, Tn, Tk, d_head, dtype),
-                                     workspace_for(B, Hq, Hkv, Tn, Tk, d_head, dtype), workspace, ws_bytes);
+    // one new token per sequence (bf16): the whole step is one launch whose
+    // workspace also holds the arrival counters of its chunk merge
+    const bool fused = uses_decode(dtype, Tn, Hq, Hkv, d_head);
+    const size_t wsb = fused ? ((workspace && ws_bytes >= rocattn::decode_step_workspace_bytes(B, Hq, Hkv, Tmax, d_head))
+                                    ? rocattn::decode_step_workspace_bytes(B, Hq, Hkv, Tmax, d_head)
+                                    : SIZE_MAX)
+                             : workspace_use(workspace_required(B, Hq, Hkv, Tn, Tk, d_head, dtype),
+                                             workspace_for(B, Hq, Hkv, Tn, Tk, d_head, dtype), workspace, ws_bytes);
     if (wsb == SIZE_MAX) return ROCATTN_ERR_WORKSPACE;
     if (wsb > 0) {
         if (!aligned16(workspace)) return ROCATTN_ERR_ALIGN;
@@ -459,6 +465,15 @@ ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, 
             return ROCATTN_ERR_SHAPE;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fused) {
+        rocattn::StepParams sp;
+        sp.q = q; sp.kn = k_new; sp.vn = v_new; sp.kc = k_cache; sp.vc = v_cache; sp.o = o; sp.lse = lse;
+        sp.B = B; sp.Hq = Hq; sp.Hkv = Hkv; sp.Tmax = Tmax; sp.pos = pos; sp.d = d_head;
+        sp.scale = scale;
+        sp.base = rope_base;
+        sp.pairing = pairing;
+        return rocattn::launch_decode_step_bf16(sp, workspace, wsb, s) == hipSuccess ? ROCATTN_OK : ROCATTN_ERR_HIP;
+    }
     if (rocattn::launch_step_prep(q, k_new, v_new, k_cache, v_cache, B, Hq, Hkv, Tn, Tmax, d_head,
                                   pos, rope_base, dtype, pairing, s) != hipSuccess)
         return ROCATTN_ERR_HIP;
@@ -467,6 +482,15 @@ ROCATTN_API int attn_decode_step(void* q, const void* k_new, const void* v_new, 
     p.ks = {(long long)Hkv * Tmax * d_head, (long long)Tmax * d_head, d_head};
     p.vs = p.ks;
     return launch(p, dtype, s, wsb ? workspace : nullptr, wsb);
+}
+
+ROCATTN_API size_t attn_decode_step_workspace_bytes(int B, int Hq, int Hkv, int Tn, int Tmax, int d_head,
+                                                   int dtype) {
+    if (dtype != ROCATTN_F32 && dtype != ROCATTN_BF16) return 0;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tn <= 0 || Tmax <= 0 || d_head <= 0 || Hq % Hkv != 0) return 0;
+    if (dtype == ROCATTN_BF16 && d_head != 64 && d_head != 128) return 0;
+    if (uses_decode(dtype, Tn, Hq, Hkv, d_head)) return rocattn::decode_step_workspace_bytes(B, Hq, Hkv, Tmax, d_head);
+    return workspace_for(B, Hq, Hkv, Tn, Tmax, d_head, dtype);
 }
 
 ROCATTN_API int attn_fwd_dv(const void* q, const void* k, const void* v, void* o, int B, int Hq,

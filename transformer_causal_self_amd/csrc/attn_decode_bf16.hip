@@ -30,6 +30,7 @@
 #include <atomic>
 
 #include "internal.hpp"
+#include "rope_math.hpp"
 
 namespace rocattn {
 namespace {
@@ -51,7 +52,92 @@ struct DecArgs {
     float c;         // |scale| * log2(e)
     unsigned neg;    // sign flip for q when scale < 0
     Strides qs, ks, vs;   // element strides (batch, head, token)
+    // the cached generation step in one launch (STEP): q is rotated at pos
+    // on load and written back rotated by the last workgroup of each
+    // (batch, K/V head); the chunk holding pos rotates the new key, appends
+    // it and the new value to the caches and uses them; the last workgroup
+    // to arrive (counted in cnt, zero between calls) merges the chunks
+    bf16* q_rot;
+    const bf16* kn;       // new keys [B][Hkv][D]
+    const bf16* vn;       // new values [B][Hkv][D]
+    int pos;              // position of the new token (kv_len - 1)
+    double rneg;          // -log2(base) / (D / 2)
+    int adj;              // RoPE pairing: 0 split-half, 1 adjacent
+    unsigned* cnt;        // arrival counters [B * Hkv]
+    bf16* o;
+    float* lse;
+    Strides os;
 };
+
+// LDS floats a STEP workgroup needs beyond the split kernel's: the (cos,
+// sin) of the D/2 pairs, the rotated new key row, the last-arrival flag.
+template <int D>
+constexpr int step_lds_extra() { return D + D / 2 + 4; }
+constexpr int kStepLdsReserve = 128 + 64 + 4;   // step_lds_extra<128>()
+
+// Merge of the S partial results of one output element: M = max_s m_s, then
+// sum_s 2^(m_s - M) o_s and sum_s 2^(m_s - M) l_s, in batches of 8 chunks
+// (one memory round trip per batch, not per chunk).
+__device__ inline void merge_partials(const float* mlr, const float* op, int S, int D, float& M, float& den,
+                                      float& acc) {
+    M = -INFINITY;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        float mv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mv[u] = s0 + u < S ? mlr[2 * (s0 + u)] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
+    }
+    den = 0.f;
+    acc = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        float mv[8], lv[8], ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool ok = s0 + u < S;
+            mv[u] = ok ? mlr[2 * (s0 + u)] : -INFINITY;
+            lv[u] = ok ? mlr[2 * (s0 + u) + 1] : 0.f;
+            ov[u] = ok ? op[(size_t)(s0 + u) * D] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float w = exp2f(mv[u] - M);
+            den = fmaf(w, lv[u], den);
+            acc = fmaf(w, ov[u], acc);
+        }
+    }
+}
+
+// RoPE of a lane's query fragments at one position (the STEP kernel's q
+// load): fragment m holds channels 32 m + 8 quarter .. + 7.  Split-half pair
+// p = (p, p + D/2) joins fragment m with fragment m + NM/2; adjacent pair
+// p = (2p, 2p + 1) lies inside a fragment.  The turn is the RoPE pass's
+// (float32, rounded once to bf16).
+template <int NM>
+__device__ inline void rope_q_lane(bf16x8 (&q)[NM], const float2* tab, int adj, int quarter) {
+    float y1, y2;
+    if (!adj) {
+#pragma unroll
+        for (int m = 0; m < NM / 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float2 t = tab[32 * m + 8 * quarter + e];
+                rope_turn((float)q[m][e], (float)q[m + NM / 2][e], t.x, t.y, y1, y2);
+                q[m][e] = (bf16)y1;
+                q[m + NM / 2][e] = (bf16)y2;
+            }
+    } else {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float2 t = tab[16 * m + 4 * quarter + e];
+                rope_turn((float)q[m][2 * e], (float)q[m][2 * e + 1], t.x, t.y, y1, y2);
+                q[m][2 * e] = (bf16)y1;
+                q[m][2 * e + 1] = (bf16)y2;
+            }
+    }
+}
 
 struct CombArgs {
     const float* o_part;
@@ -64,12 +150,16 @@ struct CombArgs {
     Strides os;
 };
 
-template <int D, int RP>  // RP: query heads per K/V head, padded to 4, 8 or 16
+template <int D, int RP, bool STEP = false>  // RP: query heads per K/V head, padded to 4, 8 or 16
 __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     extern __shared__ float dsm[];
     float* St = dsm;                  // [RP][C] scores (base-2 units)
     float* Pl = dsm + RP * a.C;       // [C][RP] weights
     float* Red = Pl + RP * a.C;       // [4][RP][D] per-wave partial outputs
+    float2* tab = reinterpret_cast<float2*>(Red + 4 * RP * D);   // STEP: (cos, sin) of the pairs at pos
+    bf16* knew = reinterpret_cast<bf16*>(tab + D / 2);            // STEP: the new key row, rotated
+    int* last_flag = reinterpret_cast<int*>(knew + D);           // STEP: this workgroup arrived last
+    (void)tab; (void)knew; (void)last_flag;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int s = blockIdx.x % a.S;
@@ -85,6 +175,39 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     //      contiguous bytes per instruction.
     constexpr int NM = D / 32;
     const int rho = lane & 15, quarter = lane >> 4;
+
+    if constexpr (STEP) {
+        // the float32 (cos, sin) of every pair at position pos, formed as
+        // the RoPE pass forms them; the chunk holding pos turns the new key
+        // (kept in LDS for its scores, appended to the key cache) and
+        // appends the new value
+        if (tid < D / 2) {
+            const double inv_freq = exp2((double)tid * a.rneg);
+            double sn, cs;
+            rope_sincos((double)a.pos * inv_freq, sn, cs);
+            tab[tid] = make_float2((float)cs, (float)sn);
+        }
+        __syncthreads();
+        if (s == a.S - 1) {
+            if (tid < D / 2) {
+                const int c1 = a.adj ? 2 * tid : tid, c2 = a.adj ? 2 * tid + 1 : tid + D / 2;
+                const bf16* kr = a.kn + (size_t)g * D;
+                float y1, y2;
+                rope_turn((float)kr[c1], (float)kr[c2], tab[tid].x, tab[tid].y, y1, y2);
+                knew[c1] = (bf16)y1;
+                knew[c2] = (bf16)y2;
+                bf16* kc = const_cast<bf16*>(a.k) + b * a.ks.b + hk * a.ks.h + (long long)a.pos * a.ks.t;
+                kc[c1] = (bf16)y1;
+                kc[c2] = (bf16)y2;
+            } else if (tid < D / 2 + D / 8) {
+                const int c = 8 * (tid - D / 2);
+                bf16* vc = const_cast<bf16*>(a.v) + b * a.vs.b + hk * a.vs.h + (long long)a.pos * a.vs.t;
+                *reinterpret_cast<uint4*>(vc + c) = *reinterpret_cast<const uint4*>(a.vn + (size_t)g * D + c);
+            }
+            __syncthreads();
+        }
+    }
+
     bf16x8 qa[NM];
     {
         const bool ok = rho < a.R;
@@ -94,6 +217,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
         for (int m = 0; m < NM; ++m) {
             uint4 u = src[4 * m];
             if (!ok) u = make_uint4(0, 0, 0, 0);
+            qa[m] = __builtin_bit_cast(bf16x8, u);
+        }
+        if constexpr (STEP) rope_q_lane(qa, tab, a.adj, quarter);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            uint4 u = __builtin_bit_cast(uint4, qa[m]);
             u.x ^= a.neg; u.y ^= a.neg; u.z ^= a.neg; u.w ^= a.neg;
             qa[m] = __builtin_bit_cast(bf16x8, u);
         }
@@ -106,12 +235,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     for (int gi = wave; gi < ngroups; gi += 4) {
         const int kl = gi * 16 + rho;            // key (local) whose row this lane loads
         const bool kvalid = kl < nkeys;
+        // STEP: the new key (position pos) comes from LDS, not the cache
+        const bool knw = STEP && kvalid && j_begin + kl == a.pos;
         const uint4* kp = reinterpret_cast<const uint4*>(
-            kbase + (j_begin + (kvalid ? kl : 0)) * a.ks.t);
+            kbase + (j_begin + (kvalid && !knw ? kl : 0)) * a.ks.t);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, kp[4 * m]);
+            bf16x8 kf = __builtin_bit_cast(bf16x8, kp[4 * m]);
+            if constexpr (STEP)
+                if (knw) kf = *reinterpret_cast<const bf16x8*>(knew + 32 * m + 8 * quarter);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], kf, acc, 0, 0, 0);
         }
         // acc[r] = score of query head 4*quarter + r against key gi*16 + rho
@@ -158,7 +291,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     const bf16* vbase = a.v + b * a.vs.b + hk * a.vs.h + j_begin * a.vs.t + col;
 #pragma unroll 8
     for (int j = wave * KPW + kk; j < nkeys; j += 4 * KPW) {
-        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vbase + j * a.vs.t);
+        const bf16* vrow = vbase + j * a.vs.t;
+        if constexpr (STEP)   // the new value (position pos) from the new row
+            if (j_begin + j == a.pos) vrow = a.vn + (size_t)g * D + col;
+        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vrow);
         float vf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vf[e] = (float)vv[e];
@@ -195,41 +331,46 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
                           Red[(2 * RP + r) * D + dd] + Red[(3 * RP + r) * D + dd];
         a.o_part[((size_t)(b * a.Hq + hq0 + r) * a.S + s) * D + dd] = sum;
     }
+
+    if constexpr (STEP) {
+        // Publish this chunk's partials, count its arrival; the last of the
+        // S chunks of (b, hk) merges all of them (every other chunk has
+        // written its partials and read q by then), writes q back rotated
+        // and leaves the counter at zero for the next call.
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) *last_flag = atomicAdd(a.cnt + g, 1u) == (unsigned)(a.S - 1) ? 1 : 0;
+        __syncthreads();
+        if (*last_flag) {
+            __threadfence();
+            for (int idx = tid; idx < a.R * D; idx += 256) {
+                const int r = idx / D, col2 = idx - r * D;
+                const size_t row = (size_t)(b * a.Hq + hq0 + r);
+                float M, den, acc2;
+                merge_partials(a.ml + row * a.S * 2, a.o_part + row * a.S * D + col2, a.S, D, M, den, acc2);
+                a.o[b * a.os.b + (hq0 + r) * a.os.h + col2] = (bf16)(acc2 / den);
+                if (a.lse && col2 == 0) a.lse[row] = (M + log2f(den)) * kLn2;
+            }
+            for (int idx = tid; idx < a.R * (D / 2); idx += 256) {
+                const int r = idx / (D / 2), p = idx - r * (D / 2);
+                const int c1 = a.adj ? 2 * p : p, c2 = a.adj ? 2 * p + 1 : p + D / 2;
+                bf16* qr = a.q_rot + b * a.qs.b + (hq0 + r) * a.qs.h;
+                float y1, y2;
+                rope_turn((float)qr[c1], (float)qr[c2], tab[p].x, tab[p].y, y1, y2);
+                qr[c1] = (bf16)y1;
+                qr[c2] = (bf16)y2;
+            }
+            if (tid == 0) a.cnt[g] = 0u;
+        }
+    }
 }
 
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(CombArgs a) {
     const size_t row = blockIdx.x;             // (b * Hq + hq) * Tq + i
     const int col = threadIdx.x;
-    const float* mlr = a.ml + row * a.S * 2;
-    const float* op = a.o_part + row * a.S * D + col;
-    // the chunks' maxima, sums and partial outputs, loaded together in
-    // batches of 8 (one memory round trip per batch, not per chunk)
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < a.S; s0 += 8) {
-        float mv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) mv[u] = s0 + u < a.S ? mlr[2 * (s0 + u)] : -INFINITY;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
-    }
-    float den = 0.f, acc = 0.f;
-    for (int s0 = 0; s0 < a.S; s0 += 8) {
-        float mv[8], lv[8], ov[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool ok = s0 + u < a.S;
-            mv[u] = ok ? mlr[2 * (s0 + u)] : -INFINITY;
-            lv[u] = ok ? mlr[2 * (s0 + u) + 1] : 0.f;
-            ov[u] = ok ? op[(size_t)(s0 + u) * D] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float w = exp2f(mv[u] - M);
-            den = fmaf(w, lv[u], den);
-            acc = fmaf(w, ov[u], acc);
-        }
-    }
+    float M, den, acc;
+    merge_partials(a.ml + row * a.S * 2, a.o_part + row * a.S * D + col, a.S, D, M, den, acc);
     const size_t bh = row / a.Tq;
     const int i = (int)(row - bh * a.Tq);
     const int b = (int)(bh / a.Hq), hq = (int)(bh - (size_t)b * a.Hq);
@@ -288,7 +429,7 @@ int pad_r(int R) { return R <= 4 ? 4 : (R <= 8 ? 8 : 16); }
 // longest chunk whose scores, weights and partial outputs fit the LDS cap
 int chunk_max(int R, int D) {
     const int rp = pad_r(R);
-    return ((kLdsFloats - 4 * rp * D) / (2 * rp)) & ~63;
+    return ((kLdsFloats - 4 * rp * D - kStepLdsReserve) / (2 * rp)) & ~63;
 }
 
 int split_target(int G) {
@@ -362,10 +503,10 @@ void plan(int G, int R, int D, int kv_len, int* C_out, int* S_out) {
     *S_out = best_S;
 }
 
-template <int D, int RP>
+template <int D, int RP, bool STEP = false>
 hipError_t launch_split(const DecArgs& a, int grid, hipStream_t stream) {
-    const size_t lds = sizeof(float) * ((size_t)2 * RP * a.C + (size_t)4 * RP * D);
-    hipLaunchKernelGGL((decode_split_kernel<D, RP>), dim3(grid), dim3(256), lds, stream, a);
+    const size_t lds = sizeof(float) * ((size_t)2 * RP * a.C + (size_t)4 * RP * D + (STEP ? step_lds_extra<D>() : 0));
+    hipLaunchKernelGGL((decode_split_kernel<D, RP, STEP>), dim3(grid), dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -444,6 +585,57 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Tk, int d) {
     int S = (Tk + c_max - 1) / c_max;
     if (S < s_target) S = s_target;
     return sizeof(float) * (size_t)B * Hq * S * (d + 2);
+}
+
+size_t decode_step_counter_offset(int B, int Hq, int Hkv, int Tmax, int d) {
+    return (decode_workspace_bytes(B, Hq, Hkv, Tmax, d) + 255) & ~(size_t)255;
+}
+
+size_t decode_step_workspace_bytes(int B, int Hq, int Hkv, int Tmax, int d) {
+    return decode_step_counter_offset(B, Hq, Hkv, Tmax, d) + sizeof(unsigned) * (size_t)B * Hkv;
+}
+
+hipError_t launch_decode_step_bf16(const StepParams& sp, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    const int D = sp.d, R = sp.Hq / sp.Hkv, G = sp.B * sp.Hkv;
+    const int kv_len = sp.pos + 1;
+    int C, S;
+    plan(G, R, D, kv_len, &C, &S);
+    const size_t cnt_off = decode_step_counter_offset(sp.B, sp.Hq, sp.Hkv, sp.Tmax, D);
+    if (ws_bytes < cnt_off + sizeof(unsigned) * (size_t)G) return hipErrorInvalidValue;
+    DecArgs a;
+    a.q = static_cast<const bf16*>(sp.q);
+    a.k = static_cast<const bf16*>(sp.kc);
+    a.v = static_cast<const bf16*>(sp.vc);
+    a.o_part = static_cast<float*>(workspace);
+    a.ml = a.o_part + (size_t)sp.B * sp.Hq * S * D;
+    a.Hq = sp.Hq; a.Hkv = sp.Hkv; a.Tk = kv_len;
+    a.R = R;
+    a.kv_len = kv_len;
+    a.C = C; a.S = S;
+    a.c = fabsf(sp.scale) * kLog2e;
+    a.neg = sp.scale < 0.f ? 0x80008000u : 0u;
+    a.qs = {(long long)sp.Hq * D, (long long)D, D};
+    a.ks = {(long long)sp.Hkv * sp.Tmax * D, (long long)sp.Tmax * D, D};
+    a.vs = a.ks;
+    a.q_rot = static_cast<bf16*>(sp.q);
+    a.kn = static_cast<const bf16*>(sp.kn);
+    a.vn = static_cast<const bf16*>(sp.vn);
+    a.pos = sp.pos;
+    a.rneg = -log2(sp.base) / (double)(D / 2);
+    a.adj = sp.pairing;
+    a.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + cnt_off);
+    a.o = static_cast<bf16*>(sp.o);
+    a.lse = sp.lse;
+    a.os = a.qs;
+    const int grid = G * S;
+    const int rp = pad_r(R);
+    if (D == 64)
+        return rp == 4 ? launch_split<64, 4, true>(a, grid, stream)
+             : rp == 8 ? launch_split<64, 8, true>(a, grid, stream)
+                       : launch_split<64, 16, true>(a, grid, stream);
+    return rp == 4 ? launch_split<128, 4, true>(a, grid, stream)
+         : rp == 8 ? launch_split<128, 8, true>(a, grid, stream)
+                   : launch_split<128, 16, true>(a, grid, stream);
 }
 
 hipError_t launch_decode_bf16(const FwdParams& p, void* workspace, size_t ws_bytes,

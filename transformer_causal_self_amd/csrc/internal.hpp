@@ -71,6 +71,31 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Tk, int d);
 hipError_t launch_decode_bf16(const FwdParams& p, void* workspace, size_t ws_bytes,
                               hipStream_t stream);
 
+// One cached generation step of one new token per sequence (bf16, d 64 or
+// 128, Hq / Hkv <= 16) in a single launch: q [B][Hq][1][d] rotated at pos
+// (written back rotated), the new key kn [B][Hkv][1][d] rotated and, with
+// the new value vn, appended to the caches kc / vc [B][Hkv][Tmax][d] at
+// pos, attention over cache tokens 0 .. pos into o [B][Hq][1][d] (and lse).
+// The workspace holds the split-K partials and, at
+// decode_step_counter_offset, B * Hkv arrival counters that must be zero
+// before the call and are zero after it.
+struct StepParams {
+    void* q;
+    const void* kn;
+    const void* vn;
+    void* kc;
+    void* vc;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, Tmax, pos, d;
+    float scale;
+    double base;
+    int pairing;
+};
+size_t decode_step_counter_offset(int B, int Hq, int Hkv, int Tmax, int d);
+size_t decode_step_workspace_bytes(int B, int Hq, int Hkv, int Tmax, int d);
+hipError_t launch_decode_step_bf16(const StepParams& sp, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 // Generic float32 kernel; d <= 256, d % 4 == 0.
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 
