@@ -69,22 +69,47 @@ struct DecArgs {
     Strides os;
 };
 
-// LDS floats a STEP workgroup needs beyond the split kernel's: the (cos,
-// sin) of the D/2 pairs, the rotated new key row, the last-arrival flag.
-template <int D>
-constexpr int step_lds_extra() { return D + D / 2 + 4; }
-constexpr int kStepLdsReserve = 128 + 64 + 4;   // step_lds_extra<128>()
 
 // Merge of the S partial results of one output element: M = max_s m_s, then
 // sum_s 2^(m_s - M) o_s and sum_s 2^(m_s - M) l_s, in batches of 8 chunks
 // (one memory round trip per batch, not per chunk).
+// COHERENT: read with device-scope atomic loads (partials other workgroups
+// wrote during this kernel, see the STEP merge).
+template <bool COHERENT = false>
+__device__ inline float ld_partial(const float* p) {
+    if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+template <bool COHERENT = false>
 __device__ inline void merge_partials(const float* mlr, const float* op, int S, int D, float& M, float& den,
                                       float& acc) {
+    if (S <= 8) {   // one batch: every value loaded at once (one memory round trip)
+        float mv[8], lv[8], ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool ok = u < S;
+            mv[u] = ok ? ld_partial<COHERENT>(mlr + 2 * u) : -INFINITY;
+            lv[u] = ok ? ld_partial<COHERENT>(mlr + 2 * u + 1) : 0.f;
+            ov[u] = ok ? ld_partial<COHERENT>(op + (size_t)u * D) : 0.f;
+        }
+        M = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
+        den = 0.f;
+        acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float w = exp2f(mv[u] - M);
+            den = fmaf(w, lv[u], den);
+            acc = fmaf(w, ov[u], acc);
+        }
+        return;
+    }
     M = -INFINITY;
     for (int s0 = 0; s0 < S; s0 += 8) {
         float mv[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) mv[u] = s0 + u < S ? mlr[2 * (s0 + u)] : -INFINITY;
+        for (int u = 0; u < 8; ++u) mv[u] = s0 + u < S ? ld_partial<COHERENT>(mlr + 2 * (s0 + u)) : -INFINITY;
 #pragma unroll
         for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
     }
@@ -95,9 +120,9 @@ __device__ inline void merge_partials(const float* mlr, const float* op, int S, 
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const bool ok = s0 + u < S;
-            mv[u] = ok ? mlr[2 * (s0 + u)] : -INFINITY;
-            lv[u] = ok ? mlr[2 * (s0 + u) + 1] : 0.f;
-            ov[u] = ok ? op[(size_t)(s0 + u) * D] : 0.f;
+            mv[u] = ok ? ld_partial<COHERENT>(mlr + 2 * (s0 + u)) : -INFINITY;
+            lv[u] = ok ? ld_partial<COHERENT>(mlr + 2 * (s0 + u) + 1) : 0.f;
+            ov[u] = ok ? ld_partial<COHERENT>(op + (size_t)(s0 + u) * D) : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -156,12 +181,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     float* St = dsm;                  // [RP][C] scores (base-2 units)
     float* Pl = dsm + RP * a.C;       // [C][RP] weights
     float* Red = Pl + RP * a.C;       // [4][RP][D] per-wave partial outputs
-    float2* tab = reinterpret_cast<float2*>(Red + 4 * RP * D);   // STEP: (cos, sin) of the pairs at pos
-    bf16* knew = reinterpret_cast<bf16*>(tab + D / 2);            // STEP: the new key row, rotated
-    int* last_flag = reinterpret_cast<int*>(knew + D);           // STEP: this workgroup arrived last
-    (void)tab; (void)knew; (void)last_flag;
+    // STEP: the (cos, sin) of the pairs at pos, in the per-wave partial
+    // region (free before phase 3 ends and after its reduction), and the
+    // last-arrival flag in the score region (free after phase 2).  The
+    // split kernel's LDS size is kept: a larger one fits fewer workgroups
+    // on a CU, which costs this bandwidth-bound kernel more than it saves.
+    float2* tab = reinterpret_cast<float2*>(Red);
+    int* last_flag = reinterpret_cast<int*>(St);
+    (void)tab; (void)last_flag;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto form_angles = [&]() {   // (cos, sin) of pair tid at pos, as the RoPE pass forms them
+        if (tid < D / 2) {
+            const double inv_freq = exp2((double)tid * a.rneg);
+            double sn, cs;
+            rope_sincos((double)a.pos * inv_freq, sn, cs);
+            tab[tid] = make_float2((float)cs, (float)sn);
+        }
+    };
+    (void)form_angles;
     const int s = blockIdx.x % a.S;
     const int g = blockIdx.x / a.S;                  // b * Hkv + hk
     const int b = g / a.Hkv, hk = g - (g / a.Hkv) * a.Hkv;
@@ -179,14 +217,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     if constexpr (STEP) {
         // the float32 (cos, sin) of every pair at position pos, formed as
         // the RoPE pass forms them; the chunk holding pos turns the new key
-        // (kept in LDS for its scores, appended to the key cache) and
-        // appends the new value
-        if (tid < D / 2) {
-            const double inv_freq = exp2((double)tid * a.rneg);
-            double sn, cs;
-            rope_sincos((double)a.pos * inv_freq, sn, cs);
-            tab[tid] = make_float2((float)cs, (float)sn);
-        }
+        // and appends it and the new value to the caches before it reads
+        // them (its own stores, completed before the barrier; no other
+        // workgroup reads that row)
+        form_angles();
         __syncthreads();
         if (s == a.S - 1) {
             if (tid < D / 2) {
@@ -194,8 +228,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
                 const bf16* kr = a.kn + (size_t)g * D;
                 float y1, y2;
                 rope_turn((float)kr[c1], (float)kr[c2], tab[tid].x, tab[tid].y, y1, y2);
-                knew[c1] = (bf16)y1;
-                knew[c2] = (bf16)y2;
                 bf16* kc = const_cast<bf16*>(a.k) + b * a.ks.b + hk * a.ks.h + (long long)a.pos * a.ks.t;
                 kc[c1] = (bf16)y1;
                 kc[c2] = (bf16)y2;
@@ -204,6 +236,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
                 bf16* vc = const_cast<bf16*>(a.v) + b * a.vs.b + hk * a.vs.h + (long long)a.pos * a.vs.t;
                 *reinterpret_cast<uint4*>(vc + c) = *reinterpret_cast<const uint4*>(a.vn + (size_t)g * D + c);
             }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
     }
@@ -230,21 +263,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
 
     // ---- phase 1: scores of 16 keys per MFMA group
     const int ngroups = (nkeys + 15) >> 4;
+
     const bf16* kbase = a.k + b * a.ks.b + hk * a.ks.h + 8 * quarter;
 #pragma unroll 4
     for (int gi = wave; gi < ngroups; gi += 4) {
         const int kl = gi * 16 + rho;            // key (local) whose row this lane loads
         const bool kvalid = kl < nkeys;
-        // STEP: the new key (position pos) comes from LDS, not the cache
-        const bool knw = STEP && kvalid && j_begin + kl == a.pos;
         const uint4* kp = reinterpret_cast<const uint4*>(
-            kbase + (j_begin + (kvalid && !knw ? kl : 0)) * a.ks.t);
+            kbase + (j_begin + (kvalid ? kl : 0)) * a.ks.t);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            bf16x8 kf = __builtin_bit_cast(bf16x8, kp[4 * m]);
-            if constexpr (STEP)
-                if (knw) kf = *reinterpret_cast<const bf16x8*>(knew + 32 * m + 8 * quarter);
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, kp[4 * m]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[m], kf, acc, 0, 0, 0);
         }
         // acc[r] = score of query head 4*quarter + r against key gi*16 + rho
@@ -273,8 +303,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
         for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
         if (lane == 0) {
             float* mlp = a.ml + ((size_t)(b * a.Hq + hq0 + row) * a.S + s) * 2;
-            mlp[0] = mx;
-            mlp[1] = sum;
+            if constexpr (STEP) {   // device-coherent: another workgroup merges them
+                __hip_atomic_store(mlp, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(mlp + 1, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                mlp[0] = mx;
+                mlp[1] = sum;
+            }
         }
     }
     __syncthreads();
@@ -291,10 +326,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     const bf16* vbase = a.v + b * a.vs.b + hk * a.vs.h + j_begin * a.vs.t + col;
 #pragma unroll 8
     for (int j = wave * KPW + kk; j < nkeys; j += 4 * KPW) {
-        const bf16* vrow = vbase + j * a.vs.t;
-        if constexpr (STEP)   // the new value (position pos) from the new row
-            if (j_begin + j == a.pos) vrow = a.vn + (size_t)g * D + col;
-        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vrow);
+        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vbase + j * a.vs.t);
         float vf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) vf[e] = (float)vv[e];
@@ -329,38 +361,69 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
         const int r = idx / D, dd = idx - r * D;
         const float sum = Red[(0 * RP + r) * D + dd] + Red[(1 * RP + r) * D + dd] +
                           Red[(2 * RP + r) * D + dd] + Red[(3 * RP + r) * D + dd];
-        a.o_part[((size_t)(b * a.Hq + hq0 + r) * a.S + s) * D + dd] = sum;
+        float* dst = a.o_part + ((size_t)(b * a.Hq + hq0 + r) * a.S + s) * D + dd;
+        if constexpr (STEP) __hip_atomic_store(dst, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *dst = sum;
     }
 
     if constexpr (STEP) {
-        // Publish this chunk's partials, count its arrival; the last of the
-        // S chunks of (b, hk) merges all of them (every other chunk has
-        // written its partials and read q by then), writes q back rotated
-        // and leaves the counter at zero for the next call.
-        __threadfence();
+        // Count this chunk's arrival once its partials are written (their
+        // device-scope stores complete before the count); the last of the S
+        // chunks of (b, hk) merges all of them with device-scope loads (every
+        // other chunk has written its partials and read q by then), writes
+        // q back rotated and leaves the counter at zero for the next call.
+        // Device-scope atomics on the partials instead of plain stores and a
+        // device-wide fence: the fence would write back the whole L2 of the
+        // XCD, once per workgroup.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0) *last_flag = atomicAdd(a.cnt + g, 1u) == (unsigned)(a.S - 1) ? 1 : 0;
+        if (tid == 0)
+            *last_flag = __hip_atomic_fetch_add(a.cnt + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                                 (unsigned)(a.S - 1)
+                             ? 1
+                             : 0;
         __syncthreads();
         if (*last_flag) {
-            __threadfence();
+            form_angles();   // the partial region is free again
+            // this thread's query pairs for the write-back, loaded before the
+            // merge so that the two memory round trips overlap
+            constexpr int QPT = (16 * (D / 2) + 255) / 256;   // pairs per thread, for up to 16 heads
+            float qx1[QPT], qx2[QPT];
+#pragma unroll
+            for (int u = 0; u < QPT; ++u) {
+                const int idx = tid + 256 * u;
+                qx1[u] = qx2[u] = 0.f;
+                if (idx < a.R * (D / 2)) {
+                    const int r = idx / (D / 2), p = idx - r * (D / 2);
+                    const int c1 = a.adj ? 2 * p : p, c2 = a.adj ? 2 * p + 1 : p + D / 2;
+                    const bf16* qr = a.q_rot + b * a.qs.b + (hq0 + r) * a.qs.h;
+                    qx1[u] = (float)qr[c1];
+                    qx2[u] = (float)qr[c2];
+                }
+            }
             for (int idx = tid; idx < a.R * D; idx += 256) {
                 const int r = idx / D, col2 = idx - r * D;
                 const size_t row = (size_t)(b * a.Hq + hq0 + r);
                 float M, den, acc2;
-                merge_partials(a.ml + row * a.S * 2, a.o_part + row * a.S * D + col2, a.S, D, M, den, acc2);
+                merge_partials<true>(a.ml + row * a.S * 2, a.o_part + row * a.S * D + col2, a.S, D, M, den, acc2);
                 a.o[b * a.os.b + (hq0 + r) * a.os.h + col2] = (bf16)(acc2 / den);
                 if (a.lse && col2 == 0) a.lse[row] = (M + log2f(den)) * kLn2;
             }
-            for (int idx = tid; idx < a.R * (D / 2); idx += 256) {
-                const int r = idx / (D / 2), p = idx - r * (D / 2);
-                const int c1 = a.adj ? 2 * p : p, c2 = a.adj ? 2 * p + 1 : p + D / 2;
-                bf16* qr = a.q_rot + b * a.qs.b + (hq0 + r) * a.qs.h;
-                float y1, y2;
-                rope_turn((float)qr[c1], (float)qr[c2], tab[p].x, tab[p].y, y1, y2);
-                qr[c1] = (bf16)y1;
-                qr[c2] = (bf16)y2;
+            __syncthreads();   // the angles are formed
+#pragma unroll
+            for (int u = 0; u < QPT; ++u) {
+                const int idx = tid + 256 * u;
+                if (idx < a.R * (D / 2)) {
+                    const int r = idx / (D / 2), p = idx - r * (D / 2);
+                    const int c1 = a.adj ? 2 * p : p, c2 = a.adj ? 2 * p + 1 : p + D / 2;
+                    bf16* qr = a.q_rot + b * a.qs.b + (hq0 + r) * a.qs.h;
+                    float y1, y2;
+                    rope_turn(qx1[u], qx2[u], tab[p].x, tab[p].y, y1, y2);
+                    qr[c1] = (bf16)y1;
+                    qr[c2] = (bf16)y2;
+                }
             }
-            if (tid == 0) a.cnt[g] = 0u;
+            if (tid == 0) __hip_atomic_store(a.cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -429,7 +492,7 @@ int pad_r(int R) { return R <= 4 ? 4 : (R <= 8 ? 8 : 16); }
 // longest chunk whose scores, weights and partial outputs fit the LDS cap
 int chunk_max(int R, int D) {
     const int rp = pad_r(R);
-    return ((kLdsFloats - 4 * rp * D - kStepLdsReserve) / (2 * rp)) & ~63;
+    return ((kLdsFloats - 4 * rp * D) / (2 * rp)) & ~63;
 }
 
 int split_target(int G) {
@@ -505,7 +568,7 @@ void plan(int G, int R, int D, int kv_len, int* C_out, int* S_out) {
 
 template <int D, int RP, bool STEP = false>
 hipError_t launch_split(const DecArgs& a, int grid, hipStream_t stream) {
-    const size_t lds = sizeof(float) * ((size_t)2 * RP * a.C + (size_t)4 * RP * D + (STEP ? step_lds_extra<D>() : 0));
+    const size_t lds = sizeof(float) * ((size_t)2 * RP * a.C + (size_t)4 * RP * D);
     hipLaunchKernelGGL((decode_split_kernel<D, RP, STEP>), dim3(grid), dim3(256), lds, stream, a);
     return hipGetLastError();
 }
