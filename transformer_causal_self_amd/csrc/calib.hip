@@ -20,6 +20,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChains = 4;   // independent accumulators per wave
 
@@ -47,19 +48,25 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float seed, f
     if (s == 1234.5f) sink[blockIdx.x] = s;   // practically never; keeps the loop live
 }
 
-// Grid-stride read of n16 16-byte vectors; one partial sum per workgroup.
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, long long n16,
+// Read of n16 16-byte vectors: workgroup w reads the contiguous block
+// [w * per, (w + 1) * per), eight 16-byte loads in flight per lane
+// (non-temporal: the data is used once); one value per workgroup.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, long long n16,
                                                           float* __restrict__ sink) {
-    const long long stride = (long long)gridDim.x * blockDim.x;
+    const long long per = (n16 + gridDim.x - 1) / gridDim.x;
+    const long long lo = (long long)blockIdx.x * per;
+    const long long hi = lo + per < n16 ? lo + per : n16;
     unsigned acc = 0;
-    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {   // four loads in flight per lane
-        const uint4 x0 = src[i], x1 = src[i + stride], x2 = src[i + 2 * stride], x3 = src[i + 3 * stride];
-        acc ^= x0.x ^ x0.y ^ x0.z ^ x0.w ^ x1.x ^ x1.y ^ x1.z ^ x1.w;
-        acc ^= x2.x ^ x2.y ^ x2.z ^ x2.w ^ x3.x ^ x3.y ^ x3.z ^ x3.w;
+    long long i = lo + threadIdx.x;
+    for (; i + 7 * 256 < hi; i += 8 * 256) {
+        u32x4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
     }
-    for (; i < n16; i += stride) {
-        const uint4 x = src[i];
+    for (; i < hi; i += 256) {
+        const u32x4 x = __builtin_nontemporal_load(src + i);
         acc ^= x.x ^ x.y ^ x.z ^ x.w;
     }
     __shared__ unsigned red[256];
@@ -72,10 +79,20 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
     if (threadIdx.x == 0) sink[blockIdx.x] = (float)(red[0] & 0xFFFF);
 }
 
-__global__ __launch_bounds__(256) void stream_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                           long long n16) {
-    const long long stride = (long long)gridDim.x * blockDim.x;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+    const long long per = (n16 + gridDim.x - 1) / gridDim.x;
+    const long long lo = (long long)blockIdx.x * per;
+    const long long hi = lo + per < n16 ? lo + per : n16;
+    long long i = lo + threadIdx.x;
+    for (; i + 3 * 256 < hi; i += 4 * 256) {
+        u32x4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(x[u], dst + i + u * 256);
+    }
+    for (; i < hi; i += 256) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 }  // namespace
@@ -96,7 +113,7 @@ CALIB_API int calib_stream_read(const void* src, size_t bytes, int n_workgroups,
     if (!src || !sink || bytes == 0 || bytes % 16 || n_workgroups <= 0) return -1;
     if (reinterpret_cast<uintptr_t>(src) & 15u) return -7;
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)n_workgroups), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
                        (long long)(bytes / 16), sink);
     return hipGetLastError() == hipSuccess ? 0 : -9;
 }
@@ -107,7 +124,7 @@ CALIB_API int calib_stream_copy(const void* src, void* dst, size_t bytes, int n_
     const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
     if (s0 < d0 + bytes && d0 < s0 + bytes) return -2;
     hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)n_workgroups), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
-                       static_cast<uint4*>(dst), (long long)(bytes / 16));
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                       static_cast<u32x4*>(dst), (long long)(bytes / 16));
     return hipGetLastError() == hipSuccess ? 0 : -9;
 }
