@@ -79,6 +79,10 @@ KERNEL_SOURCES = {
     "decode_bf16": "transformer_causal_self_amd/csrc/attn_decode_bf16.hip",
     "rope": "transformer_causal_self_amd/csrc/rope.hip",
     "attn_f32": "transformer_causal_self_amd/csrc/attn_f32.hip",
+    # one attn_fwd_rope call: the RoPE pass on k, then the prefill kernel
+    # that rotates q as it loads it
+    "attn_fwd_rope_bf16_d128": ("transformer_causal_self_amd/csrc/rope.hip",
+                                "transformer_causal_self_amd/csrc/attn_prefill_bf16.hip"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -109,8 +113,12 @@ def rope_bytes(w, decode):
 
 
 def source_hash(kernel):
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    src = KERNEL_SOURCES[kernel]
+    h = hashlib.sha256()
+    for path in ((src,) if isinstance(src, str) else src):
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload_name):
@@ -718,7 +726,8 @@ def main():
         roof["launch_us_median"] = head["attn_ms_median"] * 1e3
     roof["algorithmic_bytes"] = head["attn_bytes"]
     roof["algorithmic_flops"] = head["step_flops"]
-    roof["traffic"] = measured_traffic(kernel, w.name)
+    roof["traffic"] = measured_traffic("attn_fwd_rope_bf16_d128" if w.rope and not decode and w.d == 128
+                                       else kernel, w.name)
 
     line = {
         "metric": "causal attention TFLOP/s + % bf16 MFMA peak (prefill); GB/s + % HBM (decode)",
