@@ -58,11 +58,11 @@ struct BwdArgs {
     int causal, q_offset;
 };
 
-template <int D>
+template <int D, int NW_ = 4>
 struct BCfg {
     static constexpr int BN = 32;               // keys (dq) or query rows (dkv) per tile
-    static constexpr int NW = 4;                // waves per workgroup, 32 rows or keys each
-    static constexpr int BM = NW * 32;          // rows (dq) or keys (dkv) per workgroup
+    static constexpr int NW = NW_;              // waves per workgroup (all of them copy)
+    static constexpr int BM = 4 * 32;           // rows (dq) or keys (dkv) per workgroup
     static constexpr int NQ = D / 16;           // 16-wide d slices of a product over d
     static constexpr int NDB = D / 32;          // 32-row blocks of d in the accumulators
     static constexpr int NKC = 2;               // 16-wide slices of a 32-long tile
@@ -71,6 +71,7 @@ struct BCfg {
     static constexpr int CPL = NW * 64;         // lanes that copy
     static constexpr int NINS = BN * NCH / CPL; // 16-byte copies per lane per tile
     static constexpr int RSTR = CPL / NCH;      // tile rows filled by one copy instruction
+    static_assert(NINS >= 1 && BN * NCH == NINS * CPL, "every lane copies whole chunks of a tile");
 };
 
 // offset (before + 4h) of element e of a 32x32 accumulator block along its rows
@@ -78,9 +79,9 @@ __device__ inline int row_of(int e) { return 8 * (e >> 2) + (e & 3); }
 
 // ---------------------------------------------------------------------------
 // Per-lane tile addressing shared by the two gradient kernels.
-template <int D>
+template <int D, int NW = 4>
 struct TileLanes {
-    typedef BCfg<D> C;
+    typedef BCfg<D, NW> C;
     int cp_r0;
     unsigned cp_kcol, cp_vcol, cp_lds;
     unsigned koff, voff;   // row-read and transpose-read offsets in a tile
@@ -443,6 +444,172 @@ void bwd_dkv_kernel(BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV at head size 128 with the work of a key block split in two roles.
+// Waves w and w + 4 own the same 32 keys.  Wave w forms S = Q K^T and the
+// weights P, passes P (float32) to its partner through LDS and accumulates
+// dV^T += dO^T P; wave w + 4 forms dP = dO V^T, takes P, forms
+// dS = P (dP - D) and accumulates dK^T += Q^T dS.  Each wave keeps one of
+// the key's K / V rows and one accumulator -- half of what a wave of
+// bwd_dkv_kernel keeps -- so two waves share a SIMD and the LDS reads of one
+// overlap the products of the other.  Same products in the same order as
+// bwd_dkv_kernel: the results are bit-identical.
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkv_pair_kernel(BwdArgs a) {
+    typedef BCfg<D, 8> C;
+    constexpr int BN = C::BN, TB = C::TB, NQ = C::NQ, NDB = C::NDB, NKC = C::NKC;
+    // ring slot as in bwd_dkv_kernel, then the weights of the 4 key blocks
+    // ([block][4][lane] float4: the lane's 16 weights, 4 at a time)
+    constexpr int SLOT = 4 * TB + 1024;
+    constexpr int PX = 4 * 4 * 64 * 16;
+    __shared__ __attribute__((aligned(1024))) char lds[2 * SLOT + PX];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int role = wave >> 2, kblk = wave & 3;   // role 0: S, P, dV; role 1: dP, dS, dK
+    const int h = lane >> 5, li = lane & 31;
+    const int G = a.B * a.Hkv;
+    const int kb = (int)(blockIdx.x / G);   // ascending: early keys are seen by the most rows
+    const int g = (int)(blockIdx.x % G);
+    const int b = g / a.Hkv, hk = g - b * a.Hkv;
+    const int j0 = kb * C::BM, jw = j0 + 32 * kblk, key = jw + li;
+    const bool key_ok = key < a.Tk;
+
+    bf16x8 f[NQ];   // role 0: the lane's key row; role 1: its value row
+    load_row_frags<D>((role ? a.v : a.k) + (long long)g * a.Tk * D, key, key_ok, h, f);
+
+    // the same walk over the query tiles as bwd_dkv_kernel
+    const int n_rt = (a.Tq + BN - 1) / BN;
+    const int rt0 = a.causal ? min(n_rt, max(0, j0 - a.q_offset) / BN) : 0;
+    const int per_head = n_rt - rt0;
+    const int nsteps = a.R * per_head;
+    struct Pos { int head, tile; };
+    auto advance = [&](Pos p) {
+        if (--p.tile < rt0) { p.tile = n_rt - 1; ++p.head; }
+        return p;
+    };
+
+    const TileLanes<D, 8> tl(wave, lane);
+    const unsigned base = lds_addr(lds);
+    const long long bh0 = (long long)b * a.Hq + (long long)hk * a.R;
+    auto copy_step = [&](Pos p, int P) {
+        if (p.head >= a.R) { p.head = a.R - 1; p.tile = rt0; }
+        const long long bh = bh0 + p.head;
+        const int r0 = p.tile * BN;
+        const unsigned sl = base + (unsigned)(P * SLOT);
+        const bf16* qm = a.q + bh * a.Tq * D;
+        const bf16* gm = a.dO + bh * a.Tq * D;
+        tl.copy(qm, a.Tq, r0, sl, tl.cp_kcol);
+        tl.copy(gm, a.Tq, r0, sl + TB, tl.cp_kcol);
+        tl.copy(qm, a.Tq, r0, sl + 2 * TB, tl.cp_vcol);
+        tl.copy(gm, a.Tq, r0, sl + 3 * TB, tl.cp_vcol);
+    };
+    auto stats_step = [&](Pos p, int P) {
+        if (p.head >= a.R) { p.head = a.R - 1; p.tile = rt0; }
+        if (wave == 0)
+            copy4(a.stats + ((bh0 + p.head) * a.n_rt + p.tile) * 64, 4u * (unsigned)lane,
+                  base + (unsigned)(P * SLOT + 4 * TB));
+    };
+
+    f32x16 acc[NDB];   // role 0: dV^T; role 1: dK^T
+#pragma unroll
+    for (int cb = 0; cb < NDB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+    float4* const px = reinterpret_cast<float4*>(lds + 2 * SLOT) + kblk * 4 * 64 + lane;
+
+    Pos cur = {0, n_rt - 1};
+    if (nsteps > 0) {
+        copy_step(cur, 0);
+        stats_step(cur, 0);
+        wait_vm<0>();
+        __syncthreads();
+    }
+    auto step = [&](auto slot) {
+        constexpr int P = decltype(slot)::value;
+        const Pos nxt = advance(cur);
+        copy_step(nxt, 1 - P);
+        stats_step(nxt, 1 - P);
+        const int r0 = cur.tile * BN;
+        // some row of the tile sees a key of this block (the same for both roles)
+        const bool active = (!a.causal || jw <= a.q_offset + min(r0 + BN, a.Tq) - 1) && jw < a.Tk;
+        const unsigned sl = base + (unsigned)(P * SLOT);
+        f32x16 sd = {};     // role 0: S; role 1: dP
+        float rs[16];       // role 0: the rows' lse (base 2); role 1: their D
+        bf16x8 w[NKC];      // B operand of the second product: role 0 P, role 1 dS (bf16)
+        if (active) {
+            const unsigned src = sl + (unsigned)(role * TB);   // Q rows or dO rows
+#pragma unroll
+            for (int m = 0; m < NQ; ++m)
+                sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(src, m), f[m], sd, 0, 0, 0);
+            const float* stats = reinterpret_cast<const float*>(lds + P * SLOT + 4 * TB) + role * BN;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {   // rows 8i + 4h .. + 3 of the tile
+                const float4 r4 = *reinterpret_cast<const float4*>(stats + 8 * i + 4 * h);
+                rs[4 * i] = r4.x; rs[4 * i + 1] = r4.y; rs[4 * i + 2] = r4.z; rs[4 * i + 3] = r4.w;
+            }
+            if (role == 0) {
+                float p[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sd[e], a.c, -rs[e]));
+                const bool full =
+                    jw + 31 < a.Tk && r0 + BN <= a.Tq && (!a.causal || jw + 31 <= a.q_offset + r0);
+                if (!full) {
+                    const int lim = a.causal ? key - a.q_offset - 1 : -1;   // rows <= lim precede the key
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = r0 + row_of(e) + 4 * h;
+                        const bool vis = key_ok && row < a.Tq && row > lim;
+                        p[e] = vis ? p[e] : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    px[64 * i] = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) w[e >> 3][e & 7] = (bf16)p[e];
+            }
+        }
+        __syncthreads();   // the weights of every key block are in LDS
+        if (active) {
+            if (role) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 p4 = px[64 * i];
+                    const float pe[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int e = 4 * i + j;
+                        w[e >> 3][e & 7] = (bf16)(pe[j] * (sd[e] - rs[e]));
+                    }
+                }
+            }
+            // role 0: dV^T += dO^T P; role 1: dK^T += Q^T dS (one instruction
+            // stream for both, so the accumulators stay in place)
+            const unsigned tsrc = sl + (unsigned)((3 - role) * TB);
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int cb = 0; cb < NDB; ++cb)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.trfrag(tsrc, cb, kc), w[kc], acc[cb], 0, 0,
+                                                                      0);
+        }
+        cur = nxt;
+        wait_vm<0>();   // the next step's tiles have landed
+        __syncthreads();
+    };
+    for (int s = 0; s < nsteps; s += 2) {
+        step(IC<0>{});
+        if (s + 1 < nsteps) step(IC<1>{});
+    }
+    wait_vm<0>();
+    if (key_ok) {
+        if (role) store_rowT<D>(a.dk + ((long long)g * a.Tk + key) * D, acc, a.scale, h);
+        else store_rowT<D>(a.dv + ((long long)g * a.Tk + key) * D, acc, 1.f, h);
+    }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     typedef BCfg<D> C;
@@ -452,7 +619,10 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long n_kb = (a.Tk + C::BM - 1) / C::BM;
-    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)(n_kb * a.B * a.Hkv)), dim3(256), 0, stream, a);
+    if constexpr (D == 128)
+        hipLaunchKernelGGL(bwd_dkv_pair_kernel<D>, dim3((unsigned)(n_kb * a.B * a.Hkv)), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)(n_kb * a.B * a.Hkv)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
