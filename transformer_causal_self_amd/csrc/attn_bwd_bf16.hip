@@ -29,7 +29,10 @@
 //    query tiles of every query head of the group (S = Q K^T with queries on
 //    the MFMA rows, one key per lane), and accumulates dV^T += dO^T P and
 //    dK^T += Q^T dS with dO^T and Q^T from transpose reads.  The rows' lse
-//    and D values travel with the query tile through LDS.
+//    and D values travel with the query tile through LDS.  Head size 64
+//    runs this kernel (two waves per SIMD); head size 128 runs
+//    bwd_dkv_pair_kernel, which splits a key block's work between two waves
+//    (S, P and dV / dP, dS and dK) so that it too fits two waves per SIMD.
 // Rows past Tq and keys past Tk contribute nothing; keys no query can see
 // get dK = dV = 0.
 #include <math.h>
@@ -117,6 +120,52 @@ struct TileLanes {
         const unsigned addr = (tile + voff + (unsigned)(16 * kc * D * 2)) ^ (64u * cb);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + 16u * D));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+};
+
+// One copy of a tile serving both read patterns (head size 128): the
+// 16-byte chunk c of row r sits at chunk position c ^ (4 (r & 3) ^ (r >> 2 & 3)).
+// Sixteen consecutive rows then take sixteen distinct positions (row reads of
+// one logical chunk hit distinct banks), and four consecutive rows with the
+// same r >> 2 put an aligned 64-byte segment in four distinct 64-byte bank
+// groups (transpose reads).  Offsets as in TileLanes; the transpose read's
+// second 8-row half has a swizzle of its own.
+template <int D, int NW>
+struct OneTileLanes {
+    typedef BCfg<D, NW> C;
+    static_assert(D == 128, "the combined swizzle is laid out for 256-byte rows");
+    static __device__ int swz(int r) { return (4 * (r & 3)) ^ ((r >> 2) & 3); }
+    int cp_r0;
+    unsigned cp_col, cp_lds;
+    unsigned roff, toff_lo, toff_hi;
+    __device__ OneTileLanes(int wave, int lane) {
+        const int cl = wave * 64 + lane;
+        cp_r0 = cl / C::NCH;
+        cp_col = 16u * (unsigned)((cl % C::NCH) ^ swz(cp_r0));
+        cp_lds = (unsigned)(wave * 64 * 16);
+        const int h = lane >> 5, li = lane & 31;
+        roff = 2u * (unsigned)(li * D) + 16u * (unsigned)(h ^ swz(li));
+        const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
+        const int c0 = 2 * (tg & 1) + (tq >> 1), r = 4 * (tg >> 1) + tr;
+        toff_lo = 2u * (unsigned)(r * D) + 16u * (unsigned)(c0 ^ swz(r)) + 8u * (unsigned)(tq & 1);
+        toff_hi = 2u * (unsigned)((r + 8) * D) + 16u * (unsigned)(c0 ^ swz(r + 8)) + 8u * (unsigned)(tq & 1);
+    }
+    __device__ void copy(const bf16* m, int T, int j0, unsigned slot) const {
+#pragma unroll
+        for (int i = 0; i < C::NINS; ++i) {
+            const int row = min(cp_r0 + i * C::RSTR, T - 1 - j0);
+            copy16(m + (long long)j0 * D, (unsigned)row * (unsigned)(D * 2) + cp_col,
+                   slot + (unsigned)(i * C::CPL * 16) + cp_lds);
+        }
+    }
+    __device__ bf16x8 rowfrag(unsigned tile, int m) const {
+        return *(lds_bf16x8*)(uintptr_t)((tile + roff) ^ (32u * m));
+    }
+    __device__ bf16x8 trfrag(unsigned tile, int cb, int kc) const {
+        const unsigned t = tile + (unsigned)(16 * kc * D * 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((t + toff_lo) ^ (64u * cb)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((t + toff_hi) ^ (64u * cb)));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 };
@@ -447,23 +496,28 @@ void bwd_dkv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK, dV at head size 128 with the work of a key block split in two roles.
 // Waves w and w + 4 own the same 32 keys.  Wave w forms S = Q K^T and the
-// weights P, passes P (float32) to its partner through LDS and accumulates
-// dV^T += dO^T P; wave w + 4 forms dP = dO V^T, takes P, forms
-// dS = P (dP - D) and accumulates dK^T += Q^T dS.  Each wave keeps one of
-// the key's K / V rows and one accumulator -- half of what a wave of
-// bwd_dkv_kernel keeps -- so two waves share a SIMD and the LDS reads of one
-// overlap the products of the other.  Same products in the same order as
-// bwd_dkv_kernel: the results are bit-identical.
+// weights P of query tile s, passes P (float32) to its partner through LDS
+// and accumulates dV^T += dO^T P; in the same step wave w + 4 takes tile
+// s - 1: it forms dP = dO V^T, reads the P its partner wrote one step
+// earlier, forms dS = P (dP - D) and accumulates dK^T += Q^T dS.  The tiles
+// sit in a three-slot ring (s + 1 landing, s and s - 1 read) and the weights
+// in two buffers, so one barrier per step suffices and the two waves that
+// share a SIMD run independent work between barriers.  Each wave keeps one
+// of the key's K / V rows and one accumulator -- half of what a wave of
+// bwd_dkv_kernel keeps -- so two of them fit a SIMD.  Same products in the
+// same order as bwd_dkv_kernel: the results are bit-identical.
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkv_pair_kernel(BwdArgs a) {
     typedef BCfg<D, 8> C;
     constexpr int BN = C::BN, TB = C::TB, NQ = C::NQ, NDB = C::NDB, NKC = C::NKC;
-    // ring slot as in bwd_dkv_kernel, then the weights of the 4 key blocks
-    // ([block][4][lane] float4: the lane's 16 weights, 4 at a time)
-    constexpr int SLOT = 4 * TB + 1024;
+    // ring slot: Q | dO (one copy each, read both ways) | lse and D of the 32
+    // rows (padded to 1 KiB); then two buffers of the weights of the 4 key
+    // blocks ([block][4][lane] float4: the lane's 16 weights, 4 at a time)
+    constexpr int SLOT = 2 * TB + 1024;
+    constexpr int NSLOT = 3;
     constexpr int PX = 4 * 4 * 64 * 16;
-    __shared__ __attribute__((aligned(1024))) char lds[2 * SLOT + PX];
+    __shared__ __attribute__((aligned(1024))) char lds[NSLOT * SLOT + 2 * PX];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -490,26 +544,33 @@ void bwd_dkv_pair_kernel(BwdArgs a) {
         return p;
     };
 
-    const TileLanes<D, 8> tl(wave, lane);
+    const OneTileLanes<D, 8> tl(wave, lane);
     const unsigned base = lds_addr(lds);
     const long long bh0 = (long long)b * a.Hq + (long long)hk * a.R;
-    auto copy_step = [&](Pos p, int P) {
+    // tiles and row statistics of step position p into ring slot `slot`
+    // (positions past the end repeat the last one)
+    auto copy_step = [&](Pos p, int slot) {
         if (p.head >= a.R) { p.head = a.R - 1; p.tile = rt0; }
         const long long bh = bh0 + p.head;
         const int r0 = p.tile * BN;
-        const unsigned sl = base + (unsigned)(P * SLOT);
+        const unsigned sl = base + (unsigned)(slot * SLOT);
         const bf16* qm = a.q + bh * a.Tq * D;
         const bf16* gm = a.dO + bh * a.Tq * D;
-        tl.copy(qm, a.Tq, r0, sl, tl.cp_kcol);
-        tl.copy(gm, a.Tq, r0, sl + TB, tl.cp_kcol);
-        tl.copy(qm, a.Tq, r0, sl + 2 * TB, tl.cp_vcol);
-        tl.copy(gm, a.Tq, r0, sl + 3 * TB, tl.cp_vcol);
-    };
-    auto stats_step = [&](Pos p, int P) {
-        if (p.head >= a.R) { p.head = a.R - 1; p.tile = rt0; }
+        tl.copy(qm, a.Tq, r0, sl);
+        tl.copy(gm, a.Tq, r0, sl + TB);
         if (wave == 0)
-            copy4(a.stats + ((bh0 + p.head) * a.n_rt + p.tile) * 64, 4u * (unsigned)lane,
-                  base + (unsigned)(P * SLOT + 4 * TB));
+            copy4(a.stats + (bh * a.n_rt + p.tile) * 64, 4u * (unsigned)lane, sl + 2 * TB);
+    };
+    // some row of query tile r0 sees a key of this block (the same for both roles)
+    auto active = [&](int r0) { return (!a.causal || jw <= a.q_offset + min(r0 + BN, a.Tq) - 1) && jw < a.Tk; };
+    // rows 8i + 4h .. + 3 of a tile's statistics (lse base 2, or D)
+    auto row_stats = [&](int slot, int which, float (&rs)[16]) {
+        const float* st = reinterpret_cast<const float*>(lds + slot * SLOT + 2 * TB) + which * BN;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 r4 = *reinterpret_cast<const float4*>(st + 8 * i + 4 * h);
+            rs[4 * i] = r4.x; rs[4 * i + 1] = r4.y; rs[4 * i + 2] = r4.z; rs[4 * i + 3] = r4.w;
+        }
     };
 
     f32x16 acc[NDB];   // role 0: dV^T; role 1: dK^T
@@ -517,39 +578,60 @@ void bwd_dkv_pair_kernel(BwdArgs a) {
     for (int cb = 0; cb < NDB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-    float4* const px = reinterpret_cast<float4*>(lds + 2 * SLOT) + kblk * 4 * 64 + lane;
+    float4* const px = reinterpret_cast<float4*>(lds + NSLOT * SLOT) + kblk * 4 * 64 + lane;
 
-    Pos cur = {0, n_rt - 1};
-    if (nsteps > 0) {
-        copy_step(cur, 0);
-        stats_step(cur, 0);
-        wait_vm<0>();
-        __syncthreads();
+    if (nsteps == 0) {   // no query row sees these keys
+        if (key_ok) store_rowT<D>((role ? a.dk : a.dv) + ((long long)g * a.Tk + key) * D, acc, 1.f, h);
+        return;
     }
-    auto step = [&](auto slot) {
-        constexpr int P = decltype(slot)::value;
+    Pos cur = {0, n_rt - 1}, prev = cur;
+    copy_step(cur, 0);
+    wait_vm<0>();
+    __syncthreads();
+    // step s: role 0 on tile s (slot s % 3), role 1 on tile s - 1; tiles of
+    // step s + 1 land in slot (s + 1) % 3, last read by role 1 in step s - 1
+    int slot = 0;
+    for (int s = 0; s <= nsteps; ++s) {
+        const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
         const Pos nxt = advance(cur);
-        copy_step(nxt, 1 - P);
-        stats_step(nxt, 1 - P);
-        const int r0 = cur.tile * BN;
-        // some row of the tile sees a key of this block (the same for both roles)
-        const bool active = (!a.causal || jw <= a.q_offset + min(r0 + BN, a.Tq) - 1) && jw < a.Tk;
-        const unsigned sl = base + (unsigned)(P * SLOT);
+        if (s + 1 < nsteps) copy_step(nxt, nslot);
         f32x16 sd = {};     // role 0: S; role 1: dP
         float rs[16];       // role 0: the rows' lse (base 2); role 1: their D
         bf16x8 w[NKC];      // B operand of the second product: role 0 P, role 1 dS (bf16)
-        if (active) {
-            const unsigned src = sl + (unsigned)(role * TB);   // Q rows or dO rows
+        int rslot;          // the ring slot this wave reads
+        bool act;
+        if (role == 0) {
+            rslot = slot;
+            act = s < nsteps && active(cur.tile * BN);
+        } else {
+            rslot = slot == 0 ? NSLOT - 1 : slot - 1;
+            act = s > 0 && active(prev.tile * BN);
+        }
+        const unsigned sl = base + (unsigned)(rslot * SLOT);
+        if (act) {
+            // role 0: S = Q K^T from Q rows; role 1: dP = dO V^T from dO rows
+            // everything the step reads is in LDS when it starts (role 1's
+            // weights were written a step earlier): issue all the reads at
+            // once, so the step waits for one LDS round trip
+            const unsigned src = sl + (unsigned)(role * TB);
+            const unsigned tsrc = sl + (unsigned)((1 - role) * TB);
+            float4* const pbuf = px + (((s - role) & 1) ? 4 * 4 * 64 : 0);
+            bf16x8 rf[NQ], tf[NKC][NDB];
+            float4 pw[4];
 #pragma unroll
-            for (int m = 0; m < NQ; ++m)
-                sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.rowfrag(src, m), f[m], sd, 0, 0, 0);
-            const float* stats = reinterpret_cast<const float*>(lds + P * SLOT + 4 * TB) + role * BN;
+            for (int m = 0; m < NQ; ++m) rf[m] = tl.rowfrag(src, m);
+            if (role)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {   // rows 8i + 4h .. + 3 of the tile
-                const float4 r4 = *reinterpret_cast<const float4*>(stats + 8 * i + 4 * h);
-                rs[4 * i] = r4.x; rs[4 * i + 1] = r4.y; rs[4 * i + 2] = r4.z; rs[4 * i + 3] = r4.w;
-            }
+                for (int i = 0; i < 4; ++i) pw[i] = pbuf[64 * i];
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int cb = 0; cb < NDB; ++cb) tf[kc][cb] = tl.trfrag(tsrc, cb, kc);
+            row_stats(rslot, role, rs);
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf[m], f[m], sd, 0, 0, 0);
             if (role == 0) {
+                const int r0 = cur.tile * BN;
                 float p[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sd[e], a.c, -rs[e]));
@@ -566,17 +648,13 @@ void bwd_dkv_pair_kernel(BwdArgs a) {
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    px[64 * i] = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+                    pbuf[64 * i] = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) w[e >> 3][e & 7] = (bf16)p[e];
-            }
-        }
-        __syncthreads();   // the weights of every key block are in LDS
-        if (active) {
-            if (role) {
+            } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float4 p4 = px[64 * i];
+                    const float4 p4 = pw[i];
                     const float pe[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -587,23 +665,18 @@ void bwd_dkv_pair_kernel(BwdArgs a) {
             }
             // role 0: dV^T += dO^T P; role 1: dK^T += Q^T dS (one instruction
             // stream for both, so the accumulators stay in place)
-            const unsigned tsrc = sl + (unsigned)((3 - role) * TB);
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int cb = 0; cb < NDB; ++cb)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.trfrag(tsrc, cb, kc), w[kc], acc[cb], 0, 0,
-                                                                      0);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[kc][cb], w[kc], acc[cb], 0, 0, 0);
         }
+        prev = cur;
         cur = nxt;
+        slot = nslot;
         wait_vm<0>();   // the next step's tiles have landed
         __syncthreads();
-    };
-    for (int s = 0; s < nsteps; s += 2) {
-        step(IC<0>{});
-        if (s + 1 < nsteps) step(IC<1>{});
     }
-    wait_vm<0>();
     if (key_ok) {
         if (role) store_rowT<D>(a.dk + ((long long)g * a.Tk + key) * D, acc, a.scale, h);
         else store_rowT<D>(a.dv + ((long long)g * a.Tk + key) * D, acc, 1.f, h);
