@@ -130,7 +130,9 @@ struct TileLanes {
 // one logical chunk hit distinct banks), and four consecutive rows with the
 // same r >> 2 put an aligned 64-byte segment in four distinct 64-byte bank
 // groups (transpose reads).  Offsets as in TileLanes; the transpose read's
-// second 8-row half has a swizzle of its own.
+// second 8-row half, rows r + 8, has the swizzle of row r with chunk bit 1
+// flipped, so its address is the first half's with byte bit 5 flipped,
+// 8 rows further on.
 template <int D, int NW>
 struct OneTileLanes {
     typedef BCfg<D, NW> C;
@@ -138,7 +140,7 @@ struct OneTileLanes {
     static __device__ int swz(int r) { return (4 * (r & 3)) ^ ((r >> 2) & 3); }
     int cp_r0;
     unsigned cp_col, cp_lds;
-    unsigned roff, toff_lo, toff_hi;
+    unsigned roff, toff;
     __device__ OneTileLanes(int wave, int lane) {
         const int cl = wave * 64 + lane;
         cp_r0 = cl / C::NCH;
@@ -148,8 +150,7 @@ struct OneTileLanes {
         roff = 2u * (unsigned)(li * D) + 16u * (unsigned)(h ^ swz(li));
         const int tg = lane >> 4, tr = (lane >> 2) & 3, tq = lane & 3;
         const int c0 = 2 * (tg & 1) + (tq >> 1), r = 4 * (tg >> 1) + tr;
-        toff_lo = 2u * (unsigned)(r * D) + 16u * (unsigned)(c0 ^ swz(r)) + 8u * (unsigned)(tq & 1);
-        toff_hi = 2u * (unsigned)((r + 8) * D) + 16u * (unsigned)(c0 ^ swz(r + 8)) + 8u * (unsigned)(tq & 1);
+        toff = 2u * (unsigned)(r * D) + 16u * (unsigned)(c0 ^ swz(r)) + 8u * (unsigned)(tq & 1);
     }
     __device__ void copy(const bf16* m, int T, int j0, unsigned slot) const {
 #pragma unroll
@@ -163,9 +164,10 @@ struct OneTileLanes {
         return *(lds_bf16x8*)(uintptr_t)((tile + roff) ^ (32u * m));
     }
     __device__ bf16x8 trfrag(unsigned tile, int cb, int kc) const {
-        const unsigned t = tile + (unsigned)(16 * kc * D * 2);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((t + toff_lo) ^ (64u * cb)));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)((t + toff_hi) ^ (64u * cb)));
+        const unsigned lo_addr = (tile + (unsigned)(16 * kc * D * 2) + toff) ^ (64u * cb);
+        const unsigned hi_addr = (lo_addr ^ 32u) + 16u * D;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lo_addr);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)hi_addr);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 };
@@ -204,7 +206,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
     typedef BCfg<D> C;
     constexpr int BN = C::BN, TB = C::TB, NQ = C::NQ, NDB = C::NDB, NKC = C::NKC;
-    constexpr int SLOT = 3 * TB;   // ring slot: K (row reads) | V (row reads) | K (transpose reads)
+    // ring slot: K (row reads) | V (row reads) | K (transpose reads).  (One
+    // copy of K in the combined swizzle of OneTileLanes would do for both
+    // reads, but its second-half transpose address costs the registers that
+    // keep this kernel from spilling at head size 128.)
+    constexpr int SLOT = 3 * TB;
+    constexpr int KT = 2 * TB;   // where the transpose reads find K
     __shared__ __attribute__((aligned(1024))) char lds[2 * SLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -259,7 +266,7 @@ void bwd_dq_kernel(BwdArgs a) {
         const unsigned s = base + (unsigned)(P * SLOT);
         tl.copy(kh, a.Tk, j0, s, tl.cp_kcol);
         tl.copy(vh, a.Tk, j0, s + TB, tl.cp_kcol);
-        tl.copy(kh, a.Tk, j0, s + 2 * TB, tl.cp_vcol);
+        tl.copy(kh, a.Tk, j0, s + KT, tl.cp_vcol);
     };
 
     f32x16 acc[NDB];
@@ -300,7 +307,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
                 for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-                    for (int cb = 0; cb < NDB; ++cb) kt[kc][cb] = tl.trfrag(s + 2 * TB, cb, kc);
+                    for (int cb = 0; cb < NDB; ++cb) kt[kc][cb] = tl.trfrag(s + KT, cb, kc);
             }
             float p[16];
 #pragma unroll
@@ -317,7 +324,7 @@ void bwd_dq_kernel(BwdArgs a) {
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
                 for (int cb = 0; cb < NDB; ++cb)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(PRE ? kt[kc][cb] : tl.trfrag(s + 2 * TB, cb, kc),
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(PRE ? kt[kc][cb] : tl.trfrag(s + KT, cb, kc),
                                                                       dsb[kc], acc[cb], 0, 0, 0);
         }
         wait_vm<0>();   // tile t + 1 has landed
