@@ -14,7 +14,7 @@
 // query heads of its group ("The Transformer architecture" -- GQA), in a
 // fixed order, so results are deterministic.  D_i equals sum_j P_ij dP_ij.
 //
-// Two kernels, each a plain adaptation of the forward's tile scheme:
+// Two launches, each a plain adaptation of the forward's tile scheme:
 //  * bwd_dq_kernel: one workgroup = 4 waves x 32 query rows.  First each
 //    row's statistics: lse as a base-2 exponent and D = rowsum(dO * O),
 //    which the wave also writes to the workspace, 64 floats per 32-row tile
