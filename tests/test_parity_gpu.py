@@ -1045,6 +1045,34 @@ def test_attn_fwd_rope_workload4_equals_unfused_bit_exact():
     assert torch.equal(o1, o2)
 
 
+# ---- long dense launches at head size 128 take 12-wave workgroups of 384
+#      query rows (one per CU); these shapes cross that threshold (at least
+#      1024 such workgroups) with a ragged last tile, GQA and a cache offset
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tk,causal,qo", [
+    (4, 128, 16, 400, 400, True, 0),      # 2 x 512 workgroups; the second tile holds 16 rows
+    (2, 256, 32, 500, 900, True, 400),    # rows at 400.., more keys than rows
+    (1, 512, 64, 390, 390, False, 0),     # no mask
+])
+def test_wide_workgroups_match_oracle(B, Hq, Hkv, Tq, Tk, causal, qo):
+    say("wide prefill", B, Hq, Hkv, Tq, Tk, causal, qo)
+    assert ((Tq + 383) // 384) * B * Hq >= 1024   # the 12-wave path
+    q, k, v = wl.random_qkv(B, Hq, Hkv, Tq, Tk, 128, dtype=torch.bfloat16, seed=Tq + Tk + Hq)
+    err = check(q, k, v, 128 ** -0.5, causal, qo)
+    say("attn_fwd max abs err", err)
+    # and the fused RoPE path on the same launch shape (k turned at 0.., query
+    # row i at q_offset + i; every query position has a key angle here)
+    if (qo if causal else 0) + Tq <= Tk:
+        qd, kd, vd = gpu(q, k, v)
+        o = ra.attn_fwd_rope(qd, kd, vd, scale=128 ** -0.5, causal=causal, q_offset=qo, base=10000.0)
+        torch.cuda.synchronize()
+        want = oracle.attn(oracle.rope(q, qo if causal else 0, 10000.0), oracle.rope(k, 0, 10000.0), v,
+                           128 ** -0.5, causal=causal, q_offset=qo)
+        err = float(np.max(np.abs(f64(o) - want)))
+        say("attn_fwd_rope max abs err", err)
+        assert err <= TOL[torch.bfloat16], err
+
+
 # ---- small prefills split over the keys (a workspace of attn_workspace_bytes
 #      lets a launch that would leave the chip idle use more workgroups)
 

@@ -12,7 +12,9 @@
 // Flash Attention).
 //
 // Design (one workgroup = 4 waves = 128 query rows of one (b, hq); several
-// workgroups per CU):
+// workgroups per CU -- or, for long dense launches at head size 128, 12
+// waves = 384 rows, one workgroup per CU, so that each tile copied into LDS
+// serves three times the rows):
 //  * Each wave owns 32 query rows; its Q fragment stays in registers as the
 //    B operand of v_mfma_f32_32x32x16_bf16.  The kernel is kept small so
 //    that several waves share each SIMD (four at head size 64, about 120
@@ -66,12 +68,17 @@ namespace {
 // width of q and k rows, DV that of v and o rows:
 //   DK = DV = 64:  64-key tiles, four waves per SIMD (about 120 VGPRs)
 //   otherwise:     32-key tiles, three waves per SIMD (about 145-160 VGPRs)
-template <int DK, int DV>
+// NWS waves per workgroup: 4 (several workgroups per CU), or at head size
+// 128, 12 -- one workgroup fills a CU at three waves per SIMD and each K/V
+// tile copied into LDS serves 384 query rows (long launches; see
+// wide_prefill below).
+template <int DK, int DV, int NWS = 4>
 struct Cfg {
     static constexpr bool SMALL = DK == 64 && DV == 64;
     static constexpr int BN = SMALL ? 64 : 32;      // keys per tile
     static constexpr int WPE = SMALL ? 4 : 3;       // waves per SIMD
-    static constexpr int NW = 4;                    // waves per workgroup
+    static constexpr int NW = NWS;                  // waves per workgroup
+    static_assert(NW == 4 || (NW == 12 && !SMALL), "4-wave workgroups, or 12 at head size 128");
     static constexpr int RB = 1;                    // 32-row blocks per wave (the code allows more)
     static constexpr int BM = NW * RB * 32;         // query rows per workgroup
     static constexpr int NCHK = DK / 8;             // 16-byte chunks per key row
@@ -89,7 +96,14 @@ struct Cfg {
     static constexpr int NINSV = BN * NCHV / CPL;   // ... per V tile
     static constexpr int RSTRK = CPL / NCHK;        // K tile rows filled by one copy instruction
     static constexpr int RSTRV = CPL / NCHV;        // ... V tile rows
-    static_assert(BN % 32 == 0 && NINSK >= 1 && NINSV >= 1, "tiles of whole 32-key blocks");
+    // When the lanes do not divide a tile's 16-byte chunks (12 waves), the
+    // chunks of a K tile and then a V tile are numbered 0 .. NCP-1 and lane
+    // l of copy instruction i moves chunk i * CPL + l (GEN).
+    static constexpr int NCK = BN * NCHK, NCP = NCK + BN * NCHV;
+    static constexpr bool GEN = NCK % CPL != 0 || (NCP - NCK) % CPL != 0;
+    static constexpr int NCI = (NCP + CPL - 1) / CPL;   // copy instructions per lane (GEN)
+    static_assert(BN % 32 == 0 && NCK % 64 == 0 && (GEN || (NINSK >= 1 && NINSV >= 1)),
+                  "tiles of whole 32-key blocks, each wave's chunks all K or all V");
 };
 
 struct Args {
@@ -168,7 +182,7 @@ __device__ inline void rope_q_frags(bf16x8 (&f)[D / 16], const float2* tab, int 
 
 template <int DK, int DV>
 struct Scores {
-    f32x16 s[Cfg<DK, DV>::RB][Cfg<DK, DV>::NKB];
+    f32x16 s[Cfg<DK, DV>::RB][Cfg<DK, DV>::NKB];   // RB and NKB do not depend on the workgroup size
 };
 
 // DENSE: q and k are dense [B][H][T][DK], v and o dense [B][H][T][DV], so
@@ -178,11 +192,11 @@ struct Scores {
 // SPLIT: a.ks workgroups share a (query tile, head), each taking one
 // contiguous run of its key tiles and writing partial results that
 // combine_kernel merges (for launches too small to fill the chip).
-template <int DK, int DV, bool DENSE, bool ROPE, bool SPLIT = false>
-__global__ __launch_bounds__((Cfg<DK, DV>::NW * 64))
-__attribute__((amdgpu_waves_per_eu(Cfg<DK, DV>::WPE, Cfg<DK, DV>::WPE)))
+template <int DK, int DV, bool DENSE, bool ROPE, bool SPLIT = false, int NWS = 4>
+__global__ __launch_bounds__((Cfg<DK, DV, NWS>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(Cfg<DK, DV, NWS>::WPE, Cfg<DK, DV, NWS>::WPE)))
 void prefill_kernel(Args a) {
-    typedef Cfg<DK, DV> C;
+    typedef Cfg<DK, DV, NWS> C;
     constexpr int BN = C::BN, NW = C::NW, RB = C::RB, BM = C::BM, NCHK = C::NCHK, NCHV = C::NCHV;
     constexpr int TBK = C::TBK, TBV = C::TBV;
     constexpr int NRING = C::NRING, NQ = C::NQ, NDB = C::NDB, NKC = C::NKC, NKB = C::NKB;
@@ -321,6 +335,35 @@ void prefill_kernel(Args a) {
                    slot + (unsigned)(i * CPL * 16) + cp_lds);
         }
     };
+    // GEN: lane l of copy instruction i moves chunk g = i CPL + 64 wave + l
+    // of the tile pair (K chunks first); a wave's 64 chunks are all K or all
+    // V, so the wave picks the tensor and the LDS destination uniformly
+    int gen_row[C::NCI];
+    unsigned gen_col[C::NCI];
+#pragma unroll
+    for (int i = 0; i < C::NCI; ++i) {
+        const int g = i * CPL + 64 * wave + lane;
+        const bool isk = g < C::NCK;
+        const int c = isk ? g : g - C::NCK, nch = isk ? NCHK : NCHV;
+        gen_row[i] = c / nch;
+        gen_col[i] = 16u * (unsigned)((c % nch) ^ (isk ? swz_k<DK>(c / nch) : swz_v<DV>(c / nch)));
+    }
+    auto copy_gen = [&](int t, int P) {
+        const int j0 = min(t, n - 1) * BN;
+#pragma unroll
+        for (int i = 0; i < C::NCI; ++i) {
+            const int gw = i * CPL + 64 * wave;   // the wave's first chunk
+            if (gw < C::NCP) {
+                const bool isk = gw < C::NCK;
+                const int row = min(gen_row[i], a.Tk - 1 - j0);
+                const int rs = isk ? kst : vst;
+                const unsigned dst = isk ? kring + (unsigned)(P * TBK + 16 * gw)
+                                         : vring + (unsigned)(P * TBV + 16 * (gw - C::NCK));
+                copy16((isk ? kh : vh) + (long long)j0 * rs, (unsigned)row * (unsigned)(rs * 2) + gen_col[i], dst);
+            }
+        }
+    };
+    (void)copy_gen;
     constexpr IC<C::NINSK> nik{};
     constexpr IC<C::NINSV> niv{};
     constexpr IC<C::RSTRK> rsk{};
@@ -449,8 +492,12 @@ void prefill_kernel(Args a) {
     //      tile t_lo lands before the barrier
 #pragma unroll
     for (int t = 0; t < NRING - 1; ++t) {
-        copy_tile(kh, kst, t_lo + t, kslot(t), cp_kcol, cpk_r0, nik, rsk);
-        copy_tile(vh, vst, t_lo + t, vslot(t), cp_vcol, cpv_r0, niv, rsv);
+        if constexpr (C::GEN) {
+            copy_gen(t_lo + t, t);
+        } else {
+            copy_tile(kh, kst, t_lo + t, kslot(t), cp_kcol, cpk_r0, nik, rsk);
+            copy_tile(vh, vst, t_lo + t, vslot(t), cp_vcol, cpv_r0, niv, rsv);
+        }
     }
     static_assert(NRING == 2, "the prologue waits for every copy");
     wait_vm<0>();
@@ -466,7 +513,9 @@ void prefill_kernel(Args a) {
     auto step = [&](int t, auto slot) {
         constexpr int P = decltype(slot)::value;
         const int tc = t + 1;
-        if (tc < n && (tc + 1) * BN <= a.Tk) {
+        if constexpr (C::GEN) {
+            copy_gen(tc, 1 - P);
+        } else if (tc < n && (tc + 1) * BN <= a.Tk) {
             copy_full(kh, kst, tc, kring + (unsigned)((1 - P) * TBK), cpk, nik, rsk);
             copy_full(vh, vst, tc, vring + (unsigned)((1 - P) * TBV), cpv, niv, rsv);
         } else {
@@ -564,6 +613,18 @@ void prefill_kernel(Args a) {
     }
 }
 
+// 12-wave workgroups (one per CU, each K/V tile serving 384 query rows) for
+// dense head-size-128 launches long enough to give every CU at least four of
+// them: a third of the tile copies per MFMA of the 4-wave workgroups, at the
+// price of the overlap between workgroups on a CU.  Measured: workload 4
+// (B1 Hq32 Hkv8 T16384) 1.4-2.0 % faster; workload 3 (B2 Hq32 Hkv8 T4096,
+// 704 such workgroups) 0.7 % slower, so it keeps the 4-wave ones.
+constexpr long long kWideMinWorkgroups = 1024;
+bool wide_prefill(const FwdParams& p) {
+    const long long nwg = (long long)((p.Tq + 383) / 384) * p.B * p.Hq;
+    return nwg >= kWideMinWorkgroups;
+}
+
 template <int DK, int DV>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
     const bool dense = p.qs.t == DK && p.ks.t == DK && p.vs.t == DV && p.os.t == DV;
@@ -601,6 +662,21 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
             if (p.rope_tab || !dense) return hipErrorInvalidValue;
             hipLaunchKernelGGL((prefill_kernel<DK, DV, true, false, true>), dim3((unsigned)(nwg * p.nsplit)),
                                dim3(C::NW * 64), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (DK == 128 && DV == 128) {
+        if (dense && wide_prefill(p)) {   // fused RoPE or not
+            typedef Cfg<DK, DV, 12> W;
+            Args aw = a;
+            aw.n_qt = (p.Tq + W::BM - 1) / W::BM;
+            const long long nww = (long long)aw.n_qt * a.G * a.R;
+            if (p.rope_tab)
+                hipLaunchKernelGGL((prefill_kernel<DK, DV, true, true, false, 12>), dim3((unsigned)nww),
+                                   dim3(W::NW * 64), 0, stream, aw);
+            else
+                hipLaunchKernelGGL((prefill_kernel<DK, DV, true, false, false, 12>), dim3((unsigned)nww),
+                                   dim3(W::NW * 64), 0, stream, aw);
             return hipGetLastError();
         }
     }
