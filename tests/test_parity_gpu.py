@@ -274,6 +274,26 @@ def test_end_to_end_workload4_sampled():
         assert err <= TOL[torch.bfloat16], (name, err)
 
 
+def test_end_to_end_workload4_full():
+    """The long-context workload on the full tensor (every row of every head,
+    about 2.2e12 fp64 FLOPs for the oracle, some 20-30 s on the host's
+    cores): attn_fwd_rope -- the path the benchmark times, with its 12-wave
+    workgroups -- against the oracle's fp64 RoPE and attention."""
+    w = wl.WORKLOADS[4]
+    say("rope+attn full", w.name)
+    q, k, v = wl.inputs(w)
+    qd, kd, vd = gpu(q, k, v)
+    o = ra.attn_fwd_rope(qd, kd, vd, scale=w.scale, causal=True, q_offset=0, base=w.rope_base)
+    torch.cuda.synchronize()
+    got = f64(o)
+    del qd, kd, vd, o
+    want = oracle.attn(oracle.rope(q, 0, w.rope_base), oracle.rope(k, 0, w.rope_base), v, w.scale)
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - want)))
+    say("max abs err over the full tensor", err)
+    assert err <= TOL[torch.bfloat16], err
+
+
 # --------------------------------------------------------------------------
 # bf16 decode (split-K kernels)
 # --------------------------------------------------------------------------
