@@ -1073,6 +1073,8 @@ def test_attn_fwd_rope_workload4_equals_unfused_bit_exact():
     (4, 128, 16, 400, 400, True, 0),      # 2 x 512 workgroups; the second tile holds 16 rows
     (2, 256, 32, 500, 900, True, 400),    # rows at 400.., more keys than rows
     (1, 512, 64, 390, 390, False, 0),     # no mask
+    (8, 128, 128, 385, 385, True, 0),     # MHA; the last tile holds one row
+    (3, 171, 57, 800, 1000, True, 200),   # B * Hkv not a multiple of 8 (no XCD grouping), 3 heads per K/V head
 ])
 def test_wide_workgroups_match_oracle(B, Hq, Hkv, Tq, Tk, causal, qo):
     say("wide prefill", B, Hq, Hkv, Tq, Tk, causal, qo)
