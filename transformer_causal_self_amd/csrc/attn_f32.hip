@@ -86,19 +86,49 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdParams p) {
     const int row_pos = p.q_offset + i;                  // absolute position of this row
     const int kv_end = p.causal ? min(p.Tk, p.q_offset + qt * kRows + kRows) : p.Tk;
 
+    // a tile's K and V rows (keys past Tk as zeros), 16 bytes per lane and load
+    auto k_at = [&](int j0, int x) {
+        const int jj = x / gk, cc = x - jj * gk, j = j0 + jj;
+        return j < p.Tk ? *reinterpret_cast<const float4*>(kg + k_base + j * p.ks.t + 4 * cc)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto v_at = [&](int j0, int x) {
+        const int jj = x / gv, cc = x - jj * gv, j = j0 + jj;
+        return j < p.Tk ? *reinterpret_cast<const float4*>(vg + v_base + j * p.vs.t + 4 * cc)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    // Up to d = 128 the next tile is loaded into registers while this one is
+    // worked on (its load latency, paid once per tile otherwise, is what a
+    // short causal row walk waits on); wider rows load each tile in turn.
+    constexpr bool PF = NC <= 2;
+    constexpr int NPF = PF ? kKeys * kLanes * NC / 256 : 1;   // loads per lane and tensor
+    float4 kpf[NPF], vpf[NPF];
+    auto prefetch = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < NPF; ++u) {
+            const int x = tid + 256 * u;
+            if (x < kKeys * gk) kpf[u] = k_at(j0, x);
+            if (x < kKeys * gv) vpf[u] = v_at(j0, x);
+        }
+    };
+    if constexpr (PF) prefetch(0);
+
     for (int j0 = 0; j0 < kv_end; j0 += kKeys) {
         __syncthreads();
-        for (int x = tid; x < kKeys * gk; x += 256) {
-            const int jj = x / gk, cc = x - jj * gk, j = j0 + jj;
-            Ks[x] = j < p.Tk ? *reinterpret_cast<const float4*>(kg + k_base + j * p.ks.t + 4 * cc)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        for (int x = tid; x < kKeys * gv; x += 256) {
-            const int jj = x / gv, cc = x - jj * gv, j = j0 + jj;
-            Vs[x] = j < p.Tk ? *reinterpret_cast<const float4*>(vg + v_base + j * p.vs.t + 4 * cc)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (PF) {
+#pragma unroll
+            for (int u = 0; u < NPF; ++u) {
+                const int x = tid + 256 * u;
+                if (x < kKeys * gk) Ks[x] = kpf[u];
+                if (x < kKeys * gv) Vs[x] = vpf[u];
+            }
+        } else {
+            for (int x = tid; x < kKeys * gk; x += 256) Ks[x] = k_at(j0, x);
+            for (int x = tid; x < kKeys * gv; x += 256) Vs[x] = v_at(j0, x);
         }
         __syncthreads();
+        if constexpr (PF)
+            if (j0 + kKeys < kv_end) prefetch(j0 + kKeys);
 
         float s[kKeys];
         float tmax = -INFINITY;
