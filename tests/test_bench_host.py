@@ -100,3 +100,34 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _file_hash(rel):
+    import hashlib
+    with open(os.path.join(ROOT, "transformer_causal_self_amd", "csrc", rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# each kernel-trace summary under profiles/ names the hash of the sources it was
+# profiled on; the summary is stale (and must be taken again) once they change
+PROFILE_SOURCES = {
+    "attn_bwd_bf16_workloads2_3.txt": lambda: [_file_hash("attn_bwd_bf16.hip")],
+    "decode_split_bf16_d128_B32_Hq32_Hkv8_Tk8192.txt": lambda: [_file_hash("attn_decode_bf16.hip")],
+    "prefill_bf16_d128_gqa_B2_Hq32_Hkv8_T4096.txt": lambda: [bench.source_hash("prefill_bf16_d128")],
+    "prefill_bf16_d64_mha_B8_H12_T1024.txt": lambda: [bench.source_hash("prefill_bf16_d64")],
+    "prefill_bf16_d128_gqa_B1_Hq32_Hkv8_T16384.txt": lambda: [bench.source_hash("prefill_bf16_d128"),
+                                                              bench.source_hash("attn_fwd_rope_bf16_d128")],
+    "rope_bf16_d128_workloads3_4.txt": lambda: [_file_hash("rope.hip")],
+    "cached_steps_bf16_d128.txt": lambda: [_file_hash("attn_decode_bf16.hip"), _file_hash("attn_prefill_bf16.hip"),
+                                           _file_hash("rope.hip")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROFILE_SOURCES))
+def test_profile_summaries_were_taken_on_the_current_sources(name):
+    import re
+    with open(os.path.join(ROOT, "profiles", name)) as f:
+        text = f.read()
+    line = next(l for l in text.splitlines() if "sha256[:16] at profiling time" in l)
+    recorded = re.findall(r"\b[0-9a-f]{16}\b", line)
+    assert recorded == PROFILE_SOURCES[name](), (name, line)
